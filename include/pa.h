@@ -1,0 +1,201 @@
+/*
+ * pa.h — ragged paged attention for continuous batching, MI355X (gfx950).
+ *
+ * One step of continuous batching flattens the step's new tokens of S
+ * sequences into one [T] batch, writes their K/V into a paged cache through
+ * slot_mapping, then attends each new query row to its own sequence's cached
+ * K/V through that sequence's block table, causally.  Prefill chunks and
+ * decode tokens share the batch.
+ *
+ * Pages cited below:
+ *   [FS] "vLLM Continuous Batching：从 Forward Shape 理解两个核心参数"
+ *   [VP] "vLLM 原理"
+ *   [CB] "LLM 推理引擎 Continuous Batching 与 PagedAttention：从 vLLM 原理到生产级部署实战"
+ *   [BN] "vLLM 学习笔记（2）：从单请求到批处理"
+ *
+ * Conventions for every entry point:
+ *   - All array arguments are DEVICE pointers to caller-owned, contiguous,
+ *     row-major memory.  The library never allocates, frees or synchronises;
+ *     all work is enqueued on `stream` (a hipStream_t; NULL = default stream)
+ *     and is complete when that stream is.  The caller owns the KV cache (the
+ *     engine allocates one pool and hands out per-layer views, [VP] §3.6).
+ *   - Host-checkable problems (null pointers, bad sizes, unsupported shapes,
+ *     a too-small workspace, a failed launch) are returned synchronously as
+ *     pa_status_t and nothing is enqueued.
+ *   - Data-dependent problems found on the device are OR-ed into *d_err (an
+ *     int32 in device memory, may be NULL) as PA_DERR_* bits; the caller reads
+ *     it whenever it likes.  Outputs of rows touched by such a problem are
+ *     unspecified, but no access ever leaves the buffers described here.
+ *   - int32 is used for every index, as the pages' metadata is int32.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_F32 = 0,   /* IEEE float32 */
+  PA_BF16 = 1,  /* bfloat16 */
+  PA_F16 = 2    /* IEEE float16 */
+} pa_dtype_t;
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_NULL = 1,         /* a required pointer is NULL */
+  PA_ERR_SHAPE = 2,        /* a size argument is negative, zero where it must not be, or overflows int32 indexing */
+  PA_ERR_DTYPE = 3,        /* unknown dtype */
+  PA_ERR_UNSUPPORTED = 4,  /* well formed but not implemented (e.g. head_dim > 256) */
+  PA_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than pa_attention_workspace_size() */
+  PA_ERR_HIP = 6           /* a HIP runtime call or kernel launch failed */
+} pa_status_t;
+
+/* Device-side data-error bits (OR-ed into *d_err). */
+enum {
+  PA_DERR_QLEN_GT_SEQLEN = 1,  /* query_len < 0, seq_len < 0 or query_len > seq_len */
+  PA_DERR_TOKEN_SUM = 2,       /* sum(query_lens) != num_tokens, or query_start_loc inconsistent */
+  PA_DERR_BLOCK_OOB = 4,       /* a block-table entry a sequence needs is < 0 or >= num_blocks,
+                                  or the table is too narrow for seq_len */
+  PA_DERR_SLOT_OOB = 8,        /* a slot_mapping entry >= num_blocks * block_size */
+  PA_DERR_OVERFLOW = 16        /* a prefix sum exceeds INT32_MAX */
+};
+
+/* Human-readable name of a status code (static storage). */
+const char* pa_status_string(pa_status_t s);
+
+/* Description of the HIP error behind the most recent PA_ERR_HIP returned
+ * to this thread ("" if none).  Static storage, valid until the next call. */
+const char* pa_last_hip_error(void);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int32_t pa_version(void);
+
+/*
+ * Kernel selection for pa_attention, process-wide (not thread-safe against
+ * concurrent pa_attention calls; meant for tests and tuning):
+ *   PA_POLICY_AUTO (default)  fast paths where supported, generic elsewhere
+ *   PA_POLICY_GENERIC         always the generic fp32 kernel
+ *   PA_POLICY_FAST            fast paths only; PA_ERR_UNSUPPORTED otherwise
+ * Returns the previous policy, or -1 for an unknown value (unchanged).
+ */
+enum { PA_POLICY_AUTO = 0, PA_POLICY_GENERIC = 1, PA_POLICY_FAST = 2 };
+int32_t pa_set_kernel_policy(int32_t policy);
+
+/*
+ * pa_build_metadata — flat-batch metadata of one step.
+ *
+ * [FS] §2.1 (query_start_loc is a prefix sum with the total appended; each
+ * new token's position; seq_lens after the step), [BN] (lengths 3,5,2 give
+ * [0,3,8,10]), [VP] §3.7 (cu_seqlens_q / cu_seqlens_k), [FS] §2.3 第一步 and
+ * 第二步 (slot = physical block * block_size + offset, found through the
+ * sequence's block table at logical block pos / block_size).
+ *
+ * Inputs:
+ *   query_lens [S]   new tokens of each sequence this step (>= 0)
+ *   seq_lens   [S]   KV length of each sequence after this step, new tokens
+ *                    included (query_len <= seq_len)
+ *   num_seqs S >= 0, num_tokens T >= 0 (must equal sum(query_lens))
+ *   block_tables [S, max_blocks_per_seq], -1 padded; may be NULL, then
+ *                    slot_mapping is not written and the table is not checked
+ *   block_size >= 1, num_blocks >= 1 (only read when block_tables != NULL)
+ * Outputs:
+ *   query_start_loc [S+1]  0, running sum of query_lens, total last
+ *   seq_start_loc   [S+1]  same over seq_lens
+ *   positions       [T]    row i of sequence s: seq_lens[s] - query_lens[s] + i
+ *   token_to_seq    [T]    s
+ *   slot_mapping    [T]    (nullable) physical slot of each new token, -1 when
+ *                          its block-table entry is invalid (PA_DERR_BLOCK_OOB)
+ *   stats           [6]    (nullable) num_decodes (query_len == 1),
+ *                          num_prefills (query_len > 1), num_decode_tokens,
+ *                          num_prefill_tokens, max_query_len, max_seq_len
+ * Device checks: PA_DERR_QLEN_GT_SEQLEN, PA_DERR_TOKEN_SUM, PA_DERR_OVERFLOW,
+ * and (with a table) PA_DERR_BLOCK_OOB for every entry in each sequence's
+ * used range [0, ceil(seq_len / block_size)).
+ */
+pa_status_t pa_build_metadata(const int32_t* query_lens, const int32_t* seq_lens, int32_t num_seqs,
+                              int32_t num_tokens, const int32_t* block_tables,
+                              int32_t max_blocks_per_seq, int32_t block_size, int32_t num_blocks,
+                              int32_t* query_start_loc, int32_t* seq_start_loc, int32_t* positions,
+                              int32_t* token_to_seq, int32_t* slot_mapping, int32_t* stats,
+                              int32_t* d_err, void* stream);
+
+/*
+ * pa_write_kv — scatter this step's new K/V rows into the paged cache.
+ *
+ * [FS] §2.3 第一步 (slot_mapping says where each new token's K/V goes;
+ * written before attention), [VP] §3.7 (store_kvcache(k, v, k_cache,
+ * v_cache, slot_mapping) runs first in Attention.forward).
+ *
+ *   k, v        [T, num_kv_heads, head_dim]  new rows, `dtype`
+ *   slot_mapping [T]  slot of row t; negative = skip the row
+ *   k_cache, v_cache [num_blocks, block_size, num_kv_heads, head_dim], `dtype`;
+ *               slot s is block s / block_size, offset s % block_size
+ * A pure copy: stored bits are moved unchanged; the caches are never read.
+ * Slots >= num_blocks * block_size are skipped and flag PA_DERR_SLOT_OOB.
+ * Two rows with the same non-negative slot are invalid input (the copy-on-
+ * write rule of [VP] §2.1 keeps writers apart); which row wins is unspecified.
+ */
+pa_status_t pa_write_kv(const void* k, const void* v, const int32_t* slot_mapping, int32_t num_tokens,
+                        int32_t num_kv_heads, int32_t head_dim, void* k_cache, void* v_cache,
+                        int32_t num_blocks, int32_t block_size, pa_dtype_t dtype, int32_t* d_err,
+                        void* stream);
+
+/*
+ * Bytes of device workspace pa_attention needs for these sizes (split-K
+ * partial results and the work list).  Depends only on its arguments.
+ */
+size_t pa_attention_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t max_seq_len);
+
+/*
+ * pa_attention — ragged causal paged attention over the cache.
+ *
+ * [FS] §2.3 and §2.3补充 第二步: each sequence s takes its rows
+ * query_start_loc[s] .. query_start_loc[s+1]-1 of the flat batch and reads its
+ * own K/V through block_tables[s]; row i sits at position
+ * p = seq_lens[s] - query_len + i and sees positions 0..p of its own
+ * sequence only.  [VP] §1.1: a decode row is the last row of softmax(QK^T)V.
+ * For query head h the KV head is h / (num_q_heads / num_kv_heads).
+ *
+ *   out[t, h, :] = sum_{j<=p} e^{x_j - max x} V[j, g, :] / sum_{j<=p} e^{x_j - max x},
+ *   x_j = scale * <q[t, h, :], K[j, g, :]>.
+ *
+ *   q    [T, num_q_heads, head_dim], `dtype`
+ *   k_cache, v_cache [num_blocks, block_size, num_kv_heads, head_dim], `dtype`
+ *        (already holding this step's rows: write first, then attend)
+ *   block_tables [S, max_blocks_per_seq], -1 padded; only the first
+ *        ceil(seq_len / block_size) entries of a row are read
+ *   query_start_loc [S+1], seq_lens [S]
+ *   max_query_len, max_seq_len: host-side size hints used to shape the
+ *        launch (like max_seqlen_q / max_seqlen_k in [VP] §3.7).  Results do
+ *        not depend on them being tight; they must be >= 1 when T > 0.
+ *   scale  softmax scale (1/sqrt(head_dim) in the usual model)
+ *   out  [T, num_q_heads, head_dim], `dtype`
+ *   workspace: device memory of at least pa_attention_workspace_size() bytes;
+ *        contents on entry are irrelevant, on exit unspecified.
+ * Arithmetic is fp32 (inputs widened, products and sums in fp32), output
+ * rounded to `dtype` (nearest-even).  Supported: num_q_heads % num_kv_heads
+ * == 0, 1 <= head_dim <= 256, block_size >= 1.  bf16/fp16 with head_dim 128
+ * and block_size a multiple of 16 take the MFMA fast paths; everything else
+ * takes a generic fp32 kernel.
+ * The caches are never written.  Rows of sequences whose metadata is invalid
+ * are written as zeros and flag PA_DERR_*.
+ */
+pa_status_t pa_attention(const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_tables, const int32_t* query_start_loc,
+                         const int32_t* seq_lens, int32_t num_seqs, int32_t num_tokens,
+                         int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                         int32_t max_query_len, int32_t max_seq_len, float scale, pa_dtype_t dtype,
+                         void* out, void* workspace, size_t workspace_bytes, int32_t* d_err,
+                         void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

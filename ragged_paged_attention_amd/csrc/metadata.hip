@@ -1,0 +1,168 @@
+// pa_build_metadata kernels.
+//
+// "vLLM Continuous Batching：从 Forward Shape 理解两个核心参数" §2.1: the flat
+// batch is sliced by query_start_loc, a running sum of query_lens with the
+// total appended; every new token carries its position inside its sequence;
+// §2.3 第一步/第二步: slot = block_table[pos / bs] * bs + pos % bs.
+//
+// Two launches on the caller's stream:
+//   1. scan  — one workgroup of 1024 threads walks the S lengths in chunks,
+//              producing both offset arrays, the counters and length checks.
+//   2. fill  — one workgroup per sequence (grid-strided) writes positions,
+//              token_to_seq and slot_mapping for its rows and checks the used
+//              part of its block-table row.
+// S is at most a few thousand sequences per step, so the single-workgroup scan
+// costs a few microseconds; the fill is spread over the whole chip.
+#include "pa_common.h"
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+constexpr int kScanThreads = 1024;
+constexpr int kWaves = kScanThreads / 64;
+
+// Inclusive scan of a 64-bit value over the workgroup; returns this thread's
+// inclusive prefix and writes the workgroup total to *total.
+__device__ int64_t block_inclusive_scan(int64_t x, int64_t* lds_waves, int64_t* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int off = 1; off < 64; off <<= 1) {
+    int64_t y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) lds_waves[wave] = x;
+  __syncthreads();
+  if (wave == 0) {
+    int64_t w = lane < kWaves ? lds_waves[lane] : 0;
+    for (int off = 1; off < kWaves; off <<= 1) {
+      int64_t y = __shfl_up(w, off, 64);
+      if (lane >= off) w += y;
+    }
+    if (lane < kWaves) lds_waves[lane] = w;
+  }
+  __syncthreads();
+  int64_t prefix = wave > 0 ? lds_waves[wave - 1] : 0;
+  *total = lds_waves[kWaves - 1];
+  __syncthreads();
+  return x + prefix;
+}
+
+__global__ __launch_bounds__(kScanThreads) void meta_scan_kernel(
+    const int32_t* __restrict__ query_lens, const int32_t* __restrict__ seq_lens, int32_t S, int32_t T,
+    int32_t* __restrict__ qsl, int32_t* __restrict__ ssl, int32_t* __restrict__ stats,
+    int32_t* __restrict__ d_err) {
+  __shared__ int64_t lds_q[kWaves];
+  __shared__ int64_t lds_s[kWaves];
+  __shared__ int32_t lds_stat[6];
+  if (threadIdx.x < 6) lds_stat[threadIdx.x] = 0;
+  __syncthreads();
+  int64_t carry_q = 0, carry_s = 0;
+  int32_t n_dec = 0, n_pre = 0, dec_tok = 0, pre_tok = 0, max_q = 0, max_s = 0;
+  int32_t err = 0;
+  for (int32_t base = 0; base < S; base += kScanThreads) {
+    const int32_t idx = base + threadIdx.x;
+    int32_t q = 0, L = 0;
+    if (idx < S) {
+      q = query_lens[idx];
+      L = seq_lens[idx];
+      if (q < 0 || L < 0 || q > L) err |= PA_DERR_QLEN_GT_SEQLEN;
+      q = q < 0 ? 0 : q;
+      L = L < 0 ? 0 : L;
+      n_dec += (q == 1);
+      n_pre += (q > 1);
+      dec_tok += (q == 1) ? 1 : 0;
+      pre_tok += (q > 1) ? q : 0;
+      max_q = max(max_q, q);
+      max_s = max(max_s, L);
+    }
+    int64_t tot_q, tot_s;
+    const int64_t iq = block_inclusive_scan(q, lds_q, &tot_q);
+    const int64_t is = block_inclusive_scan(L, lds_s, &tot_s);
+    if (idx < S) {
+      const int64_t vq = carry_q + iq, vs = carry_s + is;
+      if (vq > INT32_MAX || vs > INT32_MAX) err |= PA_DERR_OVERFLOW;
+      qsl[idx + 1] = static_cast<int32_t>(vq > INT32_MAX ? INT32_MAX : vq);
+      ssl[idx + 1] = static_cast<int32_t>(vs > INT32_MAX ? INT32_MAX : vs);
+    }
+    carry_q += tot_q;
+    carry_s += tot_s;
+  }
+  if (threadIdx.x == 0) {
+    qsl[0] = 0;
+    ssl[0] = 0;
+    if (carry_q != static_cast<int64_t>(T)) err |= PA_DERR_TOKEN_SUM;
+  }
+  if (err) flag(d_err, err);
+  if (stats) {
+    atomicAdd(&lds_stat[0], n_dec);
+    atomicAdd(&lds_stat[1], n_pre);
+    atomicAdd(&lds_stat[2], dec_tok);
+    atomicAdd(&lds_stat[3], pre_tok);
+    atomicMax(&lds_stat[4], max_q);
+    atomicMax(&lds_stat[5], max_s);
+    __syncthreads();
+    if (threadIdx.x < 6) stats[threadIdx.x] = lds_stat[threadIdx.x];
+  }
+}
+
+__global__ __launch_bounds__(256) void meta_fill_kernel(
+    const int32_t* __restrict__ query_lens, const int32_t* __restrict__ seq_lens, int32_t S, int32_t T,
+    const int32_t* __restrict__ qsl, const int32_t* __restrict__ block_tables, int32_t MB, int32_t bs,
+    int32_t NB, int32_t* __restrict__ positions, int32_t* __restrict__ token_to_seq,
+    int32_t* __restrict__ slot_mapping, int32_t* __restrict__ d_err) {
+  for (int32_t s = blockIdx.x; s < S; s += gridDim.x) {
+    int32_t q = query_lens[s];
+    const int32_t L = seq_lens[s];
+    q = q < 0 ? 0 : q;
+    const int32_t start = qsl[s];
+    const int32_t* row = block_tables ? block_tables + static_cast<int64_t>(s) * MB : nullptr;
+    int32_t err = 0;
+    for (int32_t i = threadIdx.x; i < q; i += blockDim.x) {
+      const int64_t t = static_cast<int64_t>(start) + i;
+      if (t >= T) {
+        err |= PA_DERR_TOKEN_SUM;
+        break;
+      }
+      const int32_t pos = L - q + i;
+      positions[t] = pos;
+      token_to_seq[t] = s;
+      if (slot_mapping) {
+        int32_t slot = -1;
+        if (pos >= 0) {
+          const int32_t lb = pos / bs;
+          const int32_t b = lb < MB ? row[lb] : -1;
+          if (b >= 0 && b < NB) slot = b * bs + pos % bs;
+          else err |= PA_DERR_BLOCK_OOB;
+        }
+        slot_mapping[t] = slot;
+      }
+    }
+    if (row && L > 0) {
+      const int32_t used = ceil_div(L, bs);
+      if (used > MB) err |= PA_DERR_BLOCK_OOB;
+      const int32_t n = used < MB ? used : MB;
+      for (int32_t j = threadIdx.x; j < n; j += blockDim.x) {
+        const int32_t b = row[j];
+        if (b < 0 || b >= NB) err |= PA_DERR_BLOCK_OOB;
+      }
+    }
+    if (err) flag(d_err, err);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_metadata(const int32_t* query_lens, const int32_t* seq_lens, int32_t S, int32_t T,
+                           const int32_t* block_tables, int32_t MB, int32_t bs, int32_t NB,
+                           int32_t* qsl, int32_t* ssl, int32_t* positions, int32_t* token_to_seq,
+                           int32_t* slot_mapping, int32_t* stats, int32_t* d_err, hipStream_t stream) {
+  meta_scan_kernel<<<1, kScanThreads, 0, stream>>>(query_lens, seq_lens, S, T, qsl, ssl, stats, d_err);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || S == 0) return e;
+  const int grid = S < 2048 ? S : 2048;
+  meta_fill_kernel<<<grid, 256, 0, stream>>>(query_lens, seq_lens, S, T, qsl, block_tables, MB, bs, NB,
+                                             positions, token_to_seq, slot_mapping, d_err);
+  return hipGetLastError();
+}
+
+}  // namespace pa

@@ -1,0 +1,151 @@
+// C-ABI layer of libpa: argument validation, path selection, launches.
+// Every check here is on host-visible arguments only; nothing waits on the
+// device.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <climits>
+#include <cstdio>
+
+#include "pa.h"
+#include "pa_internal.h"
+
+namespace {
+
+std::atomic<int32_t> g_policy{PA_POLICY_AUTO};
+thread_local char g_last_hip_error[256] = "";
+
+// Clears an error left behind by earlier, unrelated HIP calls in this thread,
+// so that the check after our launches reports only our own failures.
+void clear_stale_error() { (void)hipGetLastError(); }
+
+pa_status_t hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return PA_OK;
+  snprintf(g_last_hip_error, sizeof(g_last_hip_error), "%s: %s (%d)", where, hipGetErrorString(e),
+           static_cast<int>(e));
+  return PA_ERR_HIP;
+}
+
+bool bad_dtype(pa_dtype_t d) { return d != PA_F32 && d != PA_BF16 && d != PA_F16; }
+int64_t elem_bytes(pa_dtype_t d) { return d == PA_F32 ? 4 : 2; }
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_string(pa_status_t s) {
+  switch (s) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_NULL: return "PA_ERR_NULL: a required pointer is NULL";
+    case PA_ERR_SHAPE: return "PA_ERR_SHAPE: invalid size argument";
+    case PA_ERR_DTYPE: return "PA_ERR_DTYPE: unknown dtype";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: shape or dtype not implemented";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing or too small";
+    case PA_ERR_HIP: return "PA_ERR_HIP: HIP runtime or launch failure";
+  }
+  return "PA_ERR_UNKNOWN";
+}
+
+int32_t pa_version(void) { return 100; }
+
+const char* pa_last_hip_error(void) { return g_last_hip_error; }
+
+int32_t pa_set_kernel_policy(int32_t policy) {
+  if (policy != PA_POLICY_AUTO && policy != PA_POLICY_GENERIC && policy != PA_POLICY_FAST) return -1;
+  return g_policy.exchange(policy);
+}
+
+pa_status_t pa_build_metadata(const int32_t* query_lens, const int32_t* seq_lens, int32_t num_seqs,
+                              int32_t num_tokens, const int32_t* block_tables,
+                              int32_t max_blocks_per_seq, int32_t block_size, int32_t num_blocks,
+                              int32_t* query_start_loc, int32_t* seq_start_loc, int32_t* positions,
+                              int32_t* token_to_seq, int32_t* slot_mapping, int32_t* stats,
+                              int32_t* d_err, void* stream) {
+  if (num_seqs < 0 || num_tokens < 0) return PA_ERR_SHAPE;
+  if (!query_start_loc || !seq_start_loc) return PA_ERR_NULL;
+  if (num_seqs > 0 && (!query_lens || !seq_lens)) return PA_ERR_NULL;
+  if (num_tokens > 0 && (!positions || !token_to_seq)) return PA_ERR_NULL;
+  if (block_tables) {
+    if (max_blocks_per_seq < 0 || block_size < 1 || num_blocks < 1) return PA_ERR_SHAPE;
+    if (static_cast<int64_t>(num_blocks) * block_size > INT32_MAX) return PA_ERR_SHAPE;
+    if (num_tokens > 0 && !slot_mapping) return PA_ERR_NULL;
+  } else {
+    slot_mapping = nullptr;
+  }
+  clear_stale_error();
+  hipError_t e = pa::launch_metadata(query_lens, seq_lens, num_seqs, num_tokens, block_tables,
+                                     max_blocks_per_seq, block_size, num_blocks, query_start_loc,
+                                     seq_start_loc, positions, token_to_seq, slot_mapping, stats, d_err,
+                                     static_cast<hipStream_t>(stream));
+  return hip_status(e, "pa_build_metadata");
+}
+
+pa_status_t pa_write_kv(const void* k, const void* v, const int32_t* slot_mapping, int32_t num_tokens,
+                        int32_t num_kv_heads, int32_t head_dim, void* k_cache, void* v_cache,
+                        int32_t num_blocks, int32_t block_size, pa_dtype_t dtype, int32_t* d_err,
+                        void* stream) {
+  if (bad_dtype(dtype)) return PA_ERR_DTYPE;
+  if (num_tokens < 0 || num_kv_heads < 1 || head_dim < 1 || num_blocks < 1 || block_size < 1)
+    return PA_ERR_SHAPE;
+  if (static_cast<int64_t>(num_blocks) * block_size > INT32_MAX) return PA_ERR_SHAPE;
+  if (num_tokens == 0) return PA_OK;
+  if (!k || !v || !slot_mapping || !k_cache || !v_cache) return PA_ERR_NULL;
+  const int64_t row_bytes = static_cast<int64_t>(num_kv_heads) * head_dim * elem_bytes(dtype);
+  clear_stale_error();
+  hipError_t e = pa::launch_write_kv(k, v, slot_mapping, num_tokens, row_bytes, k_cache, v_cache,
+                                     static_cast<int64_t>(num_blocks) * block_size, d_err,
+                                     static_cast<hipStream_t>(stream));
+  return hip_status(e, "pa_write_kv");
+}
+
+size_t pa_attention_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t max_seq_len) {
+  if (num_seqs < 0 || num_tokens < 0 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1)
+    return 0;
+  return pa::fast_workspace_bytes(num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim,
+                                  max_seq_len);
+}
+
+pa_status_t pa_attention(const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_tables, const int32_t* query_start_loc,
+                         const int32_t* seq_lens, int32_t num_seqs, int32_t num_tokens,
+                         int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                         int32_t max_query_len, int32_t max_seq_len, float scale, pa_dtype_t dtype,
+                         void* out, void* workspace, size_t workspace_bytes, int32_t* d_err,
+                         void* stream) {
+  if (bad_dtype(dtype)) return PA_ERR_DTYPE;
+  if (num_seqs < 0 || num_tokens < 0 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1 ||
+      block_size < 1 || num_blocks < 1 || max_blocks_per_seq < 0)
+    return PA_ERR_SHAPE;
+  if (num_q_heads % num_kv_heads != 0) return PA_ERR_SHAPE;
+  if (static_cast<int64_t>(num_blocks) * block_size > INT32_MAX) return PA_ERR_SHAPE;
+  if (num_q_heads > 65535) return PA_ERR_UNSUPPORTED;
+  if (head_dim > 256) return PA_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PA_OK;
+  if (num_seqs == 0) return PA_ERR_SHAPE;
+  if (max_query_len < 1 || max_seq_len < 1) return PA_ERR_SHAPE;
+  if (!q || !k_cache || !v_cache || !block_tables || !query_start_loc || !seq_lens || !out)
+    return PA_ERR_NULL;
+
+  pa::AttnArgs a{q, k_cache, v_cache, block_tables, query_start_loc, seq_lens,
+                 num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim, block_size,
+                 num_blocks, max_blocks_per_seq, max_query_len, max_seq_len, scale, dtype,
+                 out, workspace, workspace_bytes, d_err};
+  const int32_t policy = g_policy.load();
+  const bool fast_ok = pa::fast_path_supported(a);
+  hipError_t e;
+  clear_stale_error();
+  if (policy == PA_POLICY_GENERIC || (policy == PA_POLICY_AUTO && !fast_ok)) {
+    e = pa::launch_attn_generic(a, static_cast<hipStream_t>(stream));
+  } else {
+    if (!fast_ok) return PA_ERR_UNSUPPORTED;
+    const size_t need = pa::fast_workspace_bytes(num_seqs, num_tokens, num_q_heads, num_kv_heads,
+                                                 head_dim, max_seq_len);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE;
+    e = pa::launch_attn_fast(a, static_cast<hipStream_t>(stream));
+  }
+  return hip_status(e, "pa_attention");
+}
+
+}  // extern "C"

@@ -1,0 +1,48 @@
+// Host-side launch interfaces between the C-ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "pa.h"
+
+namespace pa {
+
+// metadata.hip
+hipError_t launch_metadata(const int32_t* query_lens, const int32_t* seq_lens, int32_t S, int32_t T,
+                           const int32_t* block_tables, int32_t MB, int32_t bs, int32_t NB,
+                           int32_t* qsl, int32_t* ssl, int32_t* positions, int32_t* token_to_seq,
+                           int32_t* slot_mapping, int32_t* stats, int32_t* d_err, hipStream_t stream);
+
+// write_kv.hip
+hipError_t launch_write_kv(const void* k, const void* v, const int32_t* slot_mapping, int32_t T,
+                           int64_t row_bytes, void* k_cache, void* v_cache, int64_t num_slots,
+                           int32_t* d_err, hipStream_t stream);
+
+// Shape of one pa_attention call, as the kernels see it.
+struct AttnArgs {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* qsl;
+  const int32_t* seq_lens;
+  int32_t S, T, Hq, Hkv, D, bs, NB, MB, max_qlen, max_seqlen;
+  float scale;
+  pa_dtype_t dtype;
+  void* out;
+  void* workspace;
+  size_t workspace_bytes;
+  int32_t* d_err;
+};
+
+// attn_generic.hip: any dtype, head_dim <= 256, any block size, fp32 math.
+hipError_t launch_attn_generic(const AttnArgs& a, hipStream_t stream);
+
+// attn_fast.hip: bf16/f16, head_dim 128, block_size % 16 == 0.
+bool fast_path_supported(const AttnArgs& a);
+size_t fast_workspace_bytes(int32_t S, int32_t T, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_seqlen);
+hipError_t launch_attn_fast(const AttnArgs& a, hipStream_t stream);
+
+}  // namespace pa

@@ -1,0 +1,60 @@
+"""The C-ABI library loads and exports every entry point include/pa.h
+declares; host-side argument checks return their status codes without
+touching a GPU (null pointers and bad sizes are rejected before any launch)."""
+import ctypes
+import subprocess
+
+import pytest
+
+import ragged_paged_attention_amd as rpa
+from ragged_paged_attention_amd import _lib
+
+
+def test_library_loads_and_exports_all_declared_symbols():
+    lib = rpa.library()
+    names = rpa.declared_symbols()
+    assert {"pa_build_metadata", "pa_write_kv", "pa_attention", "pa_attention_workspace_size",
+            "pa_status_string"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"libpa.so does not export {n}"
+    out = subprocess.run(["nm", "-D", "--defined-only", rpa.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert set(names) <= exported
+
+
+def test_version_and_status_strings():
+    assert rpa.pa_version() >= 100
+    for code in range(7):
+        assert rpa.status_string(code).startswith("PA_")
+
+
+def test_kernel_policy_roundtrip():
+    prev = rpa.pa_set_kernel_policy(rpa.PA_POLICY_GENERIC)
+    assert rpa.pa_set_kernel_policy(prev) == rpa.PA_POLICY_GENERIC
+    assert rpa.pa_set_kernel_policy(7) == -1
+
+
+def test_host_side_rejections_need_no_gpu():
+    lib = _lib.library()
+    NULL = None
+    # negative sizes
+    assert lib.pa_build_metadata(NULL, NULL, -1, 0, NULL, 0, 1, 1, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL) == 2
+    # missing outputs
+    assert lib.pa_build_metadata(NULL, NULL, 0, 0, NULL, 0, 1, 1, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL) == 1
+    # bad dtype
+    assert lib.pa_write_kv(NULL, NULL, NULL, 1, 1, 1, NULL, NULL, 1, 1, 9, NULL, NULL) == 3
+    # num_blocks * block_size overflowing int32 slots
+    assert lib.pa_write_kv(NULL, NULL, NULL, 1, 1, 1, NULL, NULL, 1 << 20, 1 << 12, 1, NULL, NULL) == 2
+    # nothing to write is fine
+    assert lib.pa_write_kv(NULL, NULL, NULL, 0, 1, 1, NULL, NULL, 1, 1, 1, NULL, NULL) == 0
+    att = lambda **kw: lib.pa_attention(*_attn_args(**kw))
+    assert att(Hq=6, Hkv=4) == 2          # Hq % Hkv != 0
+    assert att(D=512) == 4                # head_dim > 256
+    assert att(T=0) == 0                  # empty batch: nothing to do
+    assert att() == 1                     # null pointers
+    assert att(max_q=0) == 2              # size hints must be >= 1
+    assert lib.pa_attention_workspace_size(4, 100, 32, 32, 128, 2001) >= 0
+
+
+def _attn_args(T=3, Hq=4, Hkv=2, D=16, max_q=2, S=2):
+    return [None] * 6 + [S, T, Hq, Hkv, D, 16, 8, 4, max_q, 8, ctypes.c_float(0.25), 1, None, None, 0, None, None]

@@ -1,0 +1,198 @@
+"""GPU parity: the HIP library (through the C ABI) against the CPU oracle.
+
+Metadata and the KV scatter must match bit for bit; attention must match to
+max-abs-error 1e-5 for fp32 inputs and 2e-2 for bf16/f16 inputs (fp32
+accumulation), on the same seeded inputs.  Unwritten pool slots hold NaN, so
+any read outside a sequence's visible rows shows up as NaN.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import ragged_paged_attention_amd as rpa
+from workloads import config, random_batch, relabel_blocks, unshare
+from workloads.device import to_numpy_bits
+
+from tests.gpu_path import GpuRun, max_abs_err, tol_for
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _policy_reset():
+    prev = rpa.pa_set_kernel_policy(rpa.PA_POLICY_AUTO)
+    yield
+    rpa.pa_set_kernel_policy(prev)
+
+
+def _meta_equal(gpu_md, ref: oracle.Metadata, T):
+    assert gpu_md["query_start_loc"].cpu().numpy().tolist() == ref.query_start_loc.tolist()
+    assert gpu_md["seq_start_loc"].cpu().numpy().tolist() == ref.seq_start_loc.tolist()
+    assert gpu_md["positions"].cpu().numpy().tolist() == ref.positions.tolist()
+    assert gpu_md["token_to_seq"].cpu().numpy().tolist() == ref.token_to_seq.tolist()
+    assert gpu_md["slot_mapping"].cpu().numpy().tolist() == ref.slot_mapping.tolist()
+    assert gpu_md["stats"].cpu().numpy().tolist() == ref.stats.tolist()
+
+
+def _bits(a):
+    a = np.asarray(a)
+    return a.view(np.uint32) if a.dtype == np.float32 else a.view(np.uint16)
+
+
+SMALL = [("tiny_mixed", lambda: config(1))] + \
+    [(f"random{s}", (lambda s=s: random_batch(s, S=5, Hq=4, Hkv=2, D=16, bs=4, max_ctx=40, max_q=9)))
+     for s in range(3)] + \
+    [(f"cfg{n}_small", (lambda n=n: config(n, scale_down=32))) for n in (2, 3, 4, 5)]
+
+
+@pytest.mark.parametrize("name,make", SMALL, ids=[n for n, _ in SMALL])
+def test_metadata_and_scatter_bitexact(name, make):
+    w = make()
+    print(f"[case] {name} {w.summary()}", flush=True)
+    g = GpuRun(w).run()
+    md, kc, vc, _ = oracle.run_step(w, rows=[0])
+    _meta_equal(g.meta, md, w.num_tokens)
+    assert np.array_equal(_bits(to_numpy_bits(g.k_cache)), _bits(kc)), "k_cache differs"
+    assert np.array_equal(_bits(to_numpy_bits(g.v_cache)), _bits(vc)), "v_cache differs"
+    assert g.err() == 0
+
+
+def test_tiny_mixed_fp32_attention():
+    """The forward-shape walkthrough batch (B, C decode; A prefills 5)."""
+    w = config(1)
+    g = GpuRun(w).run()
+    _, _, _, ref = oracle.run_step(w)
+    err = max_abs_err(g.out, ref)
+    print(f"[tiny_mixed] max_abs_err={err:.3e}", flush=True)
+    assert err <= 1e-5
+    # a0 sees only itself: the output is its own V row, exactly
+    G = w.num_q_heads // w.num_kv_heads
+    v64 = oracle.widen(w.step.v[2], w.dtype)
+    out = g.out.double().cpu().numpy()
+    for h in range(w.num_q_heads):
+        assert np.array_equal(out[2, h], v64[h // G])
+    assert g.err() == 0
+
+
+SWEEP = []
+for seed in range(6):
+    for dtype in ("f32", "bf16", "f16"):
+        for (Hq, Hkv, D, bs) in ((4, 2, 16, 4), (8, 1, 64, 16), (4, 4, 128, 16), (8, 2, 128, 32), (2, 1, 32, 1)):
+            SWEEP.append(dict(seed=seed * 7 + 100, dtype=dtype, Hq=Hq, Hkv=Hkv, D=D, bs=bs))
+
+
+@pytest.mark.parametrize("policy", ["auto", "generic"])
+@pytest.mark.parametrize("case", SWEEP, ids=lambda c: f"s{c['seed']}-{c['dtype']}-{c['Hq']}x{c['Hkv']}-D{c['D']}-bs{c['bs']}")
+def test_random_sweep(case, policy):
+    rpa.pa_set_kernel_policy(rpa.PA_POLICY_GENERIC if policy == "generic" else rpa.PA_POLICY_AUTO)
+    w = random_batch(case["seed"], S=6, Hq=case["Hq"], Hkv=case["Hkv"], D=case["D"], bs=case["bs"],
+                     dtype=case["dtype"], max_ctx=70, max_q=40, decode_frac=0.5)
+    g = GpuRun(w).run()
+    _, _, _, ref = oracle.run_step(w)
+    err = max_abs_err(g.out, ref)
+    assert err <= tol_for(w.dtype), f"max_abs_err {err}"
+    assert g.err() == 0
+
+
+@pytest.mark.parametrize("policy", ["auto", "generic"])
+@pytest.mark.parametrize("n", [2, 3, 4, 5])
+def test_scaled_configs(n, policy):
+    """Same structure and head shapes as the full workloads, lengths / 16:
+    several tiles per sequence, ragged tails, every row checked."""
+    rpa.pa_set_kernel_policy(rpa.PA_POLICY_GENERIC if policy == "generic" else rpa.PA_POLICY_AUTO)
+    w = config(n, scale_down=16)
+    print(f"[case] scaled config {n} {w.summary()}", flush=True)
+    g = GpuRun(w).run()
+    _, _, _, ref = oracle.run_step(w)
+    err = max_abs_err(g.out, ref)
+    print(f"[scaled cfg{n} {policy}] max_abs_err={err:.3e}", flush=True)
+    assert err <= tol_for(w.dtype)
+    assert g.err() == 0
+
+
+def test_placement_invariance_bitexact():
+    """Relabelled physical blocks give bit-identical outputs."""
+    w = config(4, scale_down=16)
+    perm = np.random.default_rng(5).permutation(w.num_blocks)
+    a = GpuRun(w).run().out
+    b = GpuRun(relabel_blocks(w, perm)).run().out
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_sharing_invariance_bitexact():
+    """Shared prefix blocks and private copies give bit-identical outputs."""
+    w = config(5, scale_down=16)
+    w.num_blocks += int((w.step.block_tables >= 0).sum())
+    used = set(int(b) for b in w.step.block_tables.ravel() if b >= 0)
+    u = unshare(w, [b for b in range(w.num_blocks) if b not in used])
+    a = GpuRun(w).run().out
+    b = GpuRun(u).run().out
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_deterministic():
+    w = config(4, scale_down=8)
+    g = GpuRun(w).run()
+    first = g.out.clone()
+    g.step()
+    torch.cuda.synchronize()
+    assert torch.equal(first.view(torch.int16), g.out.view(torch.int16))
+
+
+def test_error_flags_from_host_forced_data():
+    """Invalid metadata is flagged on the device and no access leaves the
+    buffers (the pool is NaN-poisoned; outputs of flagged rows are zero)."""
+    w = config(1)
+    g = GpuRun(w).run()          # history and this step's rows are in the pool
+    dev = g.db
+    # query_len > seq_len for sequence 0
+    bad_sl = dev.seq_lens.clone()
+    bad_sl[0] = 0
+    qsl = torch.tensor([0, 1, 2, 7], dtype=torch.int32, device="cuda")
+    d_err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    rpa.pa_attention(dev.q, g.k_cache, g.v_cache, dev.block_tables, qsl, bad_sl, 5, 8, w.scale, d_err=d_err)
+    torch.cuda.synchronize()
+    assert int(d_err.item()) & rpa.PA_DERR_QLEN_GT_SEQLEN
+    # a -1 block inside the used range
+    bad_bt = dev.block_tables.clone()
+    bad_bt[0, 0] = -1
+    d_err.zero_()
+    md = rpa.pa_build_metadata(dev.query_lens, dev.seq_lens, w.num_tokens, bad_bt, w.block_size, w.num_blocks,
+                               d_err=d_err)
+    out = rpa.pa_attention(dev.q, g.k_cache, g.v_cache, bad_bt, md["query_start_loc"], dev.seq_lens, 5, 8,
+                           w.scale, d_err=d_err)
+    torch.cuda.synchronize()
+    assert int(d_err.item()) & rpa.PA_DERR_BLOCK_OOB
+    assert torch.isfinite(out[1:]).all()
+    # sum(query_lens) != num_tokens
+    d_err.zero_()
+    rpa.pa_build_metadata(dev.query_lens, dev.seq_lens, w.num_tokens + 1, dev.block_tables, w.block_size,
+                          w.num_blocks, d_err=d_err)
+    torch.cuda.synchronize()
+    assert int(d_err.item()) & rpa.PA_DERR_TOKEN_SUM
+    # slot beyond the pool
+    d_err.zero_()
+    slots = torch.full((w.num_tokens,), -1, dtype=torch.int32, device="cuda")
+    slots[0] = w.num_blocks * w.block_size
+    before = g.k_cache.clone()
+    rpa.pa_write_kv(dev.k, dev.v, slots, g.k_cache, g.v_cache, d_err=d_err)
+    torch.cuda.synchronize()
+    assert int(d_err.item()) & rpa.PA_DERR_SLOT_OOB
+    assert torch.equal(before.view(torch.int32), g.k_cache.view(torch.int32))
+
+
+def test_workspace_too_small_is_rejected():
+    w = config(3, scale_down=8)
+    g = GpuRun(w).fill_history()
+    need = rpa.pa_attention_workspace_size(w.num_seqs, w.num_tokens, w.num_q_heads, w.num_kv_heads,
+                                           w.head_dim, w.max_seq_len)
+    if need == 0:
+        pytest.skip("this shape needs no workspace")
+    md = rpa.pa_build_metadata(g.db.query_lens, g.db.seq_lens, w.num_tokens, g.db.block_tables, w.block_size,
+                               w.num_blocks)
+    small = torch.empty(need - 1, dtype=torch.uint8, device="cuda")
+    with pytest.raises(rpa.PAError) as e:
+        rpa.pa_attention(g.db.q, g.k_cache, g.v_cache, g.db.block_tables, md["query_start_loc"], g.db.seq_lens,
+                         w.max_query_len, w.max_seq_len, w.scale, workspace=small)
+    assert e.value.status == 5
