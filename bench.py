@@ -1,0 +1,202 @@
+"""Throughput of one continuous-batching attention step on one MI355X.
+
+A step is the whole hot path over one batch, in the order the pages give
+("vLLM Continuous Batching：从 Forward Shape 理解两个核心参数" §2.3): build the
+flat-batch metadata, scatter the new K/V by slot_mapping, then ragged paged
+attention.  All three run as libpa kernels (C ABI) on the current stream.
+
+Default workload: the chunked-prefill mixed batch (240 decode sequences with
+log-uniform contexts 128..8192 plus 16 prefill chunks of 497 tokens with
+0..4096 earlier context; T = 8192, GQA 32/8, head_dim 128, block_size 16,
+bf16).  The decode-only batch (100 x 2001-token contexts, 32/32 heads) is
+timed too, for the decode KV-read bandwidth and the roofline line.
+
+Prints ONE JSON line.  Inputs are seeded synthetic data, resident in HBM
+before the timed region starts.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, TFLOP/s
+METRIC = "decode KV-read GB/s (% HBM peak) + mixed-batch attn tokens/s, 1 MI355X"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=4, help="workload for the step (1-5)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["step", "decode"], default=None,
+                    help="run one leg only (for profiling)")
+    ap.add_argument("--cpu-sample-rows", type=int, default=2048)
+    return ap.parse_args()
+
+
+class Timer:
+    """HIP events on torch's current stream, which is the stream every libpa
+    call below is enqueued on."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def time(self, fn, iters, warmup):
+        torch = self.torch
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(iters):
+            fn()
+        end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / iters  # ms
+
+
+def setup(w, torch):
+    from tests.gpu_path import GpuRun
+    g = GpuRun(w).fill_history()
+    torch.cuda.synchronize()
+    return g
+
+
+def step_fn(g, w, rpa, workspace, meta_out):
+    db = g.db
+    from ragged_paged_attention_amd.step import forward_step
+
+    def fn():
+        forward_step(db.q, db.k, db.v, g.k_cache, g.v_cache, db.query_lens, db.seq_lens, db.block_tables,
+                     w.scale, max(1, w.max_query_len), max(1, w.max_seq_len), out=g.out_buf,
+                     workspace=workspace, meta_out=meta_out)
+    return fn
+
+
+def cpu_baseline(w, rows_wanted, seed=0):
+    """The oracle, as it stands, on a random sample of the step's rows: its
+    metadata, its KV write of the step's rows, and attention for the sampled
+    rows.  Pool filled with history first (untimed, like the GPU leg)."""
+    import numpy as np
+    import oracle
+    from threadpoolctl import threadpool_limits
+
+    shape = w.pool_shape()
+    kc = oracle.empty_pool(shape, w.dtype, w.pool_fill())
+    vc = oracle.empty_pool(shape, w.dtype, w.pool_fill())
+    oracle.fill_history(w.hist, kc, vc, w.block_size)
+    rng = np.random.default_rng(seed)
+    rows = sorted(rng.choice(w.num_tokens, size=min(rows_wanted, w.num_tokens), replace=False).tolist())
+    st = w.step
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        md = oracle.build_metadata(st.query_lens, st.seq_lens, st.num_tokens, st.block_tables, w.block_size,
+                                   w.num_blocks)
+        oracle.write_kv(st.k, st.v, md.slot_mapping, kc, vc)
+        oracle.attention(w.q, kc, vc, st.block_tables, md.query_start_loc, st.seq_lens, w.num_kv_heads,
+                         w.scale, w.dtype, rows=rows)
+        dt = time.perf_counter() - t0
+    return {"value": len(rows) / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{len(rows)} random rows of the {w.num_tokens}-token step (seed {seed}), metadata + "
+                      f"KV write of all new rows + fp64 attention of the sampled rows, {dt:.2f} s, BLAS pinned to 1 thread"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): this build has no multi-GPU path",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import ragged_paged_attention_amd as rpa
+    from workloads import accounting, config
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    timer = Timer(torch)
+    result = {"metric": METRIC, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+              "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "data": "synthetic"}
+
+    # ---------------- step on the mixed batch ----------------
+    if args.only in (None, "step"):
+        t0 = time.time()
+        w = config(args.config, poison=False)
+        print(f"[bench] generated config {args.config} {w.summary()} in {time.time() - t0:.1f}s", file=sys.stderr,
+              flush=True)
+        g = setup(w, torch)
+        g.out_buf = torch.empty_like(g.db.q)
+        need = rpa.pa_attention_workspace_size(w.num_seqs, w.num_tokens, w.num_q_heads, w.num_kv_heads,
+                                               w.head_dim, w.max_seq_len)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+        meta_out = {}
+        fn = step_fn(g, w, rpa, ws, None)
+        ms = timer.time(fn, args.steps, args.warmup)
+        # per-call split of the step
+        db = g.db
+        md = rpa.pa_build_metadata(db.query_lens, db.seq_lens, w.num_tokens, db.block_tables, w.block_size,
+                                   w.num_blocks)
+        ms_meta = timer.time(lambda: rpa.pa_build_metadata(db.query_lens, db.seq_lens, w.num_tokens,
+                                                           db.block_tables, w.block_size, w.num_blocks, out=md),
+                             args.steps, 2)
+        ms_write = timer.time(lambda: rpa.pa_write_kv(db.k, db.v, md["slot_mapping"], g.k_cache, g.v_cache),
+                              args.steps, 2)
+        attn = lambda: rpa.pa_attention(db.q, g.k_cache, g.v_cache, db.block_tables, md["query_start_loc"],
+                                        db.seq_lens, w.max_query_len, w.max_seq_len, w.scale, out=g.out_buf,
+                                        workspace=ws)
+        ms_attn = timer.time(attn, args.steps, 2)
+        kv_bytes = accounting.kv_read_bytes(w.step.seq_lens, w.num_kv_heads, w.head_dim, w.dtype)
+        flops = accounting.attention_flops(w.step.query_lens, w.step.seq_lens, w.num_q_heads, w.head_dim)
+        ql = w.step.query_lens
+        result.update({
+            "value": w.num_tokens / (ms / 1e3), "ms_per_step": ms, "dtype": w.dtype,
+            "config": {"workload": w.name, "global_batch": w.num_seqs, "tokens": w.num_tokens,
+                       "n_decode": int((ql == 1).sum()), "n_prefill": int((ql > 1).sum()),
+                       "seq_len_max": w.max_seq_len, "heads": f"{w.num_q_heads}/{w.num_kv_heads}",
+                       "head_dim": w.head_dim, "block_size": w.block_size, "seed": w.seed},
+            "step_split_ms": {"pa_build_metadata": ms_meta, "pa_write_kv": ms_write, "pa_attention": ms_attn},
+            "step_kv_bytes": kv_bytes, "step_flops": flops,
+        })
+        if not args.no_cpu_baseline:
+            w_cpu = config(args.config, poison=False)
+            result["cpu_baseline"] = cpu_baseline(w_cpu, args.cpu_sample_rows)
+        del g, ws
+        torch.cuda.empty_cache()
+
+    # ---------------- decode-only batch: KV-read bandwidth ----------------
+    if args.only in (None, "decode"):
+        w3 = config(3, poison=False)
+        g3 = setup(w3, torch)
+        g3.out_buf = torch.empty_like(g3.db.q)
+        db = g3.db
+        md3 = rpa.pa_build_metadata(db.query_lens, db.seq_lens, w3.num_tokens, db.block_tables, w3.block_size,
+                                    w3.num_blocks)
+        rpa.pa_write_kv(db.k, db.v, md3["slot_mapping"], g3.k_cache, g3.v_cache)
+        need = rpa.pa_attention_workspace_size(w3.num_seqs, w3.num_tokens, w3.num_q_heads, w3.num_kv_heads,
+                                               w3.head_dim, w3.max_seq_len)
+        ws3 = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+        attn3 = lambda: rpa.pa_attention(db.q, g3.k_cache, g3.v_cache, db.block_tables, md3["query_start_loc"],
+                                         db.seq_lens, w3.max_query_len, w3.max_seq_len, w3.scale, out=g3.out_buf,
+                                         workspace=ws3)
+        ms3 = timer.time(attn3, max(args.steps, 20), args.warmup)
+        kv3 = accounting.kv_read_bytes(w3.step.seq_lens, w3.num_kv_heads, w3.head_dim, w3.dtype)
+        gbs = kv3 / (ms3 / 1e3) / 1e9
+        result["decode_kv_read"] = {"workload": w3.name, "GBps": gbs, "frac_hbm_peak": gbs / HBM_PEAK_GBS,
+                                    "kv_bytes": kv3, "ms": ms3, "tokens": w3.num_tokens,
+                                    "seqs": w3.num_seqs, "seq_len": w3.max_seq_len}
+        result["roofline"] = {"bound": "hbm", "kernel": "pa_attention (decode batch)", "achieved": gbs,
+                              "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": None}
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -39,6 +39,8 @@ struct AttnArgs {
 
 // attn_generic.hip: any dtype, head_dim <= 256, any block size, fp32 math.
 hipError_t launch_attn_generic(const AttnArgs& a, hipStream_t stream);
+// Same kernel, skipping rows of sequences with query_len * (Hq/Hkv) <= skip_rows_le.
+hipError_t launch_attn_generic_rows(const AttnArgs& a, int32_t skip_rows_le, hipStream_t stream);
 
 // attn_fast.hip: bf16/f16, head_dim 128, block_size % 16 == 0.
 bool fast_path_supported(const AttnArgs& a);
