@@ -37,7 +37,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=4, help="workload for the step (1-5)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["step", "decode"], default=None,
+    ap.add_argument("--only", choices=["step", "decode", "prefill"], default=None,
                     help="run one leg only (for profiling)")
     ap.add_argument("--cpu-sample-rows", type=int, default=2048)
     return ap.parse_args()
@@ -195,6 +195,22 @@ def main():
                                     "seqs": w3.num_seqs, "seq_len": w3.max_seq_len}
         result["roofline"] = {"bound": "hbm", "kernel": "pa_attention (decode batch)", "achieved": gbs,
                               "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": None}
+    # ---------------- ragged prefill batch: MFMA throughput ----------------
+    if args.only in (None, "prefill"):
+        w2 = config(2, poison=False)
+        g2 = setup(w2, torch)
+        g2.out_buf = torch.empty_like(g2.db.q)
+        db = g2.db
+        md2 = rpa.pa_build_metadata(db.query_lens, db.seq_lens, w2.num_tokens, db.block_tables, w2.block_size,
+                                    w2.num_blocks)
+        rpa.pa_write_kv(db.k, db.v, md2["slot_mapping"], g2.k_cache, g2.v_cache)
+        attn2 = lambda: rpa.pa_attention(db.q, g2.k_cache, g2.v_cache, db.block_tables, md2["query_start_loc"],
+                                         db.seq_lens, w2.max_query_len, w2.max_seq_len, w2.scale, out=g2.out_buf)
+        ms2 = timer.time(attn2, max(args.steps, 20), args.warmup)
+        fl2 = accounting.attention_flops(w2.step.query_lens, w2.step.seq_lens, w2.num_q_heads, w2.head_dim)
+        tf = fl2 / (ms2 / 1e3) / 1e12
+        result["prefill_mfma"] = {"workload": w2.name, "TFLOPs": tf, "frac_bf16_peak": tf / BF16_PEAK_TFLOPS,
+                                  "flops": fl2, "ms": ms2, "tokens": w2.num_tokens}
     print(json.dumps(result), flush=True)
 
 

@@ -21,7 +21,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpa.so")
 ARCH = "gfx950"
 
-SOURCES = ["pa_api.cpp", "metadata.hip", "write_kv.hip", "attn_generic.hip", "attn_fast.hip"]
+SOURCES = ["pa_api.cpp", "metadata.hip", "write_kv.hip", "attn_generic.hip", "attn_fast.hip",
+           "attn_prefill.hip"]
 
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

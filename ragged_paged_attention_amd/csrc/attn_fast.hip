@@ -27,60 +27,17 @@
 // A part writes (m, l, O) partials to the workspace; a merge kernel combines
 // parts with the rescaling algebra.  A sequence with one part writes out
 // directly.
+#include "mfma_common.h"
 #include "pa_common.h"
 #include "pa_internal.h"
 
 namespace pa {
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-constexpr int kD = 128;             // head_dim of the fast paths
-constexpr int kChunk = 16;          // tokens per MFMA tile
-constexpr int kVRowBytes = 288;     // LDS row pitch of a staged V tile (256 + 32)
 constexpr int kPartFloats = 132;    // per partial row: O[128], m, l, pad
 constexpr int kMaxRows = 16;        // query rows of one decode item
 constexpr int kTargetItems = 8192;  // decode work items wanted to fill 256 CUs
 constexpr int kMinChunks = 16;      // do not split contexts below 256 tokens per part
-
-// --------------------------------------------------------------------------
-// per-dtype MFMA and conversions
-// --------------------------------------------------------------------------
-template <class F> struct Mma;
-template <> struct Mma<BF16> {
-  static __device__ __forceinline__ f32x4_t qk(uint4 a, uint4 b, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ f32x4_t pv(i16x4_t a, i16x4_t b, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ uint16_t cvt(float x) {
-    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
-  }
-};
-template <> struct Mma<F16> {
-  static __device__ __forceinline__ f32x4_t qk(uint4 a, uint4 b, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
-                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ f32x4_t pv(i16x4_t a, i16x4_t b, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a),
-                                                 __builtin_bit_cast(f16x4_t, b), c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ uint16_t cvt(float x) {
-    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
-  }
-};
-
-__device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
-
-__device__ __forceinline__ float xor_max(float v, int m) { return fmaxf(v, __shfl_xor(v, m, 64)); }
-__device__ __forceinline__ float xor_sum(float v, int m) { return v + __shfl_xor(v, m, 64); }
 
 // Split of a context of `nchunks` 16-token chunks into parts: at most P parts,
 // none below kMinChunks chunks unless the whole context is, none empty.
@@ -259,8 +216,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
     const int rd_off = (4 * grp + (r >> 2)) * kVRowBytes + 8 * (r & 3);
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-      const i16x4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) i16x4_t*)(vlds + rd_off + 32 * dt));
+      const i16x4_t va = lds_read_tr16(vlds + rd_off + 32 * dt);
       o[dt] = M::pv(va, pb, o[dt]);
     }
     __asm__ volatile("" ::: "memory");
@@ -376,8 +332,8 @@ hipError_t launch_attn_fast(const AttnArgs& a, hipStream_t stream) {
   if (items > INT32_MAX) return hipErrorInvalidValue;
   d.n_items = static_cast<int32_t>(items);
 
-  // prefill-class rows (query_len * G > 16) go through the generic kernel
-  hipError_t e = launch_attn_generic_rows(a, kMaxRows, stream);
+  // prefill-class rows (query_len * G > 16): MFMA prefill kernel
+  hipError_t e = launch_attn_prefill(a, kMaxRows, stream);
   if (e != hipSuccess) return e;
   if (a.dtype == PA_BF16) {
     decode_kernel<BF16><<<d.n_items, 64, 0, stream>>>(d);

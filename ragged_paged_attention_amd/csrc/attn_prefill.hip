@@ -1,0 +1,303 @@
+// MFMA prefill / chunk kernel for pa_attention (bf16/f16, head_dim 128,
+// block_size % 16 == 0): sequences with query_len * G > 16.
+//
+// "vLLM Continuous Batching：从 Forward Shape 理解两个核心参数" §2.3: the rows of
+// a prefill chunk at positions p = seq_len - query_len + i each see positions
+// 0..p of their own sequence (history and this step's rows, already written
+// to the cache); "LLM 推理引擎 Continuous Batching 与 PagedAttention" §1.1:
+// prefill is the compute-bound O(n^2) side, so this kernel is built around the
+// matrix cores.  Online softmax as in that page's §3.3 kernel.
+//
+// Work item = (sequence, 128 query rows, KV head g); the rows are the
+// (query i, head hg) pairs of the group, i-major, so the G query heads that
+// share KV head g share every K/V tile.  Workgroup = 4 waves x 32 rows.
+// KV is walked in 64-token tiles gathered through the block table (each
+// 16-token group lies in one block) into LDS by all 256 threads; the next
+// tile's loads are in flight while the current tile computes.
+//   S^T[64 tok][32 rows] = K . Q^T : 4 x 2 tiles of v_mfma_f32_16x16x32,
+//                                    A = K rows from LDS (ds_read_b128)
+//   O^T[128][32 rows]   += V^T . P^T : 8 x 2 tiles of v_mfma_f32_16x16x32
+//                                    per 32 tokens; P^T is the S^T
+//                                    accumulator of two 16-token tiles, used
+//                                    in place; V^T comes from two transposed
+//                                    LDS reads per fragment.
+// Only tiles that cross a wave's diagonal are masked.  Items are issued
+// heaviest first (last query tiles of each sequence first).
+#include "mfma_common.h"
+#include "pa_common.h"
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kRowsPerWave = 32;
+constexpr int kRowsPerWG = kWaves * kRowsPerWave;  // 128
+constexpr int kTile = 64;                          // KV tokens per tile
+constexpr int kKRowBytes = 272;                    // LDS pitch of K rows (256 + 16)
+
+struct PrefillArgs {
+  const uint16_t* q;
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;
+  const int32_t* block_tables;
+  const int32_t* qsl;
+  const int32_t* seq_lens;
+  int32_t S, Hq, Hkv, G, NB, MB, bs, n_qt, min_rows;
+  float scale_log2e;
+  uint16_t* out;
+  int32_t* d_err;
+};
+
+template <class F>
+__global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
+  using M = Mma<F>;
+  __shared__ __attribute__((aligned(16))) uint8_t klds[kTile * kKRowBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t vlds[kTile * kVRowBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 15, grp = lane >> 4;
+
+  const int32_t item = blockIdx.x;
+  const int32_t g = item % a.Hkv;
+  const int32_t tmp = item / a.Hkv;
+  const int32_t s = tmp % a.S;
+  const int32_t qt_first = a.n_qt - 1 - tmp / a.S;  // heaviest (last) query tiles first
+
+  const int32_t q0 = a.qsl[s];
+  const int32_t qlen = a.qsl[s + 1] - q0;
+  const int32_t rows_total = qlen * a.G;
+  if (rows_total <= a.min_rows || qt_first * kRowsPerWG >= rows_total) return;
+  const int32_t L = a.seq_lens[s];
+
+  if (L < qlen || ceil_div(L, a.bs) > a.MB) {
+    if (tid == 0) flag(a.d_err, L < qlen ? PA_DERR_QLEN_GT_SEQLEN : PA_DERR_BLOCK_OOB);
+    for (int64_t idx = tid + static_cast<int64_t>(qt_first) * kRowsPerWG * kD;
+         idx < static_cast<int64_t>(rows_total) * kD; idx += 256) {
+      if ((idx / kD) / kRowsPerWG % a.n_qt != qt_first) continue;  // another item's rows
+      const int32_t rho = static_cast<int32_t>(idx / kD);
+      const int32_t i = rho / a.G, hg = rho - (rho / a.G) * a.G;
+      a.out[((static_cast<int64_t>(q0) + i) * a.Hq + g * a.G + hg) * kD + idx % kD] = 0;
+    }
+    return;
+  }
+
+  // The launch covers max_query_len; any query tile beyond it (a too-small
+  // hint) is picked up by the same workgroup, n_qt tiles further on.
+  for (int32_t qt = qt_first; qt * kRowsPerWG < rows_total; qt += a.n_qt) {
+    // ---- this wave's rows and their Q^T fragments ----
+    const int32_t row0 = qt * kRowsPerWG;
+    int32_t qpos[2];
+    uint4 qf[2][4];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int32_t rho = row0 + wave * kRowsPerWave + nt * 16 + r;
+      const bool valid = rho < rows_total;
+      const int32_t i = rho / a.G, hg = rho - (rho / a.G) * a.G;
+      qpos[nt] = valid ? L - qlen + i : -1;
+      const uint16_t* qp = a.q + ((static_cast<int64_t>(q0) + i) * a.Hq + g * a.G + hg) * kD + 8 * grp;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) qf[nt][kk] = valid ? ld16(qp + 32 * kk) : make_uint4(0, 0, 0, 0);
+    }
+    const int32_t wave_row0 = row0 + wave * kRowsPerWave;
+    const bool wave_active = wave_row0 < rows_total;
+    const int32_t qpos_min_wave = L - qlen + wave_row0 / a.G;  // first row of the wave
+    const int32_t last_row = min(row0 + kRowsPerWG, rows_total) - 1;
+    const int32_t qpos_max = L - qlen + last_row / a.G;
+    const int32_t n_tiles = qpos_max / kTile + 1;
+
+    // ---- cooperative tile loads: thread -> 4 token rows x 16 bytes of K and V ----
+    const int32_t* btrow = a.block_tables + static_cast<int64_t>(s) * a.MB;
+    const int64_t slot_stride = static_cast<int64_t>(a.Hkv) * kD;
+    const int32_t my_tok = tid >> 4;     // 0..15 within each 16-token group
+    const int32_t my_col = 8 * (tid & 15);
+    const int32_t nblk = ceil_div(L, a.bs);
+    uint4 kreg[4], vreg[4];
+    auto load_tile = [&](int32_t kt) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int32_t t16 = kt * kTile + 16 * u;  // first token of the 16-token group
+        const int32_t lb = t16 / a.bs;
+        if (t16 < L && lb < nblk) {
+          int32_t b = btrow[lb];
+          if (b < 0 || b >= a.NB) {
+            flag(a.d_err, PA_DERR_BLOCK_OOB);
+            b = 0;
+          }
+          const int64_t slot = static_cast<int64_t>(b) * a.bs + (t16 - lb * a.bs) + my_tok;
+          const int64_t off = slot * slot_stride + static_cast<int64_t>(g) * kD + my_col;
+          kreg[u] = ld16(a.k_cache + off);
+          vreg[u] = ld16(a.v_cache + off);
+        } else {
+          kreg[u] = make_uint4(0, 0, 0, 0);
+          vreg[u] = make_uint4(0, 0, 0, 0);
+        }
+      }
+    };
+
+    float m[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};
+    f32x4_t o[2][8];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) o[nt][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    load_tile(0);
+    for (int32_t kt = 0; kt < n_tiles; ++kt) {
+      __syncthreads();  // every wave is done with the previous tile
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int32_t row = 16 * u + my_tok;
+        uint4 vv = vreg[u];
+        if (kt * kTile + row >= L) vv = make_uint4(0, 0, 0, 0);  // unwritten slots may hold NaN
+        *reinterpret_cast<uint4*>(klds + row * kKRowBytes + 2 * my_col) = kreg[u];
+        *reinterpret_cast<uint4*>(vlds + row * kVRowBytes + 2 * my_col) = vv;
+      }
+      __syncthreads();
+      if (kt + 1 < n_tiles) load_tile(kt + 1);
+      if (!wave_active) continue;
+
+      // S^T[16 mt + 4grp + j][row r of nt]
+      f32x4_t st[2][4];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) st[nt][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const uint4 ka = *reinterpret_cast<const uint4*>(klds + (16 * mt + r) * kKRowBytes + 64 * kk + 16 * grp);
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) st[nt][mt] = M::qk(ka, qf[nt][kk], st[nt][mt]);
+        }
+      }
+
+      const bool need_mask = kt * kTile + kTile - 1 > qpos_min_wave;
+      uint4 pb[2][2];
+      float alpha_any = 0.f;
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        if (need_mask) {
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int32_t tok = kt * kTile + 16 * mt + 4 * grp + j;
+              if (tok > qpos[nt]) st[nt][mt][j] = -INFINITY;
+            }
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          mx = fmaxf(mx, fmaxf(fmaxf(st[nt][mt][0], st[nt][mt][1]), fmaxf(st[nt][mt][2], st[nt][mt][3])));
+        mx = xor_max(mx, 16);
+        mx = xor_max(mx, 32);
+        const float m_new = fmaxf(m[nt], mx * a.scale_log2e);
+        float alpha = 1.f, ps = 0.f;
+        float p[4][4];
+        if (m_new == -INFINITY) {
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) p[mt][j] = 0.f;
+        } else {
+          alpha = __builtin_amdgcn_exp2f(m[nt] - m_new);
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              p[mt][j] = __builtin_amdgcn_exp2f(fmaf(st[nt][mt][j], a.scale_log2e, -m_new));
+              ps += p[mt][j];
+            }
+        }
+        m[nt] = m_new;
+        lsum[nt] = lsum[nt] * alpha + ps;
+        alpha_any = fmaxf(alpha_any, alpha != 1.f ? 1.f : 0.f);
+        if (alpha != 1.f) {
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt) o[nt][dt] *= alpha;
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          pb[nt][u].x = pack2(M::cvt(p[2 * u][0]), M::cvt(p[2 * u][1]));
+          pb[nt][u].y = pack2(M::cvt(p[2 * u][2]), M::cvt(p[2 * u][3]));
+          pb[nt][u].z = pack2(M::cvt(p[2 * u + 1][0]), M::cvt(p[2 * u + 1][1]));
+          pb[nt][u].w = pack2(M::cvt(p[2 * u + 1][2]), M::cvt(p[2 * u + 1][3]));
+        }
+      }
+      (void)alpha_any;
+
+      // O^T += V^T . P^T over the two 32-token halves of the tile
+      const int rd = (4 * grp + (r >> 2)) * kVRowBytes + 8 * (r & 3);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          const i16x4_t lo = lds_read_tr16(vlds + rd + (32 * u) * kVRowBytes + 32 * dt);
+          const i16x4_t hi = lds_read_tr16(vlds + rd + (32 * u + 16) * kVRowBytes + 32 * dt);
+          uint4 va;
+          va.x = pack2(static_cast<uint16_t>(lo[0]), static_cast<uint16_t>(lo[1]));
+          va.y = pack2(static_cast<uint16_t>(lo[2]), static_cast<uint16_t>(lo[3]));
+          va.z = pack2(static_cast<uint16_t>(hi[0]), static_cast<uint16_t>(hi[1]));
+          va.w = pack2(static_cast<uint16_t>(hi[2]), static_cast<uint16_t>(hi[3]));
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) o[nt][dt] = M::qk(va, pb[nt][u], o[nt][dt]);
+        }
+      }
+    }
+    if (!wave_active) continue;
+
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      float l = xor_sum(lsum[nt], 16);
+      l = xor_sum(l, 32);
+      const int32_t rho = wave_row0 + nt * 16 + r;
+      if (rho >= rows_total) continue;
+      const int32_t i = rho / a.G, hg = rho - (rho / a.G) * a.G;
+      uint16_t* orow = a.out + ((static_cast<int64_t>(q0) + i) * a.Hq + g * a.G + hg) * kD;
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        uint2 w;
+        w.x = pack2(M::cvt(o[nt][dt][0] * inv), M::cvt(o[nt][dt][1] * inv));
+        w.y = pack2(M::cvt(o[nt][dt][2] * inv), M::cvt(o[nt][dt][3] * inv));
+        *reinterpret_cast<uint2*>(orow + 16 * dt + 4 * grp) = w;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attn_prefill(const AttnArgs& a, int32_t min_rows, hipStream_t stream) {
+  PrefillArgs p;
+  p.q = static_cast<const uint16_t*>(a.q);
+  p.k_cache = static_cast<const uint16_t*>(a.k_cache);
+  p.v_cache = static_cast<const uint16_t*>(a.v_cache);
+  p.block_tables = a.block_tables;
+  p.qsl = a.qsl;
+  p.seq_lens = a.seq_lens;
+  p.S = a.S;
+  p.Hq = a.Hq;
+  p.Hkv = a.Hkv;
+  p.G = a.Hq / a.Hkv;
+  p.NB = a.NB;
+  p.MB = a.MB;
+  p.bs = a.bs;
+  const int64_t rows_max = static_cast<int64_t>(a.max_qlen) * p.G;
+  if (rows_max <= min_rows) return hipSuccess;  // no prefill-class sequence can exist
+  p.n_qt = static_cast<int32_t>((rows_max + kRowsPerWG - 1) / kRowsPerWG);
+  p.min_rows = min_rows;
+  p.scale_log2e = a.scale * 1.4426950408889634f;
+  p.out = static_cast<uint16_t*>(a.out);
+  p.d_err = a.d_err;
+  const int64_t items = static_cast<int64_t>(a.S) * p.n_qt * a.Hkv;
+  if (items > INT32_MAX) return hipErrorInvalidValue;
+  if (a.dtype == PA_BF16) prefill_kernel<BF16><<<static_cast<uint32_t>(items), 256, 0, stream>>>(p);
+  else prefill_kernel<F16><<<static_cast<uint32_t>(items), 256, 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace pa

@@ -1,0 +1,70 @@
+// MFMA helpers shared by the fast attention kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa_common.h"
+
+namespace pa {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kD = 128;          // head_dim of the fast paths
+constexpr int kChunk = 16;       // tokens per MFMA tile edge
+constexpr int kVRowBytes = 288;  // LDS row pitch of a staged V tile: 256 B + 32 B, so the
+                                 // 16 rows one transposed read touches start in distinct banks
+
+// Per-dtype MFMA.  qk: v_mfma_f32_16x16x32 (8 elements per lane per operand);
+// pv16: v_mfma_f32_16x16x16 (4 per lane).
+//   A[m = lane%16][k = 8*(lane/16) + j]  (16x16x32)   A[m][k = 4*(lane/16) + j]  (16x16x16)
+//   B[k = same][n = lane%16]             D[m = 4*(lane/16) + j][n = lane%16]
+template <class F> struct Mma;
+template <> struct Mma<BF16> {
+  static __device__ __forceinline__ f32x4_t qk(uint4 a, uint4 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4_t pv(i16x4_t a, i16x4_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint16_t cvt(float x) {
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+  }
+};
+template <> struct Mma<F16> {
+  static __device__ __forceinline__ f32x4_t qk(uint4 a, uint4 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4_t pv(i16x4_t a, i16x4_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a),
+                                                 __builtin_bit_cast(f16x4_t, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint16_t cvt(float x) {
+    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+  }
+};
+
+__device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+
+__device__ __forceinline__ float xor_max(float v, int m) { return fmaxf(v, __shfl_xor(v, m, 64)); }
+__device__ __forceinline__ float xor_sum(float v, int m) { return v + __shfl_xor(v, m, 64); }
+
+// Transposed LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane L
+// supplies the address of 4 consecutive 16-bit elements; lanes 4j..4j+3
+// together supply row j (16 elements) of a 4x16 tile, and lane i receives
+// column i, i.e. element i of rows 0..3.
+__device__ __forceinline__ i16x4_t lds_read_tr16(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(p));
+}
+
+__device__ __forceinline__ uint32_t pack2(uint16_t lo, uint16_t hi) {
+  return static_cast<uint32_t>(lo) | (static_cast<uint32_t>(hi) << 16);
+}
+
+}  // namespace pa

@@ -47,4 +47,7 @@ bool fast_path_supported(const AttnArgs& a);
 size_t fast_workspace_bytes(int32_t S, int32_t T, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_seqlen);
 hipError_t launch_attn_fast(const AttnArgs& a, hipStream_t stream);
 
+// attn_prefill.hip: rows of sequences with query_len * (Hq/Hkv) > min_rows.
+hipError_t launch_attn_prefill(const AttnArgs& a, int32_t min_rows, hipStream_t stream);
+
 }  // namespace pa
