@@ -12,8 +12,10 @@
 // (query i, head hg) pairs of the group, i-major, so the G query heads that
 // share KV head g share every K/V tile.  Workgroup = 4 waves x 32 rows.
 // KV is walked in 64-token tiles gathered through the block table (each
-// 16-token group lies in one block) into LDS by all 256 threads; the next
-// tile's loads are in flight while the current tile computes.
+// 16-token group lies in one block) straight from HBM into LDS with
+// global_load_lds_dwordx4 (no register staging); two LDS stages, so the next
+// tile's loads are in flight while the current tile computes, one barrier per
+// tile.
 //   S^T[64 tok][32 rows] = K . Q^T : 4 x 2 tiles of v_mfma_f32_16x16x32,
 //                                    A = K rows from LDS (ds_read_b128)
 //   O^T[128][32 rows]   += V^T . P^T : 8 x 2 tiles of v_mfma_f32_16x16x32
@@ -34,7 +36,9 @@ constexpr int kWaves = 4;
 constexpr int kRowsPerWave = 32;
 constexpr int kRowsPerWG = kWaves * kRowsPerWave;  // 128
 constexpr int kTile = 64;                          // KV tokens per tile
-constexpr int kKRowBytes = 272;                    // LDS pitch of K rows (256 + 16)
+constexpr int kRowBytes = 256;                     // one token row of one head (128 x 16 bit)
+constexpr int kTileBytes = kTile * kRowBytes;      // 16 KB per K or V tile
+constexpr int kStageBytes = 2 * kTileBytes;        // K tile then V tile
 
 struct PrefillArgs {
   const uint16_t* q;
@@ -49,11 +53,19 @@ struct PrefillArgs {
   int32_t* d_err;
 };
 
+// LDS tiles are 64 rows x 16 chunks of 16 bytes, stored without padding.
+// Chunk c of row R sits in slot c ^ swz(R):
+//   K: swz = R & 15 -> the 16 rows one K fragment read touches use 16
+//      different slots, i.e. all 64 banks once;
+//   V: swz = (R & 7) << 1 -> the 8 rows of a half-wave transposed read hit 8
+//      different 32-byte bank groups (chunk pairs stay adjacent).
+__device__ __forceinline__ int k_slot(int row, int chunk) { return row * kRowBytes + ((chunk ^ (row & 15)) << 4); }
+__device__ __forceinline__ int v_slot(int row, int chunk) { return row * kRowBytes + ((chunk ^ ((row & 7) << 1)) << 4); }
+
 template <class F>
-__global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   using M = Mma<F>;
-  __shared__ __attribute__((aligned(16))) uint8_t klds[kTile * kKRowBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t vlds[kTile * kVRowBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kStageBytes];  // 64 KB, two stages
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -83,11 +95,59 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     return;
   }
 
+  const int32_t* btrow = a.block_tables + static_cast<int64_t>(s) * a.MB;
+  const int64_t slot_stride = static_cast<int64_t>(a.Hkv) * kD;  // elements between slots
+  const uint16_t* kbase = a.k_cache + static_cast<int64_t>(g) * kD;
+  const uint16_t* vbase = a.v_cache + static_cast<int64_t>(g) * kD;
+
+  // DMA of one tile: wave w fills rows 16w..16w+15 (one 16-token group, so one
+  // block id) of the K and V tiles, 4 rows per instruction, lane -> 16 bytes.
+  // Rows at or past the context end re-read the last valid row, so nothing
+  // unwritten (possibly NaN) ever reaches LDS; such rows are masked anyway.
+  auto issue_tile = [&](int32_t kt, int stage) {
+    const int32_t t16 = kt * kTile + 16 * wave;
+    const int32_t lb = (t16 < L ? t16 : L - 1) / a.bs;
+    int32_t b = btrow[lb];
+    if (b < 0 || b >= a.NB) {
+      flag(a.d_err, PA_DERR_BLOCK_OOB);
+      b = 0;
+    }
+    const int64_t slot0 = static_cast<int64_t>(b) * a.bs + (t16 < L ? t16 - lb * a.bs : 0);
+    uint8_t* kdst = lds + stage * kStageBytes + (16 * wave) * kRowBytes;
+    uint8_t* vdst = kdst + kTileBytes;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int row = 16 * wave + 4 * u + grp;  // tile row this lane fills
+      const int32_t tok = kt * kTile + row;
+      int64_t slot;
+      if (tok < L) slot = slot0 + 4 * u + grp;
+      else {  // past the end: last valid token of the sequence
+        const int32_t lb2 = (L - 1) / a.bs;
+        int32_t b2 = btrow[lb2];
+        b2 = (b2 < 0 || b2 >= a.NB) ? 0 : b2;
+        slot = static_cast<int64_t>(b2) * a.bs + (L - 1 - lb2 * a.bs);
+      }
+      const int kc = r ^ (row & 15);         // chunk whose data lands in slot r
+      const int vc = r ^ ((row & 7) << 1);
+      __builtin_amdgcn_global_load_lds((const void*)(kbase + slot * slot_stride + 8 * kc),
+                                       (__attribute__((address_space(3))) void*)(kdst + 4 * u * kRowBytes),
+                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(vbase + slot * slot_stride + 8 * vc),
+                                       (__attribute__((address_space(3))) void*)(vdst + 4 * u * kRowBytes),
+                                       16, 0, 0);
+    }
+  };
+
   // The launch covers max_query_len; any query tile beyond it (a too-small
   // hint) is picked up by the same workgroup, n_qt tiles further on.
   for (int32_t qt = qt_first; qt * kRowsPerWG < rows_total; qt += a.n_qt) {
-    // ---- this wave's rows and their Q^T fragments ----
     const int32_t row0 = qt * kRowsPerWG;
+    const int32_t last_row = min(row0 + kRowsPerWG, rows_total) - 1;
+    const int32_t n_tiles = (L - qlen + last_row / a.G) / kTile + 1;
+    __syncthreads();  // LDS of a previous query tile is no longer read
+    issue_tile(0, 0);
+
+    // this wave's rows and their Q^T fragments
     int32_t qpos[2];
     uint4 qf[2][4];
 #pragma unroll
@@ -102,39 +162,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     }
     const int32_t wave_row0 = row0 + wave * kRowsPerWave;
     const bool wave_active = wave_row0 < rows_total;
-    const int32_t qpos_min_wave = L - qlen + wave_row0 / a.G;  // first row of the wave
-    const int32_t last_row = min(row0 + kRowsPerWG, rows_total) - 1;
-    const int32_t qpos_max = L - qlen + last_row / a.G;
-    const int32_t n_tiles = qpos_max / kTile + 1;
-
-    // ---- cooperative tile loads: thread -> 4 token rows x 16 bytes of K and V ----
-    const int32_t* btrow = a.block_tables + static_cast<int64_t>(s) * a.MB;
-    const int64_t slot_stride = static_cast<int64_t>(a.Hkv) * kD;
-    const int32_t my_tok = tid >> 4;     // 0..15 within each 16-token group
-    const int32_t my_col = 8 * (tid & 15);
-    const int32_t nblk = ceil_div(L, a.bs);
-    uint4 kreg[4], vreg[4];
-    auto load_tile = [&](int32_t kt) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int32_t t16 = kt * kTile + 16 * u;  // first token of the 16-token group
-        const int32_t lb = t16 / a.bs;
-        if (t16 < L && lb < nblk) {
-          int32_t b = btrow[lb];
-          if (b < 0 || b >= a.NB) {
-            flag(a.d_err, PA_DERR_BLOCK_OOB);
-            b = 0;
-          }
-          const int64_t slot = static_cast<int64_t>(b) * a.bs + (t16 - lb * a.bs) + my_tok;
-          const int64_t off = slot * slot_stride + static_cast<int64_t>(g) * kD + my_col;
-          kreg[u] = ld16(a.k_cache + off);
-          vreg[u] = ld16(a.v_cache + off);
-        } else {
-          kreg[u] = make_uint4(0, 0, 0, 0);
-          vreg[u] = make_uint4(0, 0, 0, 0);
-        }
-      }
-    };
+    const int32_t qpos_min_wave = L - qlen + wave_row0 / a.G;
 
     float m[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};
     f32x4_t o[2][8];
@@ -143,109 +171,103 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) o[nt][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    load_tile(0);
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
     for (int32_t kt = 0; kt < n_tiles; ++kt) {
-      __syncthreads();  // every wave is done with the previous tile
+      const int stage = kt & 1;
+      if (kt + 1 < n_tiles) issue_tile(kt + 1, stage ^ 1);
+      const uint8_t* kt_lds = lds + stage * kStageBytes;
+      const uint8_t* vt_lds = kt_lds + kTileBytes;
+      if (wave_active) {
+        // S^T[16 mt + 4grp + j][row r of nt]
+        f32x4_t st[2][4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int32_t row = 16 * u + my_tok;
-        uint4 vv = vreg[u];
-        if (kt * kTile + row >= L) vv = make_uint4(0, 0, 0, 0);  // unwritten slots may hold NaN
-        *reinterpret_cast<uint4*>(klds + row * kKRowBytes + 2 * my_col) = kreg[u];
-        *reinterpret_cast<uint4*>(vlds + row * kVRowBytes + 2 * my_col) = vv;
-      }
-      __syncthreads();
-      if (kt + 1 < n_tiles) load_tile(kt + 1);
-      if (!wave_active) continue;
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) st[nt][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) {
+            const uint4 ka = *reinterpret_cast<const uint4*>(kt_lds + k_slot(16 * mt + r, 4 * kk + grp));
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) st[nt][mt] = M::qk(ka, qf[nt][kk], st[nt][mt]);
+          }
+        }
 
-      // S^T[16 mt + 4grp + j][row r of nt]
-      f32x4_t st[2][4];
+        const bool need_mask = kt * kTile + kTile - 1 > qpos_min_wave;
+        uint4 pb[2][2];
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
+        for (int nt = 0; nt < 2; ++nt) {
+          if (need_mask) {
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) st[nt][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
+              for (int j = 0; j < 4; ++j) {
+                const int32_t tok = kt * kTile + 16 * mt + 4 * grp + j;
+                if (tok > qpos[nt]) st[nt][mt][j] = -INFINITY;
+              }
+          }
+          float mx = -INFINITY;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const uint4 ka = *reinterpret_cast<const uint4*>(klds + (16 * mt + r) * kKRowBytes + 64 * kk + 16 * grp);
+          for (int mt = 0; mt < 4; ++mt)
+            mx = fmaxf(mx, fmaxf(fmaxf(st[nt][mt][0], st[nt][mt][1]), fmaxf(st[nt][mt][2], st[nt][mt][3])));
+          mx = xor_max(mx, 16);
+          mx = xor_max(mx, 32);
+          const float m_new = fmaxf(m[nt], mx * a.scale_log2e);
+          float alpha = 1.f, ps = 0.f;
+          if (m_new == -INFINITY) {
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt) st[nt][mt] = M::qk(ka, qf[nt][kk], st[nt][mt]);
+            for (int mt = 0; mt < 4; ++mt) st[nt][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          } else {
+            alpha = __builtin_amdgcn_exp2f(m[nt] - m_new);
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                st[nt][mt][j] = __builtin_amdgcn_exp2f(fmaf(st[nt][mt][j], a.scale_log2e, -m_new));
+                ps += st[nt][mt][j];
+              }
+          }
+          m[nt] = m_new;
+          lsum[nt] = lsum[nt] * alpha + ps;
+          if (alpha != 1.f) {
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) o[nt][dt] *= alpha;
+          }
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            pb[nt][u].x = pack2(M::cvt(st[nt][2 * u][0]), M::cvt(st[nt][2 * u][1]));
+            pb[nt][u].y = pack2(M::cvt(st[nt][2 * u][2]), M::cvt(st[nt][2 * u][3]));
+            pb[nt][u].z = pack2(M::cvt(st[nt][2 * u + 1][0]), M::cvt(st[nt][2 * u + 1][1]));
+            pb[nt][u].w = pack2(M::cvt(st[nt][2 * u + 1][2]), M::cvt(st[nt][2 * u + 1][3]));
+          }
         }
-      }
 
-      const bool need_mask = kt * kTile + kTile - 1 > qpos_min_wave;
-      uint4 pb[2][2];
-      float alpha_any = 0.f;
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        if (need_mask) {
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const int32_t tok = kt * kTile + 16 * mt + 4 * grp + j;
-              if (tok > qpos[nt]) st[nt][mt][j] = -INFINITY;
-            }
-        }
-        float mx = -INFINITY;
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-          mx = fmaxf(mx, fmaxf(fmaxf(st[nt][mt][0], st[nt][mt][1]), fmaxf(st[nt][mt][2], st[nt][mt][3])));
-        mx = xor_max(mx, 16);
-        mx = xor_max(mx, 32);
-        const float m_new = fmaxf(m[nt], mx * a.scale_log2e);
-        float alpha = 1.f, ps = 0.f;
-        float p[4][4];
-        if (m_new == -INFINITY) {
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) p[mt][j] = 0.f;
-        } else {
-          alpha = __builtin_amdgcn_exp2f(m[nt] - m_new);
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              p[mt][j] = __builtin_amdgcn_exp2f(fmaf(st[nt][mt][j], a.scale_log2e, -m_new));
-              ps += p[mt][j];
-            }
-        }
-        m[nt] = m_new;
-        lsum[nt] = lsum[nt] * alpha + ps;
-        alpha_any = fmaxf(alpha_any, alpha != 1.f ? 1.f : 0.f);
-        if (alpha != 1.f) {
-#pragma unroll
-          for (int dt = 0; dt < 8; ++dt) o[nt][dt] *= alpha;
-        }
+        // O^T += V^T . P^T over the two 32-token halves of the tile.  Lane r of
+        // group grp supplies row 4grp + r/4 (+ 32u, + 16) and 4 columns
+        // 16dt + 4(r%4): 8 bytes inside chunk 2dt + (r%4)/2.
+        const int rsub = r >> 2, hb = 8 * ((r & 3) & 1), csub = (r & 3) >> 1;
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          pb[nt][u].x = pack2(M::cvt(p[2 * u][0]), M::cvt(p[2 * u][1]));
-          pb[nt][u].y = pack2(M::cvt(p[2 * u][2]), M::cvt(p[2 * u][3]));
-          pb[nt][u].z = pack2(M::cvt(p[2 * u + 1][0]), M::cvt(p[2 * u + 1][1]));
-          pb[nt][u].w = pack2(M::cvt(p[2 * u + 1][2]), M::cvt(p[2 * u + 1][3]));
+          const int row_lo = 32 * u + 4 * grp + rsub;
+          const int row_hi = row_lo + 16;
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt) {
+            const i16x4_t lo = lds_read_tr16(vt_lds + v_slot(row_lo, 2 * dt + csub) + hb);
+            const i16x4_t hi = lds_read_tr16(vt_lds + v_slot(row_hi, 2 * dt + csub) + hb);
+            uint4 va;
+            va.x = pack2(static_cast<uint16_t>(lo[0]), static_cast<uint16_t>(lo[1]));
+            va.y = pack2(static_cast<uint16_t>(lo[2]), static_cast<uint16_t>(lo[3]));
+            va.z = pack2(static_cast<uint16_t>(hi[0]), static_cast<uint16_t>(hi[1]));
+            va.w = pack2(static_cast<uint16_t>(hi[2]), static_cast<uint16_t>(hi[3]));
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) o[nt][dt] = M::qk(va, pb[nt][u], o[nt][dt]);
+          }
         }
       }
-      (void)alpha_any;
-
-      // O^T += V^T . P^T over the two 32-token halves of the tile
-      const int rd = (4 * grp + (r >> 2)) * kVRowBytes + 8 * (r & 3);
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-          const i16x4_t lo = lds_read_tr16(vlds + rd + (32 * u) * kVRowBytes + 32 * dt);
-          const i16x4_t hi = lds_read_tr16(vlds + rd + (32 * u + 16) * kVRowBytes + 32 * dt);
-          uint4 va;
-          va.x = pack2(static_cast<uint16_t>(lo[0]), static_cast<uint16_t>(lo[1]));
-          va.y = pack2(static_cast<uint16_t>(lo[2]), static_cast<uint16_t>(lo[3]));
-          va.z = pack2(static_cast<uint16_t>(hi[0]), static_cast<uint16_t>(hi[1]));
-          va.w = pack2(static_cast<uint16_t>(hi[2]), static_cast<uint16_t>(hi[3]));
-#pragma unroll
-          for (int nt = 0; nt < 2; ++nt) o[nt][dt] = M::qk(va, pb[nt][u], o[nt][dt]);
-        }
-      }
+      __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();  // next tile landed everywhere; this stage is free again
     }
     if (!wave_active) continue;
 
