@@ -37,7 +37,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=4, help="workload for the step (1-5)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["step", "decode", "prefill"], default=None,
+    ap.add_argument("--only", choices=["step", "decode", "prefill", "shared"], default=None,
                     help="run one leg only (for profiling)")
     ap.add_argument("--cpu-sample-rows", type=int, default=2048)
     return ap.parse_args()
@@ -190,11 +190,46 @@ def main():
         ms3 = timer.time(attn3, max(args.steps, 20), args.warmup)
         kv3 = accounting.kv_read_bytes(w3.step.seq_lens, w3.num_kv_heads, w3.head_dim, w3.dtype)
         gbs = kv3 / (ms3 / 1e3) / 1e9
+        # ceilings on this machine: a contiguous streaming read of the K cache,
+        # and the same paged gather as the decode kernel with no arithmetic
+        sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+        ms_stream = timer.time(lambda: rpa.pa_bench_stream_read(g3.k_cache, sink), 10, 3)
+        stream_gbs = g3.k_cache.numel() * 2 / (ms_stream / 1e3) / 1e9
+        ms_paged = timer.time(lambda: rpa.pa_bench_paged_read(g3.k_cache, g3.v_cache, db.block_tables, db.seq_lens,
+                                                              w3.max_seq_len, sink), 20, 3)
+        rounded = int(((w3.step.seq_lens.astype("int64") + 15) // 16 * 16).sum()) * 2 * w3.num_kv_heads * 256
+        paged_gbs = rounded / (ms_paged / 1e3) / 1e9
         result["decode_kv_read"] = {"workload": w3.name, "GBps": gbs, "frac_hbm_peak": gbs / HBM_PEAK_GBS,
                                     "kv_bytes": kv3, "ms": ms3, "tokens": w3.num_tokens,
-                                    "seqs": w3.num_seqs, "seq_len": w3.max_seq_len}
+                                    "seqs": w3.num_seqs, "seq_len": w3.max_seq_len,
+                                    "stream_read_GBps": stream_gbs, "paged_read_no_math_GBps": paged_gbs}
         result["roofline"] = {"bound": "hbm", "kernel": "pa_attention (decode batch)", "achieved": gbs,
                               "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": None}
+    # ---------------- shared-prefix long-context decode ----------------
+    if args.only in (None, "shared"):
+        w5 = config(5, poison=False)
+        g5 = setup(w5, torch)
+        g5.out_buf = torch.empty_like(g5.db.q)
+        db = g5.db
+        md5 = rpa.pa_build_metadata(db.query_lens, db.seq_lens, w5.num_tokens, db.block_tables, w5.block_size,
+                                    w5.num_blocks)
+        rpa.pa_write_kv(db.k, db.v, md5["slot_mapping"], g5.k_cache, g5.v_cache)
+        need = rpa.pa_attention_workspace_size(w5.num_seqs, w5.num_tokens, w5.num_q_heads, w5.num_kv_heads,
+                                               w5.head_dim, w5.max_seq_len)
+        ws5 = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+        attn5 = lambda: rpa.pa_attention(db.q, g5.k_cache, g5.v_cache, db.block_tables, md5["query_start_loc"],
+                                         db.seq_lens, w5.max_query_len, w5.max_seq_len, w5.scale, out=g5.out_buf,
+                                         workspace=ws5)
+        ms5 = timer.time(attn5, max(args.steps, 20), args.warmup)
+        kv5 = accounting.kv_read_bytes(w5.step.seq_lens, w5.num_kv_heads, w5.head_dim, w5.dtype)
+        uq5 = accounting.unique_kv_bytes_fast(w5.step.block_tables, w5.step.seq_lens, w5.block_size,
+                                              w5.num_kv_heads, w5.head_dim, w5.dtype)
+        result["shared_prefix_decode"] = {"workload": w5.name, "logical_GBps": kv5 / (ms5 / 1e3) / 1e9,
+                                          "unique_GBps": uq5 / (ms5 / 1e3) / 1e9, "logical_bytes": kv5,
+                                          "unique_bytes": uq5, "ms": ms5}
+        del g5, ws5
+        torch.cuda.empty_cache()
+
     # ---------------- ragged prefill batch: MFMA throughput ----------------
     if args.only in (None, "prefill"):
         w2 = config(2, poison=False)

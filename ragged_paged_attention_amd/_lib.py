@@ -15,6 +15,7 @@ import re
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libpa.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "pa.h")
+HEADERS = [HEADER, os.path.join(os.path.dirname(PKG), "include", "pa_bench.h")]
 
 PA_F32, PA_BF16, PA_F16 = 0, 1, 2
 PA_POLICY_AUTO, PA_POLICY_GENERIC, PA_POLICY_FAST = 0, 1, 2
@@ -63,16 +64,22 @@ _lib.pa_write_kv.restype = _i32
 _lib.pa_write_kv.argtypes = [_p, _p, _p, _i32, _i32, _i32, _p, _p, _i32, _i32, _i32, _p, _p]
 _lib.pa_attention_workspace_size.restype = _size
 _lib.pa_attention_workspace_size.argtypes = [_i32] * 6
+_lib.pa_bench_stream_read.restype = _i32
+_lib.pa_bench_stream_read.argtypes = [_p, _size, _p, _p]
+_lib.pa_bench_paged_read.restype = _i32
+_lib.pa_bench_paged_read.argtypes = [_p, _p, _p, _p] + [_i32] * 6 + [_p, _p]
 _lib.pa_attention.restype = _i32
 _lib.pa_attention.argtypes = [_p, _p, _p, _p, _p, _p] + [_i32] * 10 + [_f32, _i32, _p, _p, _size, _p, _p]
 
 
 def declared_symbols() -> list:
-    """Names of the functions include/pa.h declares."""
-    with open(HEADER) as f:
-        text = f.read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(pa_[a-z_]+)\s*\(", text)))
+    """Names of the functions include/pa.h and include/pa_bench.h declare."""
+    names = set()
+    for h in HEADERS:
+        with open(h) as f:
+            text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+        names |= set(re.findall(r"\b(pa_[a-z_]+)\s*\(", text))
+    return sorted(names)
 
 
 def library() -> ctypes.CDLL:
@@ -213,3 +220,21 @@ def pa_attention(q, k_cache, v_cache, block_tables, query_start_loc, seq_lens, m
                            _ptr(out), _ptr(workspace), wbytes, _ptr(d_err), _stream(q.device))
     _check(st, "pa_attention")
     return out
+
+
+# --------------------------------------------------------------------------
+# measurement helpers (include/pa_bench.h)
+# --------------------------------------------------------------------------
+def pa_bench_stream_read(buf, sink) -> None:
+    """Reads every byte of the contiguous device tensor `buf` once."""
+    nbytes = buf.numel() * buf.element_size()
+    _check(_lib.pa_bench_stream_read(_ptr(buf), nbytes, _ptr(sink), _stream(buf.device)), "pa_bench_stream_read")
+
+
+def pa_bench_paged_read(k_cache, v_cache, block_tables, seq_lens, max_seq_len: int, sink) -> None:
+    """Reads the K/V rows of every sequence through its block table, no math."""
+    NB, BS, Hkv = int(k_cache.shape[0]), int(k_cache.shape[1]), int(k_cache.shape[2])
+    st = _lib.pa_bench_paged_read(_ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(seq_lens),
+                                  int(seq_lens.shape[0]), Hkv, BS, NB, int(block_tables.shape[1]),
+                                  int(max_seq_len), _ptr(sink), _stream(k_cache.device))
+    _check(st, "pa_bench_paged_read")

@@ -36,14 +36,18 @@ namespace {
 
 constexpr int kPartFloats = 132;    // per partial row: O[128], m, l, pad
 constexpr int kMaxRows = 16;        // query rows of one decode item
-constexpr int kTargetItems = 8192;  // decode work items wanted to fill 256 CUs
-constexpr int kMinChunks = 16;      // do not split contexts below 256 tokens per part
+// Compile-time tuning of the decode work split (measured on MI355X).
+constexpr int kPartChunks = 48;     // a context part is at most 48 chunks = 768 tokens
+constexpr int kMaxParts = 64;       // parts per sequence (longer parts past 48k tokens)
+constexpr int kXcdRun = 16;         // consecutive decode items kept on one XCD
+constexpr int kGroupHeadsBelow = 16;  // item order: head-grouped when Hkv < this
 
-// Split of a context of `nchunks` 16-token chunks into parts: at most P parts,
-// none below kMinChunks chunks unless the whole context is, none empty.
+// Split of a context of `nchunks` 16-token chunks into parts of about
+// kPartChunks chunks: at most P parts, none empty.  Equal-sized parts keep the
+// tail of the launch short however uneven the context lengths are.
 __host__ __device__ __forceinline__ void plan_parts(int32_t nchunks, int32_t P, int32_t* nparts,
                                                     int32_t* cpp) {
-  int32_t np = (nchunks + kMinChunks - 1) / kMinChunks;
+  int32_t np = (nchunks + kPartChunks - 1) / kPartChunks;
   if (np > P) np = P;
   if (np < 1) np = 1;
   int32_t c = (nchunks + np - 1) / np;
@@ -59,7 +63,7 @@ struct DecodeArgs {
   const int32_t* block_tables;
   const int32_t* qsl;
   const int32_t* seq_lens;
-  int32_t S, Hq, Hkv, G, NB, MB, bs, P, n_items;
+  int32_t S, Hq, Hkv, G, NB, MB, bs, P, n_items, grouped;
   float scale_log2e;
   uint16_t* out;
   float* ws;
@@ -67,22 +71,49 @@ struct DecodeArgs {
 };
 
 template <class F>
-__global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void decode_kernel(DecodeArgs a) {
   using M = Mma<F>;
-  __shared__ __attribute__((aligned(16))) uint8_t vlds[kChunk * kVRowBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t vlds[2 * kChunk * kVRowBytes];
   const int lane = threadIdx.x;
   const int r = lane & 15;    // MFMA column = query row of the item
   const int grp = lane >> 4;  // 16-lane group
 
-  // XCD-aware mapping: workgroup b runs on XCD b % 8; give each XCD a
-  // contiguous range of items.
+  // XCD-aware mapping: workgroup b runs on XCD b % 8.  Items go out in runs of
+  // kXcdRun consecutive items per XCD, the runs rotating over the 8 XCDs: every
+  // XCD gets an even share of every part index (balance), and a run of
+  // neighbouring items lives on one XCD's L2.  The grid is a multiple of
+  // 8 * kXcdRun.
   const int32_t bid = blockIdx.x;
-  const int32_t per = a.n_items >> 3, rem = a.n_items & 7, xcd = bid & 7, loc = bid >> 3;
-  const int32_t item = xcd * per + (xcd < rem ? xcd : rem) + loc;
-  const int32_t s = item % a.S;
-  const int32_t tmp = item / a.S;
-  const int32_t g = tmp % a.Hkv;
-  const int32_t part = tmp / a.Hkv;
+  const int32_t xcd = bid & 7, j = bid >> 3;
+  const int32_t item = ((j / kXcdRun) * 8 + xcd) * kXcdRun + (j % kXcdRun);
+  if (item >= a.n_items) return;
+  // item = (part, sequence, KV head), head fastest: the Hkv waves reading the
+  // same token rows (all heads of a slot are one contiguous row of the cache)
+  // run side by side.
+  int32_t s, g, part;
+  if (a.grouped) {
+    // (part, block of kXcdRun sequences, head, sequence in block): a run is the
+    // same (part, head) of kXcdRun neighbouring sequences on one XCD (shared
+    // prefix blocks stay in its L2); the runs in flight on the other XCDs are
+    // the other heads of the same sequences, so each token row -- all heads of
+    // a slot, contiguous -- is read by all heads at about the same time.
+    const int32_t si = item % kXcdRun;
+    const int32_t tmp = item / kXcdRun;
+    g = tmp % a.Hkv;
+    const int32_t tmp2 = tmp / a.Hkv;
+    const int32_t sblocks = (a.S + kXcdRun - 1) / kXcdRun;
+    s = (tmp2 % sblocks) * kXcdRun + si;
+    part = tmp2 / sblocks;
+    if (s >= a.S) return;
+  } else {
+    // (part, head, sequence): with many KV heads a token row is long, and
+    // spreading the concurrent reads over many sequences' randomly placed
+    // blocks keeps more HBM channels busy than reading whole rows at once.
+    s = item % a.S;
+    const int32_t tmp = item / a.S;
+    g = tmp % a.Hkv;
+    part = tmp / a.Hkv;
+  }
 
   const int32_t q0 = a.qsl[s];
   const int32_t qlen = a.qsl[s + 1] - q0;
@@ -143,15 +174,35 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
     return static_cast<int64_t>(b) * a.bs + (c - lb * cpb) * kChunk;
   };
 
-  uint4 kf[4], vf[4];
-  auto load_chunk = [&](int32_t c) {
-    const int64_t slot0 = slot_of_chunk(c);
-    const uint16_t* kp = kbase + (slot0 + r) * slot_stride + 8 * grp;
+  // Chunks are taken two at a time (32 tokens, 16 KB of K+V per wave in
+  // flight).  One register buffer per pair: the next pair's K loads are issued
+  // as soon as the QK MFMAs have read the current K, the next V loads as soon
+  // as the current V is in LDS.  A pair's second chunk may lie past the part
+  // (odd chunk counts): it is then neither loaded nor counted.
+  uint4 kf[2][4], vf[2][4];
+  auto load_pair = [&](int32_t c, bool do_k, bool do_v) {
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) kf[kk] = ld16(kp + 32 * kk);
-    const uint16_t* vp = vbase + (slot0 + grp) * slot_stride + 8 * r;
+    for (int h2 = 0; h2 < 2; ++h2) {
+      if (c + h2 < c1) {
+        const int64_t slot0 = slot_of_chunk(c + h2);
+        if (do_k) {
+          const uint16_t* kp = kbase + (slot0 + r) * slot_stride + 8 * grp;
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) vf[r4] = ld16(vp + 4 * r4 * slot_stride);
+          for (int kk = 0; kk < 4; ++kk) kf[h2][kk] = ld16(kp + 32 * kk);
+        }
+        if (do_v) {
+          const uint16_t* vp = vbase + (slot0 + grp) * slot_stride + 8 * r;
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) vf[h2][r4] = ld16(vp + 4 * r4 * slot_stride);
+        }
+      } else {
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          if (do_k) kf[h2][x] = make_uint4(0, 0, 0, 0);
+          if (do_v) vf[h2][x] = make_uint4(0, 0, 0, 0);
+        }
+      }
+    }
   };
 
   float m = -INFINITY, lsum = 0.f;
@@ -159,65 +210,81 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  load_chunk(c0);
-  for (int32_t c = c0; c < c1; ++c) {
-    uint4 kc[4], vc[4];
-#pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      kc[x] = kf[x];
-      vc[x] = vf[x];
-    }
-    if (c + 1 < c1) load_chunk(c + 1);
+  load_pair(c0, true, true);
+  const int rd_off = (4 * grp + (r >> 2)) * kVRowBytes + 8 * (r & 3);
+  for (int32_t c = c0; c < c1; c += 2) {
     const int32_t tok0 = c * kChunk;
+    const bool more = c + 2 < c1;
 
-    // scores: S^T[tok 4grp + j][row r]
-    f32x4_t st = {0.f, 0.f, 0.f, 0.f};
+    // scores: S^T[tok0 + 16 h2 + 4grp + j][row r]
+    f32x4_t st[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) st = M::qk(kc[kk], qf[kk], st);
-    float x[4];
-    const int32_t tb = tok0 + 4 * grp;
+    for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) x[j] = (tb + j <= qpos) ? st[j] * a.scale_log2e : -INFINITY;
-    float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      for (int h2 = 0; h2 < 2; ++h2) st[h2] = M::qk(kf[h2][kk], qf[kk], st[h2]);
+    if (more) load_pair(c + 2, true, false);
+
+    // stage V; rows past the context or the part are zeroed (unwritten slots
+    // may hold NaN, and the second chunk may not have been loaded)
+    const int32_t tok_end = min(L, c1 * kChunk);
+    if (tok0 + 2 * kChunk > tok_end) {
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+          if (tok0 + 16 * h2 + 4 * r4 + grp >= tok_end) vf[h2][r4] = make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        *reinterpret_cast<uint4*>(vlds + (16 * h2 + 4 * r4 + grp) * kVRowBytes + 16 * r) = vf[h2][r4];
+    __asm__ volatile("" ::: "memory");
+    if (more) load_pair(c + 2, false, true);
+
+    float x[2][4];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int32_t tb = tok0 + 16 * h2 + 4 * grp;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        x[h2][j] = (tb + j <= qpos && tb + j < tok_end) ? st[h2][j] * a.scale_log2e : -INFINITY;
+    }
+    float mx = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
+                     fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
     mx = xor_max(mx, 16);
     mx = xor_max(mx, 32);
     const float m_new = fmaxf(m, mx);
-    float p[4];
+    float p[2][4];
     float alpha = 1.f;
     if (m_new == -INFINITY) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) p[j] = 0.f;
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) p[h2][j] = 0.f;
     } else {
       alpha = __builtin_amdgcn_exp2f(m - m_new);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) p[j] = __builtin_amdgcn_exp2f(x[j] - m_new);
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) p[h2][j] = __builtin_amdgcn_exp2f(x[h2][j] - m_new);
     }
     m = m_new;
-    lsum = lsum * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+    lsum = lsum * alpha + (((p[0][0] + p[0][1]) + (p[0][2] + p[0][3])) + ((p[1][0] + p[1][1]) + (p[1][2] + p[1][3])));
     if (__any(alpha != 1.f)) {  // wave-uniform: skip the rescale when no row's max moved
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
     }
-    i16x4_t pb;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) pb[j] = static_cast<short>(M::cvt(p[j]));
-
-    // stage V (rows past the context are zeroed: garbage there could be NaN)
-    if (tok0 + kChunk > L) {
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4)
-        if (tok0 + 4 * r4 + grp >= L) vc[r4] = make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4)
-      *reinterpret_cast<uint4*>(vlds + (4 * r4 + grp) * kVRowBytes + 16 * r) = vc[r4];
-    __asm__ volatile("" ::: "memory");
-    // A = V^T: lane r of group grp gets V[4grp + j][16dt + r] (j = 0..3)
-    const int rd_off = (4 * grp + (r >> 2)) * kVRowBytes + 8 * (r & 3);
+    // B = P^T for 32 tokens: k = 8grp + j holds token 4grp + j (j < 4) and
+    // 16 + 4grp + (j - 4); A = V^T uses the same token order.
+    const uint4 pb = make_uint4(M::pk(p[0][0], p[0][1]), M::pk(p[0][2], p[0][3]),
+                                M::pk(p[1][0], p[1][1]), M::pk(p[1][2], p[1][3]));
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-      const i16x4_t va = lds_read_tr16(vlds + rd_off + 32 * dt);
-      o[dt] = M::pv(va, pb, o[dt]);
+      const i16x4_t lo = lds_read_tr16(vlds + rd_off + 32 * dt);
+      const i16x4_t hi = lds_read_tr16(vlds + rd_off + 16 * kVRowBytes + 32 * dt);
+      const uint4 va = __builtin_bit_cast(uint4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      o[dt] = M::qk(va, pb, o[dt]);
     }
     __asm__ volatile("" ::: "memory");
   }
@@ -250,8 +317,12 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
 
 // Combine the parts of every split decode item: with m = max_p m_p,
 //   o = sum_p 2^(m_p - m) O_p / sum_p 2^(m_p - m) l_p.
+// One workgroup per (sequence, KV head); the per-(row, part) weights are
+// computed once into LDS, then each thread produces output elements.
 template <class F>
 __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
+  __shared__ float wts[kMaxRows][kMaxParts];
+  __shared__ float inv_den[kMaxRows];
   const int32_t s = blockIdx.x, g = blockIdx.y;
   const int32_t q0 = a.qsl[s];
   const int32_t qlen = a.qsl[s + 1] - q0;
@@ -263,33 +334,39 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
   if (np == 1) return;
   const int32_t rows = qlen * a.G;
   const float* base = a.ws + (static_cast<int64_t>(s) * a.Hkv + g) * a.P * (kMaxRows * kPartFloats);
-  for (int idx = threadIdx.x; idx < rows * kD; idx += blockDim.x) {
-    const int r = idx / kD, d = idx - r * kD;
+  if (threadIdx.x < rows) {
+    const int r = threadIdx.x;
     float mm = -INFINITY;
     for (int p = 0; p < np; ++p) mm = fmaxf(mm, base[(p * kMaxRows + r) * kPartFloats + kD]);
-    float num = 0.f, den = 0.f;
-    if (mm != -INFINITY) {
-      for (int p = 0; p < np; ++p) {
-        const float* e = base + (p * kMaxRows + r) * kPartFloats;
-        const float w = __builtin_amdgcn_exp2f(e[kD] - mm);
-        num = fmaf(w, e[d], num);
-        den = fmaf(w, e[kD + 1], den);
-      }
+    float den = 0.f;
+    for (int p = 0; p < np; ++p) {
+      const float* e = base + (p * kMaxRows + r) * kPartFloats;
+      const float w = mm == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(e[kD] - mm);
+      wts[r][p] = w;
+      den = fmaf(w, e[kD + 1], den);
     }
+    inv_den[r] = den > 0.f ? 1.f / den : 0.f;
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < rows * kD; idx += blockDim.x) {
+    const int r = idx / kD, d = idx - r * kD;
+    float num = 0.f;
+    for (int p = 0; p < np; ++p) num = fmaf(wts[r][p], base[(p * kMaxRows + r) * kPartFloats + d], num);
     const int32_t i_row = r / a.G, hg = r - i_row * a.G;
     const int64_t t = q0 + i_row;
-    a.out[(t * a.Hq + g * a.G + hg) * kD + d] = Mma<F>::cvt(den > 0.f ? num / den : 0.f);
+    a.out[(t * a.Hq + g * a.G + hg) * kD + d] = Mma<F>::cvt(num * inv_den[r]);
   }
 }
 
+// Parts per sequence the launch provides for: enough for max_seq_len.  A
+// longer sequence than the hint still works (its parts just get longer).
 int32_t decode_parts(int32_t S, int32_t Hkv, int32_t max_seqlen) {
-  const int64_t units = static_cast<int64_t>(S) * Hkv;
-  int64_t P = (kTargetItems + units - 1) / (units > 0 ? units : 1);
-  const int64_t max_useful = (ceil_div(max_seqlen > 0 ? max_seqlen : 1, kChunk) + kMinChunks - 1) / kMinChunks;
-  if (P > max_useful) P = max_useful;
+  (void)S;
+  (void)Hkv;
+  int32_t P = (ceil_div(max_seqlen > 0 ? max_seqlen : 1, kChunk) + kPartChunks - 1) / kPartChunks;
   if (P < 1) P = 1;
-  if (P > 64) P = 64;
-  return static_cast<int32_t>(P);
+  if (P > kMaxParts) P = kMaxParts;
+  return P;
 }
 
 }  // namespace
@@ -328,18 +405,21 @@ hipError_t launch_attn_fast(const AttnArgs& a, hipStream_t stream) {
   d.out = static_cast<uint16_t*>(a.out);
   d.ws = static_cast<float*>(a.workspace);
   d.d_err = a.d_err;
-  const int64_t items = static_cast<int64_t>(a.S) * a.Hkv * d.P;
-  if (items > INT32_MAX) return hipErrorInvalidValue;
+  d.grouped = a.Hkv < kGroupHeadsBelow ? 1 : 0;
+  const int64_t s_pad = d.grouped ? (a.S + kXcdRun - 1) / kXcdRun * kXcdRun : a.S;
+  const int64_t items = s_pad * a.Hkv * d.P;
+  const int64_t grid = (items + 8 * kXcdRun - 1) / (8 * kXcdRun) * (8 * kXcdRun);
+  if (grid > INT32_MAX) return hipErrorInvalidValue;
   d.n_items = static_cast<int32_t>(items);
 
   // prefill-class rows (query_len * G > 16): MFMA prefill kernel
   hipError_t e = launch_attn_prefill(a, kMaxRows, stream);
   if (e != hipSuccess) return e;
   if (a.dtype == PA_BF16) {
-    decode_kernel<BF16><<<d.n_items, 64, 0, stream>>>(d);
+    decode_kernel<BF16><<<static_cast<uint32_t>(grid), 64, 0, stream>>>(d);
     if (d.P > 1) merge_kernel<BF16><<<dim3(a.S, a.Hkv), 256, 0, stream>>>(d);
   } else {
-    decode_kernel<F16><<<d.n_items, 64, 0, stream>>>(d);
+    decode_kernel<F16><<<static_cast<uint32_t>(grid), 64, 0, stream>>>(d);
     if (d.P > 1) merge_kernel<F16><<<dim3(a.S, a.Hkv), 256, 0, stream>>>(d);
   }
   return hipGetLastError();

@@ -39,6 +39,7 @@ constexpr int kTile = 64;                          // KV tokens per tile
 constexpr int kRowBytes = 256;                     // one token row of one head (128 x 16 bit)
 constexpr int kTileBytes = kTile * kRowBytes;      // 16 KB per K or V tile
 constexpr int kStageBytes = 2 * kTileBytes;        // K tile then V tile
+constexpr float kRescaleSlack = 8.f;               // log2 units the running max may lag
 
 struct PrefillArgs {
   const uint16_t* q;
@@ -164,12 +165,28 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     const bool wave_active = wave_row0 < rows_total;
     const int32_t qpos_min_wave = L - qlen + wave_row0 / a.G;
 
-    float m[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};
-    f32x4_t o[2][8];
+    // Running max per row in log2 units.  It is only moved when a tile's max
+    // exceeds it by more than kRescaleSlack, so p = 2^(x - m) stays <= 2^8 and
+    // the O rescale is rare; numerator and denominator always share the same
+    // m, so the result is unchanged.
+    float m[2] = {-INFINITY, -INFINITY};
+    f32x4_t o[2][8], osum[2];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
+    for (int nt = 0; nt < 2; ++nt) {
+      osum[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) o[nt][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    // per-lane LDS byte offsets inside a stage: K fragment (chunk 4kk + grp of
+    // row r, + 16 mt rows) and transposed V read (row 4grp + r/4, + 16 / 32
+    // rows, chunk 2dt + (r%4)/2, half r%2).  Row offsets that are multiples of
+    // 16 (K) or 8 (V) leave the swizzle unchanged, so they fold into constants.
+    int koff[4], voff[8];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) koff[kk] = k_slot(r, 4 * kk + grp);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) voff[dt] = v_slot(4 * grp + (r >> 2), 2 * dt + ((r & 3) >> 1)) + 8 * (r & 1);
+    const uint4 ones = make_uint4(M::kOnePair, M::kOnePair, M::kOnePair, M::kOnePair);
 
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -179,88 +196,86 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
       const uint8_t* kt_lds = lds + stage * kStageBytes;
       const uint8_t* vt_lds = kt_lds + kTileBytes;
       if (wave_active) {
-        // S^T[16 mt + 4grp + j][row r of nt]
+        // S^T[16 mt + 4grp + j][row r of nt]; 8 independent MFMAs per K column block
         f32x4_t st[2][4];
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
           for (int mt = 0; mt < 4; ++mt) st[nt][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
+        for (int kk = 0; kk < 4; ++kk) {
+          uint4 ka[4];
 #pragma unroll
-          for (int kk = 0; kk < 4; ++kk) {
-            const uint4 ka = *reinterpret_cast<const uint4*>(kt_lds + k_slot(16 * mt + r, 4 * kk + grp));
+          for (int mt = 0; mt < 4; ++mt)
+            ka[mt] = *reinterpret_cast<const uint4*>(kt_lds + koff[kk] + mt * 16 * kRowBytes);
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) st[nt][mt] = M::qk(ka, qf[nt][kk], st[nt][mt]);
-          }
+          for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) st[nt][mt] = M::qk(ka[mt], qf[nt][kk], st[nt][mt]);
         }
 
         const bool need_mask = kt * kTile + kTile - 1 > qpos_min_wave;
         uint4 pb[2][2];
+        float alpha[2];
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
-          if (need_mask) {
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                const int32_t tok = kt * kTile + 16 * mt + 4 * grp + j;
-                if (tok > qpos[nt]) st[nt][mt][j] = -INFINITY;
-              }
-          }
-          float mx = -INFINITY;
+          float x[4][4];
 #pragma unroll
           for (int mt = 0; mt < 4; ++mt)
-            mx = fmaxf(mx, fmaxf(fmaxf(st[nt][mt][0], st[nt][mt][1]), fmaxf(st[nt][mt][2], st[nt][mt][3])));
-          mx = xor_max(mx, 16);
-          mx = xor_max(mx, 32);
-          const float m_new = fmaxf(m[nt], mx * a.scale_log2e);
-          float alpha = 1.f, ps = 0.f;
-          if (m_new == -INFINITY) {
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) st[nt][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-          } else {
-            alpha = __builtin_amdgcn_exp2f(m[nt] - m_new);
+            for (int j = 0; j < 4; ++j) x[mt][j] = st[nt][mt][j];
+          if (need_mask) {
+            const int32_t lim = qpos[nt] - (kt * kTile + 4 * grp);  // visible iff 16 mt + j <= lim
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                st[nt][mt][j] = __builtin_amdgcn_exp2f(fmaf(st[nt][mt][j], a.scale_log2e, -m_new));
-                ps += st[nt][mt][j];
-              }
+              for (int j = 0; j < 4; ++j)
+                if (16 * mt + j > lim) x[mt][j] = -INFINITY;
           }
-          m[nt] = m_new;
-          lsum[nt] = lsum[nt] * alpha + ps;
-          if (alpha != 1.f) {
-#pragma unroll
-            for (int dt = 0; dt < 8; ++dt) o[nt][dt] *= alpha;
+          float mx = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
+                           fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
+          mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(x[2][0], x[2][1]), fmaxf(x[2][2], x[2][3])),
+                               fmaxf(fmaxf(x[3][0], x[3][1]), fmaxf(x[3][2], x[3][3]))));
+          mx = xor_max(mx, 16);
+          mx = xor_max(mx, 32);
+          mx *= a.scale_log2e;
+          alpha[nt] = 1.f;
+          if (mx > m[nt] + kRescaleSlack) {
+            alpha[nt] = __builtin_amdgcn_exp2f(m[nt] - mx);  // 0 on the first visible tile
+            m[nt] = mx;
           }
+          const float msub = m[nt] == -INFINITY ? 0.f : m[nt];
+          float p[4][4];
 #pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            pb[nt][u].x = pack2(M::cvt(st[nt][2 * u][0]), M::cvt(st[nt][2 * u][1]));
-            pb[nt][u].y = pack2(M::cvt(st[nt][2 * u][2]), M::cvt(st[nt][2 * u][3]));
-            pb[nt][u].z = pack2(M::cvt(st[nt][2 * u + 1][0]), M::cvt(st[nt][2 * u + 1][1]));
-            pb[nt][u].w = pack2(M::cvt(st[nt][2 * u + 1][2]), M::cvt(st[nt][2 * u + 1][3]));
+          for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) p[mt][j] = __builtin_amdgcn_exp2f(fmaf(x[mt][j], a.scale_log2e, -msub));
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+            pb[nt][u] = make_uint4(M::pk(p[2 * u][0], p[2 * u][1]), M::pk(p[2 * u][2], p[2 * u][3]),
+                                   M::pk(p[2 * u + 1][0], p[2 * u + 1][1]),
+                                   M::pk(p[2 * u + 1][2], p[2 * u + 1][3]));
+        }
+        if (__any(alpha[0] != 1.f || alpha[1] != 1.f)) {  // wave-uniform, rare after the first tiles
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) {
+            osum[nt] *= alpha[nt];
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) o[nt][dt] *= alpha[nt];
           }
         }
 
-        // O^T += V^T . P^T over the two 32-token halves of the tile.  Lane r of
-        // group grp supplies row 4grp + r/4 (+ 32u, + 16) and 4 columns
-        // 16dt + 4(r%4): 8 bytes inside chunk 2dt + (r%4)/2.
-        const int rsub = r >> 2, hb = 8 * ((r & 3) & 1), csub = (r & 3) >> 1;
+        // O^T += V^T . P^T over the two 32-token halves; the row sums of P ride
+        // along as one more MFMA against a tile of ones.
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          const int row_lo = 32 * u + 4 * grp + rsub;
-          const int row_hi = row_lo + 16;
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) osum[nt] = M::qk(ones, pb[nt][u], osum[nt]);
 #pragma unroll
           for (int dt = 0; dt < 8; ++dt) {
-            const i16x4_t lo = lds_read_tr16(vt_lds + v_slot(row_lo, 2 * dt + csub) + hb);
-            const i16x4_t hi = lds_read_tr16(vt_lds + v_slot(row_hi, 2 * dt + csub) + hb);
-            uint4 va;
-            va.x = pack2(static_cast<uint16_t>(lo[0]), static_cast<uint16_t>(lo[1]));
-            va.y = pack2(static_cast<uint16_t>(lo[2]), static_cast<uint16_t>(lo[3]));
-            va.z = pack2(static_cast<uint16_t>(hi[0]), static_cast<uint16_t>(hi[1]));
-            va.w = pack2(static_cast<uint16_t>(hi[2]), static_cast<uint16_t>(hi[3]));
+            const i16x4_t lo = lds_read_tr16(vt_lds + voff[dt] + (32 * u) * kRowBytes);
+            const i16x4_t hi = lds_read_tr16(vt_lds + voff[dt] + (32 * u + 16) * kRowBytes);
+            const uint4 va = __builtin_bit_cast(uint4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) o[nt][dt] = M::qk(va, pb[nt][u], o[nt][dt]);
           }
@@ -273,20 +288,16 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
 
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-      float l = xor_sum(lsum[nt], 16);
-      l = xor_sum(l, 32);
       const int32_t rho = wave_row0 + nt * 16 + r;
       if (rho >= rows_total) continue;
       const int32_t i = rho / a.G, hg = rho - (rho / a.G) * a.G;
       uint16_t* orow = a.out + ((static_cast<int64_t>(q0) + i) * a.Hq + g * a.G + hg) * kD;
+      const float l = osum[nt][0];
       const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        uint2 w;
-        w.x = pack2(M::cvt(o[nt][dt][0] * inv), M::cvt(o[nt][dt][1] * inv));
-        w.y = pack2(M::cvt(o[nt][dt][2] * inv), M::cvt(o[nt][dt][3] * inv));
-        *reinterpret_cast<uint2*>(orow + 16 * dt + 4 * grp) = w;
-      }
+      for (int dt = 0; dt < 8; ++dt)
+        *reinterpret_cast<uint2*>(orow + 16 * dt + 4 * grp) =
+            make_uint2(M::pk(o[nt][dt][0] * inv, o[nt][dt][1] * inv), M::pk(o[nt][dt][2] * inv, o[nt][dt][3] * inv));
     }
   }
 }

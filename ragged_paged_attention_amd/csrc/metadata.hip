@@ -53,9 +53,6 @@ __global__ __launch_bounds__(kScanThreads) void meta_scan_kernel(
     int32_t* __restrict__ d_err) {
   __shared__ int64_t lds_q[kWaves];
   __shared__ int64_t lds_s[kWaves];
-  __shared__ int32_t lds_stat[6];
-  if (threadIdx.x < 6) lds_stat[threadIdx.x] = 0;
-  __syncthreads();
   int64_t carry_q = 0, carry_s = 0;
   int32_t n_dec = 0, n_pre = 0, dec_tok = 0, pre_tok = 0, max_q = 0, max_s = 0;
   int32_t err = 0;
@@ -94,14 +91,27 @@ __global__ __launch_bounds__(kScanThreads) void meta_scan_kernel(
   }
   if (err) flag(d_err, err);
   if (stats) {
-    atomicAdd(&lds_stat[0], n_dec);
-    atomicAdd(&lds_stat[1], n_pre);
-    atomicAdd(&lds_stat[2], dec_tok);
-    atomicAdd(&lds_stat[3], pre_tok);
-    atomicMax(&lds_stat[4], max_q);
-    atomicMax(&lds_stat[5], max_s);
+    // workgroup reduction of the six counters: within each wave by shuffles,
+    // then one value per wave through LDS
+    int32_t v[6] = {n_dec, n_pre, dec_tok, pre_tok, max_q, max_s};
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) v[c] += __shfl_xor(v[c], off, 64);
+      v[4] = max(v[4], __shfl_xor(v[4], off, 64));
+      v[5] = max(v[5], __shfl_xor(v[5], off, 64));
+    }
+    __shared__ int32_t lds_red[kWaves][6];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0)
+      for (int c = 0; c < 6; ++c) lds_red[wave][c] = v[c];
     __syncthreads();
-    if (threadIdx.x < 6) stats[threadIdx.x] = lds_stat[threadIdx.x];
+    if (threadIdx.x < 6) {
+      const int c = threadIdx.x;
+      int32_t acc = lds_red[0][c];
+      for (int w = 1; w < kWaves; ++w) acc = c < 4 ? acc + lds_red[w][c] : max(acc, lds_red[w][c]);
+      stats[c] = acc;
+    }
   }
 }
 

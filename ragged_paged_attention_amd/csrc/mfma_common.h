@@ -23,8 +23,17 @@ constexpr int kVRowBytes = 288;  // LDS row pitch of a staged V tile: 256 B + 32
 // pv16: v_mfma_f32_16x16x16 (4 per lane).
 //   A[m = lane%16][k = 8*(lane/16) + j]  (16x16x32)   A[m][k = 4*(lane/16) + j]  (16x16x16)
 //   B[k = same][n = lane%16]             D[m = 4*(lane/16) + j][n = lane%16]
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
 template <class F> struct Mma;
 template <> struct Mma<BF16> {
+  static constexpr uint32_t kOnePair = 0x3F803F80u;  // two bf16 1.0
+  // two floats -> two bf16 (nearest-even) in one 32-bit word, low half first
+  static __device__ __forceinline__ uint32_t pk(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{lo, hi}), bf16x2_t));
+  }
   static __device__ __forceinline__ f32x4_t qk(uint4 a, uint4 b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
@@ -37,6 +46,10 @@ template <> struct Mma<BF16> {
   }
 };
 template <> struct Mma<F16> {
+  static constexpr uint32_t kOnePair = 0x3C003C00u;  // two f16 1.0
+  static __device__ __forceinline__ uint32_t pk(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{lo, hi}), f16x2_t));
+  }
   static __device__ __forceinline__ f32x4_t qk(uint4 a, uint4 b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
                                                   __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
