@@ -180,6 +180,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void
   // as the current V is in LDS.  A pair's second chunk may lie past the part
   // (odd chunk counts): it is then neither loaded nor counted.
   uint4 kf[2][4], vf[2][4];
+  // Sequence-fastest order streams K/V past the caches (read once: 6.0 vs
+  // 5.6 TB/s measured); in head-grouped order neighbouring sequences may share
+  // prefix blocks, so those loads stay cacheable for the L2 hits.
+  const bool stream = !a.grouped;
   auto load_pair = [&](int32_t c, bool do_k, bool do_v) {
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
@@ -188,12 +192,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void
         if (do_k) {
           const uint16_t* kp = kbase + (slot0 + r) * slot_stride + 8 * grp;
 #pragma unroll
-          for (int kk = 0; kk < 4; ++kk) kf[h2][kk] = ld16(kp + 32 * kk);
+          for (int kk = 0; kk < 4; ++kk) kf[h2][kk] = stream ? ld16_nt(kp + 32 * kk) : ld16(kp + 32 * kk);
         }
         if (do_v) {
           const uint16_t* vp = vbase + (slot0 + grp) * slot_stride + 8 * r;
 #pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) vf[h2][r4] = ld16(vp + 4 * r4 * slot_stride);
+          for (int r4 = 0; r4 < 4; ++r4)
+            vf[h2][r4] = stream ? ld16_nt(vp + 4 * r4 * slot_stride) : ld16(vp + 4 * r4 * slot_stride);
         }
       } else {
 #pragma unroll

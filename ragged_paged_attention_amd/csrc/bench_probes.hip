@@ -12,9 +12,14 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const uint4* __restric
   uint32_t acc = 0;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
   int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  for (; i + 3 * stride < n; i += 4 * stride) {
-    const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
-    acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+  typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+  const u4v* s4 = reinterpret_cast<const u4v*>(src);
+  for (; i + 7 * stride < n; i += 8 * stride) {
+    u4v v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(s4 + i + u * stride);  // streaming
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
   for (; i < n; i += stride) {
     const uint4 a = src[i];
@@ -71,8 +76,8 @@ extern "C" pa_status_t pa_bench_stream_read(const void* src, size_t bytes, uint3
   if (bytes % 16 || reinterpret_cast<uintptr_t>(src) % 16) return PA_ERR_SHAPE;
   (void)hipGetLastError();
   const int64_t n = static_cast<int64_t>(bytes / 16);
-  int64_t blocks = (n + 1023) / 1024;
-  if (blocks > 256 * 32) blocks = 256 * 32;
+  int64_t blocks = (n + 2047) / 2048;
+  if (blocks > 32768) blocks = 32768;
   if (blocks < 1) blocks = 1;
   pa::stream_read_kernel<<<static_cast<uint32_t>(blocks), 256, 0, static_cast<hipStream_t>(stream)>>>(
       static_cast<const uint4*>(src), n, sink);
