@@ -3,22 +3,28 @@
 A step is the whole hot path over one batch, in the order the pages give
 ("vLLM Continuous Batching：从 Forward Shape 理解两个核心参数" §2.3): build the
 flat-batch metadata, scatter the new K/V by slot_mapping, then ragged paged
-attention.  All three run as libpa kernels (C ABI) on the current stream.
+attention (decode rows, split-K merge, prefill chunks, one mixed batch).  All
+of it runs as libpa kernels (C ABI) on torch's current stream.
 
-Default workload: the chunked-prefill mixed batch (240 decode sequences with
-log-uniform contexts 128..8192 plus 16 prefill chunks of 497 tokens with
-0..4096 earlier context; T = 8192, GQA 32/8, head_dim 128, block_size 16,
-bf16).  The decode-only batch (100 x 2001-token contexts, 32/32 heads) is
-timed too, for the decode KV-read bandwidth and the roofline line.
+Step workload (the JSON `value`): the chunked-prefill mixed batch -- 240
+decode sequences with log-uniform contexts 128..8192 plus 16 prefill chunks of
+497 tokens with 0..4096 earlier tokens; T = 8192 new tokens, S = 256, GQA
+32/8 heads, head_dim 128, block_size 16, bf16, seeded synthetic data,
+inputs resident in HBM before timing.  value = T / step time (tokens/s).
 
-Prints ONE JSON line.  Inputs are seeded synthetic data, resident in HBM
-before the timed region starts.
+Also reported (same run): the decode batch's KV-read bandwidth (100 x
+2001-token contexts, 32/32 heads) against HBM peak and against measured read
+ceilings, the ragged prefill batch's TFLOP/s (16/128/1024/2048-token prompts),
+the shared-prefix long-context decode batch, and the oracle's CPU throughput
+on a sample of the step's rows.  Prints ONE JSON line on stdout.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -26,8 +32,15 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
-BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, TFLOP/s
+BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, TFLOP/s (256 CU x 2.4 GHz x 4096 FLOP/clk)
 METRIC = "decode KV-read GB/s (% HBM peak) + mixed-batch attn tokens/s, 1 MI355X"
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = {
+    "decode_kernel": "ragged_paged_attention_amd/csrc/attn_fast.hip",
+    "merge_kernel": "ragged_paged_attention_amd/csrc/attn_fast.hip",
+    "prefill_kernel": "ragged_paged_attention_amd/csrc/attn_prefill.hip",
+    "write_kv_kernel": "ragged_paged_attention_amd/csrc/write_kv.hip",
+}
 
 
 def parse():
@@ -35,12 +48,23 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=4, help="workload for the step (1-5)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["step", "decode", "prefill", "shared"], default=None,
                     help="run one leg only (for profiling)")
     ap.add_argument("--cpu-sample-rows", type=int, default=2048)
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("ROCPROF_DIR", "OUT_MD"),
+                    help="write a kernel-time summary (profiles/*.md) from a rocprofv3 --kernel-trace --stats "
+                         "--output-format csv directory; no GPU needed")
+    ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "KERNEL", "WORKLOAD"),
+                    help="write profiles/KERNEL.WORKLOAD.pmc.md from two rocprofv3 --pmc runs (FETCH_SIZE, "
+                         "WRITE_SIZE) of a bench leg, calibrated on the leg's copy of known size; no GPU needed")
+    ap.add_argument("--command", default="", help="the command that produced the rocprofv3 output (recorded)")
     return ap.parse_args()
+
+
+def source_hash(rel: str) -> str:
+    with open(os.path.join(ROOT, rel), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
 class Timer:
@@ -64,6 +88,16 @@ class Timer:
         torch.cuda.synchronize()
         return start.elapsed_time(end) / iters  # ms
 
+    def kernels(self, rpa, fn, iters):
+        """Per-kernel launch durations (library-side HIP events on the launch
+        stream) over `iters` calls of fn: {name: (launches, avg ms)}."""
+        self.torch.cuda.synchronize()
+        rpa.pa_bench_timing_begin()
+        for _ in range(iters):
+            fn()
+        res = rpa.pa_bench_timing_end()
+        return {k: (n, ms / n) for k, (n, ms) in res.items()}
+
 
 def setup(w, torch):
     from tests.gpu_path import GpuRun
@@ -72,21 +106,32 @@ def setup(w, torch):
     return g
 
 
-def step_fn(g, w, rpa, workspace, meta_out):
-    db = g.db
-    from ragged_paged_attention_amd.step import forward_step
+def workspace_for(w, rpa, torch):
+    need = rpa.pa_attention_workspace_size(w.num_seqs, w.num_tokens, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                                           w.max_seq_len)
+    return torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
 
-    def fn():
-        forward_step(db.q, db.k, db.v, g.k_cache, g.v_cache, db.query_lens, db.seq_lens, db.block_tables,
-                     w.scale, max(1, w.max_query_len), max(1, w.max_seq_len), out=g.out_buf,
-                     workspace=workspace, meta_out=meta_out)
-    return fn
+
+def traffic_from_profiles(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    (FETCH_SIZE + WRITE_SIZE, calibrated on a copy of known size), or None if
+    there is none or the kernel's source changed since it was taken."""
+    path = os.path.join(PROFILES, f"{kernel}.{workload}.pmc.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"source_sha256_16:\s*([0-9a-f]{16})", text)
+    b = re.search(r"hbm_bytes_per_launch:\s*([0-9.e+]+)", text)
+    if not m or not b or m.group(1) != source_hash(KERNEL_SOURCES[kernel]):
+        return None
+    return float(b.group(1))
 
 
 def cpu_baseline(w, rows_wanted, seed=0):
     """The oracle, as it stands, on a random sample of the step's rows: its
-    metadata, its KV write of the step's rows, and attention for the sampled
-    rows.  Pool filled with history first (untimed, like the GPU leg)."""
+    metadata, its KV write of all the step's new rows, and fp64 attention for
+    the sampled rows.  The pool is filled with history first (untimed, like
+    the GPU leg)."""
     import numpy as np
     import oracle
     from threadpoolctl import threadpool_limits
@@ -107,145 +152,267 @@ def cpu_baseline(w, rows_wanted, seed=0):
                          w.scale, w.dtype, rows=rows)
         dt = time.perf_counter() - t0
     return {"value": len(rows) / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{len(rows)} random rows of the {w.num_tokens}-token step (seed {seed}), metadata + "
-                      f"KV write of all new rows + fp64 attention of the sampled rows, {dt:.2f} s, BLAS pinned to 1 thread"}
+            "sample": f"{len(rows)} random rows of the {w.num_tokens}-token mixed step (seed {seed}): metadata + "
+                      f"KV write of all new rows + fp64 attention of the sampled rows in {dt:.2f} s; "
+                      f"NumPy with BLAS pinned to 1 thread"}
+
+
+def work_split(w):
+    """Algorithmic work of the step's two attention kernels: KV/Q/O bytes of
+    the decode-class sequences (query_len * G <= 16) and causal FLOPs of the
+    prefill-class ones."""
+    import numpy as np
+    from workloads import accounting
+    G = w.num_q_heads // w.num_kv_heads
+    ql, sl = w.step.query_lens.astype(np.int64), w.step.seq_lens.astype(np.int64)
+    dec = ql * G <= 16
+    es = accounting.itemsize(w.dtype)
+    dec_bytes = (accounting.kv_read_bytes(sl[dec], w.num_kv_heads, w.head_dim, w.dtype)
+                 + 2 * int(ql[dec].sum()) * w.num_q_heads * w.head_dim * es)
+    pre_flops = accounting.attention_flops(ql[~dec], sl[~dec], w.num_q_heads, w.head_dim)
+    return dec_bytes, pre_flops
+
+
+def roofline_for(kernel, avg_ms, w, workload_tag):
+    dec_bytes, pre_flops = work_split(w)
+    if kernel == "prefill_kernel":
+        a = pre_flops / (avg_ms / 1e3) / 1e12
+        return {"bound": "mfma", "kernel": kernel, "achieved": a, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": a / BF16_PEAK_TFLOPS, "traffic": traffic_from_profiles(kernel, workload_tag),
+                "work_per_launch": pre_flops, "avg_launch_ms": avg_ms}
+    a = dec_bytes / (avg_ms / 1e3) / 1e9
+    return {"bound": "hbm", "kernel": kernel, "achieved": a, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": a / HBM_PEAK_GBS, "traffic": traffic_from_profiles(kernel, workload_tag),
+            "work_per_launch": dec_bytes, "avg_launch_ms": avg_ms}
+
+
+CAL_BYTES = 256 << 20  # calibration copy: 256 MiB read + 256 MiB written
+
+
+def _csv_rows(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def _find(dirpath, suffix):
+    for root, _, files in os.walk(dirpath):
+        for f in files:
+            if f.endswith(suffix):
+                return os.path.join(root, f)
+    raise FileNotFoundError(f"no *{suffix} under {dirpath}")
+
+
+def summarize_trace(src_dir, out_md, command):
+    rows = _csv_rows(_find(src_dir, "kernel_stats.csv"))
+    lines = [f"# Kernel time summary: {os.path.basename(out_md)[:-3]}", "",
+             f"Command (run from the repository root on one MI355X): `{command}`", "",
+             "| kernel | calls | avg us | min us | max us | share of GPU time |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        name = re.sub(r"\(anonymous namespace\)::", "", r["Name"])
+        name = re.sub(r"\(.*", "", name).replace("void ", "")
+        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+                     f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}% |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(f"wrote {out_md}")
+
+
+def _counter_per_dispatch(rows, counter, kernel_substr):
+    per = {}
+    for r in rows:
+        if r["Counter_Name"] == counter and kernel_substr in r["Kernel_Name"]:
+            per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    return per
+
+
+def summarize_pmc(fetch_dir, write_dir, kernel, workload, command):
+    """FETCH_SIZE / WRITE_SIZE are in KiB per dispatch.  The bench leg runs a
+    copy of CAL_BYTES (read CAL_BYTES, write CAL_BYTES); the ratio of what the
+    counters report for it to CAL_BYTES is the calibration factor applied to
+    the kernel's counts."""
+    fr = _csv_rows(_find(fetch_dir, "counter_collection.csv"))
+    wr = _csv_rows(_find(write_dir, "counter_collection.csv"))
+    kf = _counter_per_dispatch(fr, "FETCH_SIZE", kernel)
+    kw = _counter_per_dispatch(wr, "WRITE_SIZE", kernel)
+    # torch's fill_ (writes) and copy_ (reads and writes) of the calibration buffers
+    cf, cw = [], []
+    for cal in ("copyBuffer", "elementwise_kernel"):
+        cf += list(_counter_per_dispatch(fr, "FETCH_SIZE", cal).values())
+        cw += list(_counter_per_dispatch(wr, "WRITE_SIZE", cal).values())
+    cal_kib = CAL_BYTES / 1024
+    f_fac = max(cf, key=lambda v: -abs(v - cal_kib)) / cal_kib if cf else 1.0
+    w_fac = max(cw, key=lambda v: -abs(v - cal_kib)) / cal_kib if cw else 1.0
+    fetch = sum(kf.values()) / max(1, len(kf)) * 1024 / f_fac
+    write = sum(kw.values()) / max(1, len(kw)) * 1024 / w_fac
+    out_md = os.path.join(PROFILES, f"{kernel}.{workload}.pmc.md")
+    text = f"""# HBM traffic: {kernel} on the {workload} workload
+
+Commands (run from the repository root on one MI355X):
+- `{command.replace("COUNTER", "FETCH_SIZE")}`
+- `{command.replace("COUNTER", "WRITE_SIZE")}`
+
+Counters are KiB per dispatch.  Calibration: the same bench leg copies {CAL_BYTES >> 20} MiB with torch
+(`copy_`); FETCH_SIZE read {f_fac:.4f}x and WRITE_SIZE {w_fac:.4f}x of the known bytes for it, and the
+kernel's counts are divided by those factors.
+
+| quantity | value |
+|---|---|
+| dispatches measured | {len(kf)} (FETCH) / {len(kw)} (WRITE) |
+| FETCH_SIZE per dispatch, calibrated | {fetch / 1e6:.2f} MB |
+| WRITE_SIZE per dispatch, calibrated | {write / 1e6:.2f} MB |
+| calibration factors (fetch, write) | {f_fac:.4f}, {w_fac:.4f} |
+
+hbm_bytes_per_launch: {fetch + write:.6e}
+source_sha256_16: {source_hash(KERNEL_SOURCES[kernel])}
+"""
+    with open(out_md, "w") as f:
+        f.write(text)
+    print(f"wrote {out_md}")
 
 
 def main():
     args = parse()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace[0], args.summarize_trace[1], args.command)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc, args.command)
+        return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): this build has no multi-GPU path",
-              file=sys.stderr)
+        print(f"bench.py measures one GPU only (--gpus {args.gpus} was asked for): this build has no multi-GPU "
+              "path; run it with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch
 
     import ragged_paged_attention_amd as rpa
+    from ragged_paged_attention_amd.step import forward_step
     from workloads import accounting, config
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     timer = Timer(torch)
-    result = {"metric": METRIC, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-              "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "data": "synthetic"}
+    # a copy of known size, for calibrating HBM byte counters in profiling runs
+    cal_src = torch.empty(CAL_BYTES // 2, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+    cal_dst = torch.empty_like(cal_src)
+    cal_dst.copy_(cal_src)
+    torch.cuda.synchronize()
+    del cal_src, cal_dst
+    result = {"metric": METRIC, "value": None, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+              "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True, "scaling": "weak",
+              "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) bf16, random block placement)"}
 
-    # ---------------- step on the mixed batch ----------------
+    # ---------------- the step: mixed batch ----------------
     if args.only in (None, "step"):
         t0 = time.time()
-        w = config(args.config, poison=False)
-        print(f"[bench] generated config {args.config} {w.summary()} in {time.time() - t0:.1f}s", file=sys.stderr,
-              flush=True)
+        w = config(4, poison=False)
+        print(f"[bench] mixed batch {w.summary()} generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
         g = setup(w, torch)
-        g.out_buf = torch.empty_like(g.db.q)
-        need = rpa.pa_attention_workspace_size(w.num_seqs, w.num_tokens, w.num_q_heads, w.num_kv_heads,
-                                               w.head_dim, w.max_seq_len)
-        ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
-        meta_out = {}
-        fn = step_fn(g, w, rpa, ws, None)
-        ms = timer.time(fn, args.steps, args.warmup)
-        # per-call split of the step
+        out = torch.empty_like(g.db.q)
+        ws = workspace_for(w, rpa, torch)
         db = g.db
-        md = rpa.pa_build_metadata(db.query_lens, db.seq_lens, w.num_tokens, db.block_tables, w.block_size,
-                                   w.num_blocks)
-        ms_meta = timer.time(lambda: rpa.pa_build_metadata(db.query_lens, db.seq_lens, w.num_tokens,
-                                                           db.block_tables, w.block_size, w.num_blocks, out=md),
-                             args.steps, 2)
-        ms_write = timer.time(lambda: rpa.pa_write_kv(db.k, db.v, md["slot_mapping"], g.k_cache, g.v_cache),
-                              args.steps, 2)
-        attn = lambda: rpa.pa_attention(db.q, g.k_cache, g.v_cache, db.block_tables, md["query_start_loc"],
-                                        db.seq_lens, w.max_query_len, w.max_seq_len, w.scale, out=g.out_buf,
-                                        workspace=ws)
-        ms_attn = timer.time(attn, args.steps, 2)
-        kv_bytes = accounting.kv_read_bytes(w.step.seq_lens, w.num_kv_heads, w.head_dim, w.dtype)
-        flops = accounting.attention_flops(w.step.query_lens, w.step.seq_lens, w.num_q_heads, w.head_dim)
+
+        def step():
+            forward_step(db.q, db.k, db.v, g.k_cache, g.v_cache, db.query_lens, db.seq_lens, db.block_tables,
+                         w.scale, w.max_query_len, w.max_seq_len, out=out, workspace=ws)
+
+        ms = timer.time(step, args.steps, args.warmup)
+        kern = timer.kernels(rpa, step, args.steps)
         ql = w.step.query_lens
+        dec_bytes, pre_flops = work_split(w)
         result.update({
             "value": w.num_tokens / (ms / 1e3), "ms_per_step": ms, "dtype": w.dtype,
-            "config": {"workload": w.name, "global_batch": w.num_seqs, "tokens": w.num_tokens,
-                       "n_decode": int((ql == 1).sum()), "n_prefill": int((ql > 1).sum()),
-                       "seq_len_max": w.max_seq_len, "heads": f"{w.num_q_heads}/{w.num_kv_heads}",
-                       "head_dim": w.head_dim, "block_size": w.block_size, "seed": w.seed},
-            "step_split_ms": {"pa_build_metadata": ms_meta, "pa_write_kv": ms_write, "pa_attention": ms_attn},
-            "step_kv_bytes": kv_bytes, "step_flops": flops,
+            "config": {"workload": "chunked-prefill mixed batch", "seqs": w.num_seqs, "tokens": w.num_tokens,
+                       "n_decode": int((ql == 1).sum()), "n_prefill_chunks": int((ql > 1).sum()),
+                       "chunk_len": int(ql.max()), "seq_len_max": w.max_seq_len,
+                       "heads_q_kv": [w.num_q_heads, w.num_kv_heads], "head_dim": w.head_dim,
+                       "block_size": w.block_size, "pool_blocks": w.num_blocks, "seed": w.seed},
+            "kernels_ms_per_step": {k: round(n * avg / args.steps, 5) for k, (n, avg) in kern.items()},
+            "step_work": {"decode_bytes": dec_bytes, "prefill_flops": pre_flops},
         })
+        weight = lambda k: kern.get(k, (0, 0.0))[0] * kern.get(k, (0, 0.0))[1]
+        dominant = max(("decode_kernel", "prefill_kernel"), key=weight)
+        result["roofline"] = roofline_for(dominant, kern[dominant][1], w, w.name)
+        other = "prefill_kernel" if dominant == "decode_kernel" else "decode_kernel"
+        if other in kern:
+            result["roofline_other_kernel"] = roofline_for(other, kern[other][1], w, w.name)
         if not args.no_cpu_baseline:
-            w_cpu = config(args.config, poison=False)
-            result["cpu_baseline"] = cpu_baseline(w_cpu, args.cpu_sample_rows)
-        del g, ws
+            result["cpu_baseline"] = cpu_baseline(config(4, poison=False), args.cpu_sample_rows)
+        del g, ws, out
         torch.cuda.empty_cache()
 
     # ---------------- decode-only batch: KV-read bandwidth ----------------
     if args.only in (None, "decode"):
         w3 = config(3, poison=False)
-        g3 = setup(w3, torch)
-        g3.out_buf = torch.empty_like(g3.db.q)
+        g3 = setup(w3, torch).write_step_rows()
         db = g3.db
-        md3 = rpa.pa_build_metadata(db.query_lens, db.seq_lens, w3.num_tokens, db.block_tables, w3.block_size,
-                                    w3.num_blocks)
-        rpa.pa_write_kv(db.k, db.v, md3["slot_mapping"], g3.k_cache, g3.v_cache)
-        need = rpa.pa_attention_workspace_size(w3.num_seqs, w3.num_tokens, w3.num_q_heads, w3.num_kv_heads,
-                                               w3.head_dim, w3.max_seq_len)
-        ws3 = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
-        attn3 = lambda: rpa.pa_attention(db.q, g3.k_cache, g3.v_cache, db.block_tables, md3["query_start_loc"],
-                                         db.seq_lens, w3.max_query_len, w3.max_seq_len, w3.scale, out=g3.out_buf,
-                                         workspace=ws3)
+        ws3 = workspace_for(w3, rpa, torch)
+        out3 = torch.empty_like(db.q)
+        qsl3 = g3.meta["query_start_loc"]
+        attn3 = lambda: rpa.pa_attention(db.q, g3.k_cache, g3.v_cache, db.block_tables, qsl3, db.seq_lens,
+                                         w3.max_query_len, w3.max_seq_len, w3.scale, out=out3, workspace=ws3)
         ms3 = timer.time(attn3, max(args.steps, 20), args.warmup)
+        kern3 = timer.kernels(rpa, attn3, 10)
         kv3 = accounting.kv_read_bytes(w3.step.seq_lens, w3.num_kv_heads, w3.head_dim, w3.dtype)
         gbs = kv3 / (ms3 / 1e3) / 1e9
-        # ceilings on this machine: a contiguous streaming read of the K cache,
-        # and the same paged gather as the decode kernel with no arithmetic
         sink = torch.zeros(1, dtype=torch.int32, device="cuda")
         ms_stream = timer.time(lambda: rpa.pa_bench_stream_read(g3.k_cache, sink), 10, 3)
         stream_gbs = g3.k_cache.numel() * 2 / (ms_stream / 1e3) / 1e9
-        ms_paged = timer.time(lambda: rpa.pa_bench_paged_read(g3.k_cache, g3.v_cache, db.block_tables, db.seq_lens,
-                                                              w3.max_seq_len, sink), 20, 3)
+        ms_paged = timer.time(lambda: rpa.pa_bench_paged_read(g3.k_cache, g3.v_cache, db.block_tables,
+                                                              db.seq_lens, w3.max_seq_len, sink), 20, 3)
         rounded = int(((w3.step.seq_lens.astype("int64") + 15) // 16 * 16).sum()) * 2 * w3.num_kv_heads * 256
-        paged_gbs = rounded / (ms_paged / 1e3) / 1e9
-        result["decode_kv_read"] = {"workload": w3.name, "GBps": gbs, "frac_hbm_peak": gbs / HBM_PEAK_GBS,
-                                    "kv_bytes": kv3, "ms": ms3, "tokens": w3.num_tokens,
-                                    "seqs": w3.num_seqs, "seq_len": w3.max_seq_len,
-                                    "stream_read_GBps": stream_gbs, "paged_read_no_math_GBps": paged_gbs}
-        result["roofline"] = {"bound": "hbm", "kernel": "pa_attention (decode batch)", "achieved": gbs,
-                              "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": None}
+        result["decode_kv_read"] = {
+            "workload": "decode batch: 100 seqs x 2001 tokens, 32/32 heads, D 128, bs 16, bf16",
+            "GBps": gbs, "frac_hbm_peak": gbs / HBM_PEAK_GBS, "kv_bytes": kv3, "ms_per_call": ms3,
+            "kernels_ms": {k: round(avg, 5) for k, (n, avg) in kern3.items()},
+            "decode_kernel_GBps": kv3 / (kern3["decode_kernel"][1] / 1e3) / 1e9,
+            "ceiling_stream_read_GBps": stream_gbs,
+            "ceiling_paged_read_no_math_GBps": rounded / (ms_paged / 1e3) / 1e9}
+        if args.only == "decode":
+            result["roofline"] = roofline_for("decode_kernel", kern3["decode_kernel"][1], w3, w3.name)
+        del g3, ws3, out3
+        torch.cuda.empty_cache()
+
     # ---------------- shared-prefix long-context decode ----------------
     if args.only in (None, "shared"):
         w5 = config(5, poison=False)
-        g5 = setup(w5, torch)
-        g5.out_buf = torch.empty_like(g5.db.q)
+        g5 = setup(w5, torch).write_step_rows()
         db = g5.db
-        md5 = rpa.pa_build_metadata(db.query_lens, db.seq_lens, w5.num_tokens, db.block_tables, w5.block_size,
-                                    w5.num_blocks)
-        rpa.pa_write_kv(db.k, db.v, md5["slot_mapping"], g5.k_cache, g5.v_cache)
-        need = rpa.pa_attention_workspace_size(w5.num_seqs, w5.num_tokens, w5.num_q_heads, w5.num_kv_heads,
-                                               w5.head_dim, w5.max_seq_len)
-        ws5 = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
-        attn5 = lambda: rpa.pa_attention(db.q, g5.k_cache, g5.v_cache, db.block_tables, md5["query_start_loc"],
-                                         db.seq_lens, w5.max_query_len, w5.max_seq_len, w5.scale, out=g5.out_buf,
-                                         workspace=ws5)
+        ws5 = workspace_for(w5, rpa, torch)
+        out5 = torch.empty_like(db.q)
+        qsl5 = g5.meta["query_start_loc"]
+        attn5 = lambda: rpa.pa_attention(db.q, g5.k_cache, g5.v_cache, db.block_tables, qsl5, db.seq_lens,
+                                         w5.max_query_len, w5.max_seq_len, w5.scale, out=out5, workspace=ws5)
         ms5 = timer.time(attn5, max(args.steps, 20), args.warmup)
         kv5 = accounting.kv_read_bytes(w5.step.seq_lens, w5.num_kv_heads, w5.head_dim, w5.dtype)
         uq5 = accounting.unique_kv_bytes_fast(w5.step.block_tables, w5.step.seq_lens, w5.block_size,
                                               w5.num_kv_heads, w5.head_dim, w5.dtype)
-        result["shared_prefix_decode"] = {"workload": w5.name, "logical_GBps": kv5 / (ms5 / 1e3) / 1e9,
-                                          "unique_GBps": uq5 / (ms5 / 1e3) / 1e9, "logical_bytes": kv5,
-                                          "unique_bytes": uq5, "ms": ms5}
-        del g5, ws5
+        result["shared_prefix_decode"] = {
+            "workload": "64 seqs in 4 groups sharing 16384-token prefixes + 512 private, 64/8 heads, bf16",
+            "ms_per_call": ms5, "logical_GBps": kv5 / (ms5 / 1e3) / 1e9, "unique_GBps": uq5 / (ms5 / 1e3) / 1e9,
+            "logical_bytes": kv5, "unique_bytes": uq5}
+        del g5, ws5, out5
         torch.cuda.empty_cache()
 
     # ---------------- ragged prefill batch: MFMA throughput ----------------
     if args.only in (None, "prefill"):
         w2 = config(2, poison=False)
-        g2 = setup(w2, torch)
-        g2.out_buf = torch.empty_like(g2.db.q)
+        g2 = setup(w2, torch).write_step_rows()
         db = g2.db
-        md2 = rpa.pa_build_metadata(db.query_lens, db.seq_lens, w2.num_tokens, db.block_tables, w2.block_size,
-                                    w2.num_blocks)
-        rpa.pa_write_kv(db.k, db.v, md2["slot_mapping"], g2.k_cache, g2.v_cache)
-        attn2 = lambda: rpa.pa_attention(db.q, g2.k_cache, g2.v_cache, db.block_tables, md2["query_start_loc"],
-                                         db.seq_lens, w2.max_query_len, w2.max_seq_len, w2.scale, out=g2.out_buf)
+        out2 = torch.empty_like(db.q)
+        qsl2 = g2.meta["query_start_loc"]
+        attn2 = lambda: rpa.pa_attention(db.q, g2.k_cache, g2.v_cache, db.block_tables, qsl2, db.seq_lens,
+                                         w2.max_query_len, w2.max_seq_len, w2.scale, out=out2)
         ms2 = timer.time(attn2, max(args.steps, 20), args.warmup)
+        kern2 = timer.kernels(rpa, attn2, 10)
         fl2 = accounting.attention_flops(w2.step.query_lens, w2.step.seq_lens, w2.num_q_heads, w2.head_dim)
         tf = fl2 / (ms2 / 1e3) / 1e12
-        result["prefill_mfma"] = {"workload": w2.name, "TFLOPs": tf, "frac_bf16_peak": tf / BF16_PEAK_TFLOPS,
-                                  "flops": fl2, "ms": ms2, "tokens": w2.num_tokens}
+        result["prefill_mfma"] = {
+            "workload": "ragged prefill: prompts 16/128/1024/2048 (T=3216), 32/32 heads, D 128, bs 16, bf16",
+            "TFLOPs": tf, "frac_bf16_peak": tf / BF16_PEAK_TFLOPS, "flops": fl2, "ms_per_call": ms2,
+            "kernels_ms": {k: round(avg, 5) for k, (n, avg) in kern2.items()},
+            "prefill_kernel_TFLOPs": fl2 / (kern2["prefill_kernel"][1] / 1e3) / 1e12}
+        if args.only == "prefill":
+            result["roofline"] = roofline_for("prefill_kernel", kern2["prefill_kernel"][1], w2, w2.name)
     print(json.dumps(result), flush=True)
 
 

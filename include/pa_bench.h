@@ -38,6 +38,27 @@ pa_status_t pa_bench_paged_read(const void* k_cache, const void* v_cache, const 
                                 int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
                                 int32_t max_seq_len, uint32_t* sink, void* stream);
 
+/*
+ * Per-kernel timing.  Between pa_bench_timing_begin() and
+ * pa_bench_timing_end(), every kernel the library launches (from any entry
+ * point, on any stream) is bracketed by two hipEvents recorded on the stream
+ * it is launched on.  pa_bench_timing_end() waits for those events and
+ * returns, per kernel name, the number of launches and their summed
+ * duration in milliseconds (entries sorted by descending total; at most
+ * max_entries are written, *n_entries receives the number written).  Events
+ * come from a pool owned by the library; not thread-safe.  Timing adds a few
+ * microseconds per launch: use it to split time among kernels, not for the
+ * headline clock.
+ */
+typedef struct {
+  char name[64];
+  int32_t launches;
+  double total_ms;
+} pa_kernel_time_t;
+
+pa_status_t pa_bench_timing_begin(void);
+pa_status_t pa_bench_timing_end(pa_kernel_time_t* out, int32_t max_entries, int32_t* n_entries);
+
 #ifdef __cplusplus
 }
 #endif

@@ -68,6 +68,14 @@ _lib.pa_bench_stream_read.restype = _i32
 _lib.pa_bench_stream_read.argtypes = [_p, _size, _p, _p]
 _lib.pa_bench_paged_read.restype = _i32
 _lib.pa_bench_paged_read.argtypes = [_p, _p, _p, _p] + [_i32] * 6 + [_p, _p]
+class KernelTime(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 64), ("launches", ctypes.c_int32), ("total_ms", ctypes.c_double)]
+
+
+_lib.pa_bench_timing_begin.restype = _i32
+_lib.pa_bench_timing_begin.argtypes = []
+_lib.pa_bench_timing_end.restype = _i32
+_lib.pa_bench_timing_end.argtypes = [ctypes.POINTER(KernelTime), _i32, ctypes.POINTER(_i32)]
 _lib.pa_attention.restype = _i32
 _lib.pa_attention.argtypes = [_p, _p, _p, _p, _p, _p] + [_i32] * 10 + [_f32, _i32, _p, _p, _size, _p, _p]
 
@@ -238,3 +246,15 @@ def pa_bench_paged_read(k_cache, v_cache, block_tables, seq_lens, max_seq_len: i
                                   int(seq_lens.shape[0]), Hkv, BS, NB, int(block_tables.shape[1]),
                                   int(max_seq_len), _ptr(sink), _stream(k_cache.device))
     _check(st, "pa_bench_paged_read")
+
+
+def pa_bench_timing_begin() -> None:
+    _check(_lib.pa_bench_timing_begin(), "pa_bench_timing_begin")
+
+
+def pa_bench_timing_end() -> dict:
+    """{kernel name: (launches, total ms)} for the launches since begin()."""
+    arr = (KernelTime * 32)()
+    n = _i32(0)
+    _check(_lib.pa_bench_timing_end(arr, 32, ctypes.byref(n)), "pa_bench_timing_end")
+    return {arr[i].name.decode(): (int(arr[i].launches), float(arr[i].total_ms)) for i in range(n.value)}

@@ -420,12 +420,15 @@ hipError_t launch_attn_fast(const AttnArgs& a, hipStream_t stream) {
   // prefill-class rows (query_len * G > 16): MFMA prefill kernel
   hipError_t e = launch_attn_prefill(a, kMaxRows, stream);
   if (e != hipSuccess) return e;
-  if (a.dtype == PA_BF16) {
-    decode_kernel<BF16><<<static_cast<uint32_t>(grid), 64, 0, stream>>>(d);
-    if (d.P > 1) merge_kernel<BF16><<<dim3(a.S, a.Hkv), 256, 0, stream>>>(d);
-  } else {
-    decode_kernel<F16><<<static_cast<uint32_t>(grid), 64, 0, stream>>>(d);
-    if (d.P > 1) merge_kernel<F16><<<dim3(a.S, a.Hkv), 256, 0, stream>>>(d);
+  launch_mark("decode_kernel", stream);
+  if (a.dtype == PA_BF16) decode_kernel<BF16><<<static_cast<uint32_t>(grid), 64, 0, stream>>>(d);
+  else decode_kernel<F16><<<static_cast<uint32_t>(grid), 64, 0, stream>>>(d);
+  launch_done(stream);
+  if (d.P > 1) {
+    launch_mark("merge_kernel", stream);
+    if (a.dtype == PA_BF16) merge_kernel<BF16><<<dim3(a.S, a.Hkv), 256, 0, stream>>>(d);
+    else merge_kernel<F16><<<dim3(a.S, a.Hkv), 256, 0, stream>>>(d);
+    launch_done(stream);
   }
   return hipGetLastError();
 }

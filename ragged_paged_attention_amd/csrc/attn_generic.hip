@@ -146,12 +146,14 @@ hipError_t launch_attn_generic_rows(const AttnArgs& a, int32_t skip_rows_le, hip
       static_cast<const F::T*>(a.q), static_cast<const F::T*>(a.k_cache),                          \
       static_cast<const F::T*>(a.v_cache), a.block_tables, a.qsl, a.seq_lens, a.S, a.Hq, a.Hkv,   \
       a.D, a.bs, a.NB, a.MB, a.scale, static_cast<F::T*>(a.out), a.d_err, skip_rows_le)
+  launch_mark("attn_generic_kernel", stream);
   switch (a.dtype) {
     case PA_F32: PA_GENERIC(F32); break;
     case PA_BF16: PA_GENERIC(BF16); break;
     case PA_F16: PA_GENERIC(F16); break;
     default: return hipErrorInvalidValue;
   }
+  launch_done(stream);
 #undef PA_GENERIC
   return hipGetLastError();
 }

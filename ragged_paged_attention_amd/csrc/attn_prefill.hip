@@ -328,8 +328,10 @@ hipError_t launch_attn_prefill(const AttnArgs& a, int32_t min_rows, hipStream_t 
   p.d_err = a.d_err;
   const int64_t items = static_cast<int64_t>(a.S) * p.n_qt * a.Hkv;
   if (items > INT32_MAX) return hipErrorInvalidValue;
+  launch_mark("prefill_kernel", stream);
   if (a.dtype == PA_BF16) prefill_kernel<BF16><<<static_cast<uint32_t>(items), 256, 0, stream>>>(p);
   else prefill_kernel<F16><<<static_cast<uint32_t>(items), 256, 0, stream>>>(p);
+  launch_done(stream);
   return hipGetLastError();
 }
 

@@ -166,12 +166,16 @@ hipError_t launch_metadata(const int32_t* query_lens, const int32_t* seq_lens, i
                            const int32_t* block_tables, int32_t MB, int32_t bs, int32_t NB,
                            int32_t* qsl, int32_t* ssl, int32_t* positions, int32_t* token_to_seq,
                            int32_t* slot_mapping, int32_t* stats, int32_t* d_err, hipStream_t stream) {
+  launch_mark("meta_scan_kernel", stream);
   meta_scan_kernel<<<1, kScanThreads, 0, stream>>>(query_lens, seq_lens, S, T, qsl, ssl, stats, d_err);
+  launch_done(stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 0) return e;
   const int grid = S < 2048 ? S : 2048;
+  launch_mark("meta_fill_kernel", stream);
   meta_fill_kernel<<<grid, 256, 0, stream>>>(query_lens, seq_lens, S, T, qsl, block_tables, MB, bs, NB,
                                              positions, token_to_seq, slot_mapping, d_err);
+  launch_done(stream);
   return hipGetLastError();
 }
 

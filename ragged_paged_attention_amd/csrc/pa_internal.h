@@ -9,6 +9,12 @@
 
 namespace pa {
 
+// Optional per-kernel timing (pa_bench.h).  launch_mark(name, stream) records
+// an event before a launch and launch_done(stream) one after it; both are a
+// single branch when timing is off.
+void launch_mark(const char* name, hipStream_t stream);
+void launch_done(hipStream_t stream);
+
 // metadata.hip
 hipError_t launch_metadata(const int32_t* query_lens, const int32_t* seq_lens, int32_t S, int32_t T,
                            const int32_t* block_tables, int32_t MB, int32_t bs, int32_t NB,

@@ -67,12 +67,14 @@ hipError_t launch_write_kv(const void* k, const void* v, const int32_t* slot_map
   const char* vc = static_cast<const char*>(v);
   char* kd = static_cast<char*>(k_cache);
   char* vd = static_cast<char*>(v_cache);
+  launch_mark("write_kv_kernel", stream);
   switch (vec) {
     case 16: write_kv_kernel<16><<<grid, 256, 0, stream>>>(kc, vc, slot_mapping, T, row_bytes, kd, vd, num_slots, d_err); break;
     case 8: write_kv_kernel<8><<<grid, 256, 0, stream>>>(kc, vc, slot_mapping, T, row_bytes, kd, vd, num_slots, d_err); break;
     case 4: write_kv_kernel<4><<<grid, 256, 0, stream>>>(kc, vc, slot_mapping, T, row_bytes, kd, vd, num_slots, d_err); break;
     default: write_kv_kernel<2><<<grid, 256, 0, stream>>>(kc, vc, slot_mapping, T, row_bytes, kd, vd, num_slots, d_err); break;
   }
+  launch_done(stream);
   return hipGetLastError();
 }
 

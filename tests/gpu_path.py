@@ -36,6 +36,16 @@ class GpuRun:
                             d_err=self.d_err)
         return self
 
+    def write_step_rows(self):
+        """Metadata and KV write of the step's new rows, no attention (for
+        timing attention alone)."""
+        w, db = self.w, self.db
+        self.meta = rpa.pa_build_metadata(db.query_lens, db.seq_lens, w.num_tokens, db.block_tables, w.block_size,
+                                          w.num_blocks, d_err=self.d_err)
+        rpa.pa_write_kv(db.k, db.v, self.meta["slot_mapping"], self.k_cache, self.v_cache, d_err=self.d_err)
+        torch.cuda.synchronize()
+        return self
+
     def step(self, workspace=None):
         w, db = self.w, self.db
         self.out, self.meta = forward_step(db.q, db.k, db.v, self.k_cache, self.v_cache, db.query_lens,
