@@ -1,0 +1,146 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration
+bench.py times, plus edge cases.
+
+Full sizes: metadata compared in full (bit-exact), the pool compared in full
+(bit-exact, NaN poison included) for the decode and shared-prefix batches,
+attention compared on sampled rows the oracle computes one by one (first and
+last rows, query-tile and KV-tile boundaries, the longest sequences, random
+rows) to the dtype's tolerance.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import ragged_paged_attention_amd as rpa
+from tests.gpu_path import GpuRun, max_abs_err, tol_for
+from workloads import Batch, Workload, config, random_batch
+from workloads.device import to_numpy_bits
+from workloads.generators import _pad_tables
+
+pytestmark = pytest.mark.gpu
+
+
+def _sample_rows(w, n_random=12, seed=0):
+    rng = np.random.default_rng(seed)
+    offs = w.new_row_offsets()
+    rows = {0, w.num_tokens - 1}
+    ql, sl = w.step.query_lens, w.step.seq_lens
+    for s in np.argsort(-sl)[:4]:                        # longest contexts
+        rows.add(int(offs[s + 1]) - 1)
+    for s in range(w.num_seqs):                           # tile boundaries inside long chunks
+        q = int(ql[s])
+        for i in (31, 32, 127, 128, 255, 256, q - 2):
+            if 0 <= i < q:
+                rows.add(int(offs[s]) + i)
+    rows |= set(int(x) for x in rng.choice(w.num_tokens, size=min(n_random, w.num_tokens), replace=False))
+    rows = sorted(rows)
+    if len(rows) > 48:
+        rows = sorted(rng.choice(rows, size=48, replace=False).tolist())
+    return rows
+
+
+def _bits(a):
+    a = np.asarray(a)
+    return a.view(np.uint32) if a.dtype == np.float32 else a.view(np.uint16)
+
+
+@pytest.mark.parametrize("n", [2, 3, 4, 5])
+def test_full_size_config(n):
+    w = config(n)
+    print(f"[full] config {n} {w.summary()}", flush=True)
+    rows = _sample_rows(w)
+    g = GpuRun(w).run()
+    torch.cuda.synchronize()
+    md, kc, vc, ref = oracle.run_step(w, rows=rows)
+    assert g.err() == 0
+    for name in ("query_start_loc", "seq_start_loc", "positions", "token_to_seq", "slot_mapping", "stats"):
+        assert np.array_equal(g.meta[name].cpu().numpy(), getattr(md, name)), name
+    if n in (3, 5):
+        assert np.array_equal(_bits(to_numpy_bits(g.k_cache)), _bits(kc)), "k_cache differs"
+        assert np.array_equal(_bits(to_numpy_bits(g.v_cache)), _bits(vc)), "v_cache differs"
+    got = g.out[torch.tensor(rows, device="cuda")]
+    err = max_abs_err(got, ref)
+    print(f"[full] config {n}: {len(rows)} sampled rows, max_abs_err={err:.3e}", flush=True)
+    assert err <= tol_for(w.dtype)
+    assert torch.isfinite(g.out).all()
+
+
+def test_empty_batch_is_a_no_op():
+    w = config(1)
+    g = GpuRun(w).run()
+    out = torch.full_like(g.db.q, 7.0)
+    qsl = torch.zeros(1, dtype=torch.int32, device="cuda")
+    sl = torch.zeros(0, dtype=torch.int32, device="cuda")
+    st = rpa.library().pa_attention(g.db.q.data_ptr(), g.k_cache.data_ptr(), g.v_cache.data_ptr(),
+                                    g.db.block_tables.data_ptr(), qsl.data_ptr(), sl.data_ptr(), 0, 0,
+                                    w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size, w.num_blocks,
+                                    w.max_blocks_per_seq, 1, 1, 0.25, 0, out.data_ptr(), None, 0, None, None)
+    torch.cuda.synchronize()
+    assert st == 0 and bool((out == 7.0).all())
+
+
+def _explicit(dtype, Hq, Hkv, D, bs, NB, q_lens, s_lens, tables, seed, hist_tables=None):
+    """A workload with given lengths: history for every sequence, random values."""
+    from workloads.generators import build_workload
+    return build_workload("explicit", dtype, Hq, Hkv, D, bs, NB, q_lens, s_lens, tables, seed)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_zero_length_queries_mixed_in(dtype):
+    """Sequences with query_len 0 own no rows and must not disturb others."""
+    rng = np.random.default_rng(3)
+    ql = [0, 3, 0, 1, 0, 40, 1, 0]
+    sl = [5, 9, 0, 30, 17, 77, 1, 16]
+    bs = 16
+    counts = [-(-L // bs) for L in sl]
+    ids = rng.permutation(64)
+    tables, o = [], 0
+    for c in counts:
+        tables.append([int(x) for x in ids[o:o + c]])
+        o += c
+    w = _explicit(dtype, 8, 2, 128, bs, 64, ql, sl, tables, 5)
+    g = GpuRun(w).run()
+    _, _, _, ref = oracle.run_step(w)
+    assert g.err() == 0
+    assert max_abs_err(g.out, ref) <= tol_for(dtype)
+
+
+def test_small_max_query_len_hint_still_correct():
+    """The hints shape the launch only: a too-small max_query_len is slower,
+    not wrong."""
+    w = config(2, scale_down=4)
+    g = GpuRun(w).fill_history().write_step_rows()
+    out = rpa.pa_attention(g.db.q, g.k_cache, g.v_cache, g.db.block_tables, g.meta["query_start_loc"],
+                           g.db.seq_lens, 17, 3, w.scale)
+    torch.cuda.synchronize()
+    _, _, _, ref = oracle.run_step(w)
+    assert max_abs_err(out, ref) <= tol_for(w.dtype)
+
+
+def test_very_long_decode_context_beyond_part_cap():
+    """A 60,001-token context needs more than 64 parts of 768 tokens: parts
+    get longer instead, and the result stays exact."""
+    L = 60001
+    bs = 16
+    nb = -(-L // bs)
+    rng = np.random.default_rng(9)
+    tables = [[int(x) for x in rng.permutation(nb + 8)[:nb]]]
+    w = _explicit("bf16", 4, 1, 128, bs, nb + 8, [1], [L], tables, 11)
+    g = GpuRun(w).run()
+    _, _, _, ref = oracle.run_step(w)
+    assert g.err() == 0
+    assert max_abs_err(g.out, ref) <= tol_for("bf16")
+
+
+@pytest.mark.parametrize("shape", [dict(Hq=64, Hkv=1, D=128, bs=16),   # G = 64 > 16: generic path
+                                   dict(Hq=4, Hkv=2, D=256, bs=8),     # head_dim 256
+                                   dict(Hq=8, Hkv=8, D=128, bs=64)],   # large blocks on the fast path
+                         ids=["G64", "D256", "bs64"])
+def test_other_shapes(shape):
+    w = random_batch(77, S=5, Hq=shape["Hq"], Hkv=shape["Hkv"], D=shape["D"], bs=shape["bs"], dtype="bf16",
+                     max_ctx=300, max_q=70)
+    g = GpuRun(w).run()
+    _, _, _, ref = oracle.run_step(w)
+    assert g.err() == 0
+    assert max_abs_err(g.out, ref) <= tol_for("bf16")
