@@ -257,8 +257,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void
     }
     float mx = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
                      fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
-    mx = xor_max(mx, 16);
-    mx = xor_max(mx, 32);
+    mx = group_max4(mx);
     const float m_new = fmaxf(m, mx);
     float p[2][4];
     float alpha = 1.f;
@@ -294,8 +293,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void
     __asm__ volatile("" ::: "memory");
   }
 
-  lsum = xor_sum(lsum, 16);
-  lsum = xor_sum(lsum, 32);
+  lsum = group_sum4(lsum);
   if (np == 1) {
     if (rvalid) {
       const float inv = lsum > 0.f ? 1.f / lsum : 0.f;

@@ -40,6 +40,7 @@ constexpr int kRowBytes = 256;                     // one token row of one head 
 constexpr int kTileBytes = kTile * kRowBytes;      // 16 KB per K or V tile
 constexpr int kStageBytes = 2 * kTileBytes;        // K tile then V tile
 constexpr float kRescaleSlack = 8.f;               // log2 units the running max may lag
+constexpr int kQtRun = 4;                          // query tiles of one (sequence, head) per XCD run
 
 struct PrefillArgs {
   const uint16_t* q;
@@ -72,11 +73,23 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   const int lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, grp = lane >> 4;
 
-  const int32_t item = blockIdx.x;
-  const int32_t g = item % a.Hkv;
-  const int32_t tmp = item / a.Hkv;
+  // Items: (block of kQtRun query tiles, heaviest block first; sequence; KV
+  // head; tile in block, heaviest first).  Workgroup b runs on XCD b % 8, and
+  // runs of kQtRun consecutive items are kept on one XCD, so the query tiles
+  // of one (sequence, head) that share every K/V tile read them through the
+  // same L2 at about the same time.
+  const int32_t bid = blockIdx.x;
+  const int32_t xcd = bid & 7, jj = bid >> 3;
+  const int32_t item = ((jj / kQtRun) * 8 + xcd) * kQtRun + (jj % kQtRun);
+  const int32_t n_qb = (a.n_qt + kQtRun - 1) / kQtRun;
+  if (item >= n_qb * kQtRun * a.S * a.Hkv) return;
+  const int32_t qi = item % kQtRun;
+  const int32_t tmp0 = item / kQtRun;
+  const int32_t g = tmp0 % a.Hkv;
+  const int32_t tmp = tmp0 / a.Hkv;
   const int32_t s = tmp % a.S;
-  const int32_t qt_first = a.n_qt - 1 - tmp / a.S;  // heaviest (last) query tiles first
+  const int32_t qt_first = (n_qb - 1 - tmp / a.S) * kQtRun + (kQtRun - 1 - qi);
+  if (qt_first >= a.n_qt) return;
 
   const int32_t q0 = a.qsl[s];
   const int32_t qlen = a.qsl[s + 1] - q0;
@@ -236,9 +249,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
                            fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
           mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(x[2][0], x[2][1]), fmaxf(x[2][2], x[2][3])),
                                fmaxf(fmaxf(x[3][0], x[3][1]), fmaxf(x[3][2], x[3][3]))));
-          mx = xor_max(mx, 16);
-          mx = xor_max(mx, 32);
-          mx *= a.scale_log2e;
+          mx = group_max4(mx) * a.scale_log2e;
           alpha[nt] = 1.f;
           if (mx > m[nt] + kRescaleSlack) {
             alpha[nt] = __builtin_amdgcn_exp2f(m[nt] - mx);  // 0 on the first visible tile
@@ -326,7 +337,9 @@ hipError_t launch_attn_prefill(const AttnArgs& a, int32_t min_rows, hipStream_t 
   p.scale_log2e = a.scale * 1.4426950408889634f;
   p.out = static_cast<uint16_t*>(a.out);
   p.d_err = a.d_err;
-  const int64_t items = static_cast<int64_t>(a.S) * p.n_qt * a.Hkv;
+  const int64_t n_qb = (p.n_qt + kQtRun - 1) / kQtRun;
+  const int64_t items_raw = n_qb * kQtRun * a.S * a.Hkv;
+  const int64_t items = (items_raw + 8 * kQtRun - 1) / (8 * kQtRun) * (8 * kQtRun);
   if (items > INT32_MAX) return hipErrorInvalidValue;
   launch_mark("prefill_kernel", stream);
   if (a.dtype == PA_BF16) prefill_kernel<BF16><<<static_cast<uint32_t>(items), 256, 0, stream>>>(p);

@@ -76,6 +76,27 @@ __device__ __forceinline__ uint4 ld16_nt(const uint16_t* p) {
 __device__ __forceinline__ float xor_max(float v, int m) { return fmaxf(v, __shfl_xor(v, m, 64)); }
 __device__ __forceinline__ float xor_sum(float v, int m) { return v + __shfl_xor(v, m, 64); }
 
+// Combine the four 16-lane groups (lanes l, l^16, l^32, l^48) with gfx950's
+// VALU lane swaps instead of LDS-based shuffles.  With both operands equal to
+// x, v_permlane32_swap leaves x[l] and x[l ^ 32] in the two results, and
+// v_permlane16_swap x[l] and x[l ^ 16] (lane layout checked on the GPU).
+__device__ __forceinline__ float group_max4(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const float m32 = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t w = __float_as_uint(m32);
+  const auto b = __builtin_amdgcn_permlane16_swap(w, w, false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float group_sum4(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const float s32 = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const uint32_t w = __float_as_uint(s32);
+  const auto b = __builtin_amdgcn_permlane16_swap(w, w, false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Transposed LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane L
 // supplies the address of 4 consecutive 16-bit elements; lanes 4j..4j+3
 // together supply row j (16 elements) of a 4x16 tile, and lane i receives
