@@ -180,10 +180,19 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void
   // as the current V is in LDS.  A pair's second chunk may lie past the part
   // (odd chunk counts): it is then neither loaded nor counted.
   uint4 kf[2][4], vf[2][4];
-  // Sequence-fastest order streams K/V past the caches (read once: 6.0 vs
-  // 5.6 TB/s measured); in head-grouped order neighbouring sequences may share
-  // prefix blocks, so those loads stay cacheable for the L2 hits.
-  const bool stream = !a.grouped;
+  // K/V read once are streamed past the caches (6.0 vs 5.6 TB/s measured on
+  // the decode batch).  A part whose first block is also mapped by a
+  // neighbouring sequence (a shared prefix) keeps cacheable loads, so the
+  // sequences sharing it hit in L2.
+  bool stream = true;
+  if (a.grouped) {
+    const int32_t lb0 = c0 / cpb;
+    const int32_t mine = btrow[lb0];
+    bool shared = false;
+    if (s > 0) shared |= a.block_tables[static_cast<int64_t>(s - 1) * a.MB + lb0] == mine;
+    if (s + 1 < a.S) shared |= a.block_tables[static_cast<int64_t>(s + 1) * a.MB + lb0] == mine;
+    stream = !shared;
+  }
   auto load_pair = [&](int32_t c, bool do_k, bool do_v) {
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
