@@ -32,9 +32,14 @@
 namespace pa {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kRowsPerWave = 32;
-constexpr int kRowsPerWG = kWaves * kRowsPerWave;  // 128
+#ifndef PA_PREFILL_ROWS_PER_WAVE
+#define PA_PREFILL_ROWS_PER_WAVE 32
+#endif
+constexpr int kRowsPerWG = 128;                         // query rows per workgroup
+constexpr int kRowsPerWave = PA_PREFILL_ROWS_PER_WAVE;  // 16 or 32
+constexpr int kNt = kRowsPerWave / 16;                  // 16-row MFMA tiles per wave
+constexpr int kWaves = kRowsPerWG / kRowsPerWave;
+constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 64;                          // KV tokens per tile
 constexpr int kRowBytes = 256;                     // one token row of one head (128 x 16 bit)
 constexpr int kTileBytes = kTile * kRowBytes;      // 16 KB per K or V tile
@@ -65,7 +70,7 @@ __device__ __forceinline__ int k_slot(int row, int chunk) { return row * kRowByt
 __device__ __forceinline__ int v_slot(int row, int chunk) { return row * kRowBytes + ((chunk ^ ((row & 7) << 1)) << 4); }
 
 template <class F>
-__global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 2, kWaves / 2))) void prefill_kernel(PrefillArgs a) {
   using M = Mma<F>;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kStageBytes];  // 64 KB, two stages
 
@@ -100,7 +105,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   if (L < qlen || ceil_div(L, a.bs) > a.MB) {
     if (tid == 0) flag(a.d_err, L < qlen ? PA_DERR_QLEN_GT_SEQLEN : PA_DERR_BLOCK_OOB);
     for (int64_t idx = tid + static_cast<int64_t>(qt_first) * kRowsPerWG * kD;
-         idx < static_cast<int64_t>(rows_total) * kD; idx += 256) {
+         idx < static_cast<int64_t>(rows_total) * kD; idx += kThreads) {
       if ((idx / kD) / kRowsPerWG % a.n_qt != qt_first) continue;  // another item's rows
       const int32_t rho = static_cast<int32_t>(idx / kD);
       const int32_t i = rho / a.G, hg = rho - (rho / a.G) * a.G;
@@ -118,8 +123,11 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   // block id) of the K and V tiles, 4 rows per instruction, lane -> 16 bytes.
   // Rows at or past the context end re-read the last valid row, so nothing
   // unwritten (possibly NaN) ever reaches LDS; such rows are masked anyway.
+  constexpr int kDmaRows = kTile / kWaves;  // tile rows each wave fills
+  constexpr int kDmaInst = kDmaRows / 4;     // 4 rows per DMA instruction
+  const int row_base = kDmaRows * wave;      // within one 16-token group
   auto issue_tile = [&](int32_t kt, int stage) {
-    const int32_t t16 = kt * kTile + 16 * wave;
+    const int32_t t16 = kt * kTile + (row_base & ~15);
     const int32_t lb = (t16 < L ? t16 : L - 1) / a.bs;
     int32_t b = btrow[lb];
     if (b < 0 || b >= a.NB) {
@@ -127,14 +135,14 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
       b = 0;
     }
     const int64_t slot0 = static_cast<int64_t>(b) * a.bs + (t16 < L ? t16 - lb * a.bs : 0);
-    uint8_t* kdst = lds + stage * kStageBytes + (16 * wave) * kRowBytes;
+    uint8_t* kdst = lds + stage * kStageBytes + row_base * kRowBytes;
     uint8_t* vdst = kdst + kTileBytes;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int row = 16 * wave + 4 * u + grp;  // tile row this lane fills
+    for (int u = 0; u < kDmaInst; ++u) {
+      const int row = row_base + 4 * u + grp;  // tile row this lane fills
       const int32_t tok = kt * kTile + row;
       int64_t slot;
-      if (tok < L) slot = slot0 + 4 * u + grp;
+      if (tok < L) slot = slot0 + (row & 15);
       else {  // past the end: last valid token of the sequence
         const int32_t lb2 = (L - 1) / a.bs;
         int32_t b2 = btrow[lb2];
@@ -162,10 +170,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     issue_tile(0, 0);
 
     // this wave's rows and their Q^T fragments
-    int32_t qpos[2];
-    uint4 qf[2][4];
+    int32_t qpos[kNt];
+    uint4 qf[kNt][4];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
+    for (int nt = 0; nt < kNt; ++nt) {
       const int32_t rho = row0 + wave * kRowsPerWave + nt * 16 + r;
       const bool valid = rho < rows_total;
       const int32_t i = rho / a.G, hg = rho - (rho / a.G) * a.G;
@@ -182,10 +190,11 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     // exceeds it by more than kRescaleSlack, so p = 2^(x - m) stays <= 2^8 and
     // the O rescale is rare; numerator and denominator always share the same
     // m, so the result is unchanged.
-    float m[2] = {-INFINITY, -INFINITY};
-    f32x4_t o[2][8], osum[2];
+    float m[kNt];
+    f32x4_t o[kNt][8], osum[kNt];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
+    for (int nt = 0; nt < kNt; ++nt) {
+      m[nt] = -INFINITY;
       osum[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) o[nt][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -210,9 +219,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
       const uint8_t* vt_lds = kt_lds + kTileBytes;
       if (wave_active) {
         // S^T[16 mt + 4grp + j][row r of nt]; 8 independent MFMAs per K column block
-        f32x4_t st[2][4];
+        f32x4_t st[kNt][4];
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
+        for (int nt = 0; nt < kNt; ++nt)
 #pragma unroll
           for (int mt = 0; mt < 4; ++mt) st[nt][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -224,14 +233,14 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
           for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) st[nt][mt] = M::qk(ka[mt], qf[nt][kk], st[nt][mt]);
+            for (int nt = 0; nt < kNt; ++nt) st[nt][mt] = M::qk(ka[mt], qf[nt][kk], st[nt][mt]);
         }
 
         const bool need_mask = kt * kTile + kTile - 1 > qpos_min_wave;
-        uint4 pb[2][2];
-        float alpha[2];
+        uint4 pb[kNt][2];
+        float alpha[kNt];
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
+        for (int nt = 0; nt < kNt; ++nt) {
           float x[4][4];
 #pragma unroll
           for (int mt = 0; mt < 4; ++mt)
@@ -267,9 +276,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
                                    M::pk(p[2 * u + 1][0], p[2 * u + 1][1]),
                                    M::pk(p[2 * u + 1][2], p[2 * u + 1][3]));
         }
-        if (__any(alpha[0] != 1.f || alpha[1] != 1.f)) {  // wave-uniform, rare after the first tiles
+        if (__any(kNt == 1 ? alpha[0] != 1.f : (alpha[0] != 1.f || alpha[kNt - 1] != 1.f))) {  // wave-uniform, rare after the first tiles
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt) {
+          for (int nt = 0; nt < kNt; ++nt) {
             osum[nt] *= alpha[nt];
 #pragma unroll
             for (int dt = 0; dt < 8; ++dt) o[nt][dt] *= alpha[nt];
@@ -281,14 +290,14 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt) osum[nt] = M::qk(ones, pb[nt][u], osum[nt]);
+          for (int nt = 0; nt < kNt; ++nt) osum[nt] = M::qk(ones, pb[nt][u], osum[nt]);
 #pragma unroll
           for (int dt = 0; dt < 8; ++dt) {
             const i16x4_t lo = lds_read_tr16(vt_lds + voff[dt] + (32 * u) * kRowBytes);
             const i16x4_t hi = lds_read_tr16(vt_lds + voff[dt] + (32 * u + 16) * kRowBytes);
             const uint4 va = __builtin_bit_cast(uint4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) o[nt][dt] = M::qk(va, pb[nt][u], o[nt][dt]);
+            for (int nt = 0; nt < kNt; ++nt) o[nt][dt] = M::qk(va, pb[nt][u], o[nt][dt]);
           }
         }
       }
@@ -298,7 +307,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     if (!wave_active) continue;
 
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
+    for (int nt = 0; nt < kNt; ++nt) {
       const int32_t rho = wave_row0 + nt * 16 + r;
       if (rho >= rows_total) continue;
       const int32_t i = rho / a.G, hg = rho - (rho / a.G) * a.G;
@@ -342,8 +351,8 @@ hipError_t launch_attn_prefill(const AttnArgs& a, int32_t min_rows, hipStream_t 
   const int64_t items = (items_raw + 8 * kQtRun - 1) / (8 * kQtRun) * (8 * kQtRun);
   if (items > INT32_MAX) return hipErrorInvalidValue;
   launch_mark("prefill_kernel", stream);
-  if (a.dtype == PA_BF16) prefill_kernel<BF16><<<static_cast<uint32_t>(items), 256, 0, stream>>>(p);
-  else prefill_kernel<F16><<<static_cast<uint32_t>(items), 256, 0, stream>>>(p);
+  if (a.dtype == PA_BF16) prefill_kernel<BF16><<<static_cast<uint32_t>(items), kThreads, 0, stream>>>(p);
+  else prefill_kernel<F16><<<static_cast<uint32_t>(items), kThreads, 0, stream>>>(p);
   launch_done(stream);
   return hipGetLastError();
 }
