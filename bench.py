@@ -15,8 +15,9 @@ inputs resident in HBM before timing.  value = T / step time (tokens/s).
 Also reported (same run): the decode batch's KV-read bandwidth (100 x
 2001-token contexts, 32/32 heads) against HBM peak and against measured read
 ceilings, the ragged prefill batch's TFLOP/s (16/128/1024/2048-token prompts),
-the shared-prefix long-context decode batch, and the oracle's CPU throughput
-on a sample of the step's rows.  Prints ONE JSON line on stdout.
+the shared-prefix long-context decode batch, block copies for copy-on-write
+(device to device) and swap (device to pinned host and back), and the
+oracle's CPU throughput on a sample of the step's rows.  Prints ONE JSON line on stdout.
 """
 from __future__ import annotations
 
@@ -40,6 +41,7 @@ KERNEL_SOURCES = {
     "merge_kernel": "ragged_paged_attention_amd/csrc/attn_fast.hip",
     "prefill_kernel": "ragged_paged_attention_amd/csrc/attn_prefill.hip",
     "write_kv_kernel": "ragged_paged_attention_amd/csrc/write_kv.hip",
+    "copy_blocks_kernel": "ragged_paged_attention_amd/csrc/copy_blocks.hip",
 }
 
 
@@ -49,7 +51,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["step", "decode", "prefill", "shared"], default=None,
+    ap.add_argument("--only", choices=["step", "decode", "prefill", "shared", "blocks"], default=None,
                     help="run one leg only (for profiling)")
     ap.add_argument("--cpu-sample-rows", type=int, default=2048)
     ap.add_argument("--summarize-trace", nargs=2, metavar=("ROCPROF_DIR", "OUT_MD"),
@@ -413,7 +415,47 @@ def main():
             "prefill_kernel_TFLOPs": fl2 / (kern2["prefill_kernel"][1] / 1e3) / 1e12}
         if args.only == "prefill":
             result["roofline"] = roofline_for("prefill_kernel", kern2["prefill_kernel"][1], w2, w2.name)
+
+    # ---------------- block copies: copy-on-write and swap ----------------
+    if args.only in (None, "blocks"):
+        result["block_copies"] = bench_block_copies(torch, rpa, timer, args)
     print(json.dumps(result), flush=True)
+
+
+def bench_block_copies(torch, rpa, timer, args):
+    """pa_copy_blocks on the mixed batch's pool geometry (block_size 16, 8 KV
+    heads, head_dim 128, bf16: 32 KiB per block of K or V): 4096 copy-on-write
+    pairs inside one device pool, then 1024 blocks swapped out to a pinned
+    host pool and back in.  Bytes = read + write of K and V per pair."""
+    import numpy as np
+    bs, hkv, d = 16, 8, 128
+    nb, n_cow, n_swap = 9216, 4096, 1024
+    kc = torch.zeros((nb, bs, hkv, d), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    block_bytes = bs * hkv * d * 2
+    rng = np.random.default_rng(7)
+    perm = rng.permutation(nb).astype(np.int32)
+    cow = torch.from_numpy(np.stack([perm[:n_cow], perm[n_cow:2 * n_cow]], 1).copy()).cuda()
+    ms = timer.time(lambda: rpa.pa_copy_blocks(kc, vc, kc, vc, cow), max(args.steps, 20), args.warmup)
+    kern = timer.kernels(rpa, lambda: rpa.pa_copy_blocks(kc, vc, kc, vc, cow), 10)
+    cow_bytes = n_cow * 2 * 2 * block_bytes
+    hk = torch.empty((n_swap, bs, hkv, d), dtype=torch.bfloat16, pin_memory=True)
+    hv = torch.empty_like(hk, pin_memory=True)
+    out_pairs = torch.from_numpy(np.stack([perm[:n_swap], np.arange(n_swap, dtype=np.int32)], 1).copy()).cuda()
+    in_pairs = torch.from_numpy(np.stack([np.arange(n_swap, dtype=np.int32), perm[n_cow:n_cow + n_swap]], 1)
+                                .copy()).cuda()
+    ms_out = timer.time(lambda: rpa.pa_copy_blocks(kc, vc, hk, hv, out_pairs), 5, 2)
+    ms_in = timer.time(lambda: rpa.pa_copy_blocks(hk, hv, kc, vc, in_pairs), 5, 2)
+    swap_bytes = n_swap * 2 * block_bytes
+    res = {"workload": f"{n_cow} copy-on-write pairs in a {nb}-block pool + {n_swap}-block swap out/in, "
+                       "bs 16, 8 KV heads, D 128, bf16",
+           "cow_ms": ms, "cow_GBps": cow_bytes / (ms / 1e3) / 1e9,
+           "cow_kernel_GBps": cow_bytes / (kern["copy_blocks_kernel"][1] / 1e3) / 1e9,
+           "cow_frac_hbm_peak": cow_bytes / (kern["copy_blocks_kernel"][1] / 1e3) / 1e9 / HBM_PEAK_GBS,
+           "swap_out_GBps": swap_bytes / (ms_out / 1e3) / 1e9, "swap_in_GBps": swap_bytes / (ms_in / 1e3) / 1e9}
+    del kc, vc, hk, hv
+    torch.cuda.empty_cache()
+    return res
 
 
 if __name__ == "__main__":

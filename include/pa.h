@@ -145,6 +145,31 @@ pa_status_t pa_write_kv(const void* k, const void* v, const int32_t* slot_mappin
                         void* stream);
 
 /*
+ * pa_copy_blocks — copy whole KV blocks by (source, destination) pairs.
+ *
+ * The device half of copy-on-write ([VP] §2.1: before a block shared by
+ * several sequences (ref_count > 1) is written, the writer gets a fresh block
+ * holding a copy, and its table is repointed) and of swapping ([CB] §4.4:
+ * blocks move to CPU memory under memory pressure and back later).
+ *
+ *   src_k, src_v  [src_num_blocks, block_size, Hkv, D] source pool (K and V)
+ *   dst_k, dst_v  [dst_num_blocks, block_size, Hkv, D] destination pool; may
+ *                 be the same pool as the source (copy-on-write)
+ *   pairs         [num_pairs, 2] int32 (source block, destination block),
+ *                 device-accessible memory
+ *   block_bytes   bytes of one block of one of K/V (block_size*Hkv*D*esize),
+ *                 a multiple of 16
+ * Any pool may live in device memory or in pinned host memory the device can
+ * access (for swap-out / swap-in).  A pure copy of bits.  Pairs with a block
+ * id out of range are skipped and flag PA_DERR_BLOCK_OOB.  A destination
+ * written twice, or a block that is both a destination and a source of the
+ * same call, is invalid input (order unspecified).
+ */
+pa_status_t pa_copy_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
+                           int32_t src_num_blocks, int32_t dst_num_blocks, const int32_t* pairs,
+                           int32_t num_pairs, int64_t block_bytes, int32_t* d_err, void* stream);
+
+/*
  * Bytes of device workspace pa_attention needs for these sizes (split-K
  * partial results and the work list).  Depends only on its arguments.
  */

@@ -198,6 +198,28 @@ def write_kv(k_new: np.ndarray, v_new: np.ndarray, slot_mapping: np.ndarray,
 
 
 # ---------------------------------------------------------------------------
+# block copies ([VP] §2.1 copy-on-write; [CB] §4.4 swap)
+# ---------------------------------------------------------------------------
+def copy_blocks(src_k: np.ndarray, src_v: np.ndarray, dst_k: np.ndarray, dst_v: np.ndarray, pairs) -> None:
+    """In place: for each (source, destination) pair, the destination block of
+    both pools receives the source block's K and V, bit for bit.  A
+    destination written twice, or used as a source too, is invalid."""
+    pairs = [(int(a), int(b)) for a, b in np.asarray(pairs).reshape(-1, 2)]
+    dsts = [d for _, d in pairs]
+    if len(set(dsts)) != len(dsts):
+        raise OracleInputError("a destination block appears twice")
+    if src_k is dst_k and set(dsts) & {s for s, _ in pairs}:
+        raise OracleInputError("a block is both a source and a destination")
+    for s_, d_ in pairs:
+        if not (0 <= s_ < src_k.shape[0]) or not (0 <= d_ < dst_k.shape[0]):
+            raise OracleInputError("block id out of range")
+    staged = [(d_, src_k[s_].copy(), src_v[s_].copy()) for s_, d_ in pairs]
+    for d_, kb, vb in staged:
+        dst_k[d_] = kb
+        dst_v[d_] = vb
+
+
+# ---------------------------------------------------------------------------
 # attention ([FS] §2.3 and §2.3补充 第二步; [VP] §1.1 and §3.7)
 # ---------------------------------------------------------------------------
 def gather_sequence(cache: np.ndarray, block_table_row: np.ndarray, seq_len: int, dtype: str) -> np.ndarray:

@@ -62,6 +62,8 @@ _lib.pa_build_metadata.restype = _i32
 _lib.pa_build_metadata.argtypes = [_p, _p, _i32, _i32, _p, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p]
 _lib.pa_write_kv.restype = _i32
 _lib.pa_write_kv.argtypes = [_p, _p, _p, _i32, _i32, _i32, _p, _p, _i32, _i32, _i32, _p, _p]
+_lib.pa_copy_blocks.restype = _i32
+_lib.pa_copy_blocks.argtypes = [_p, _p, _p, _p, _i32, _i32, _p, _i32, ctypes.c_int64, _p, _p]
 _lib.pa_attention_workspace_size.restype = _size
 _lib.pa_attention_workspace_size.argtypes = [_i32] * 6
 _lib.pa_bench_stream_read.restype = _i32
@@ -196,6 +198,27 @@ def pa_write_kv(k, v, slot_mapping, k_cache, v_cache, d_err=None) -> None:
     st = _lib.pa_write_kv(_ptr(k), _ptr(v), _ptr(slot_mapping), T, Hkv, D, _ptr(k_cache), _ptr(v_cache),
                           NB, BS, _dtype_code(k.dtype), _ptr(d_err), _stream(k.device))
     _check(st, "pa_write_kv")
+
+
+def pa_copy_blocks(src_k, src_v, dst_k, dst_v, pairs, d_err=None, stream_device=None) -> None:
+    """Calls pa_copy_blocks.  Pools [NB, BS, Hkv, D] (device or pinned host),
+    pairs [n, 2] int32 (source block, destination block), device-accessible."""
+    torch = _torch()
+    for t, n in ((src_k, "src_k"), (src_v, "src_v"), (dst_k, "dst_k"), (dst_v, "dst_v")):
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
+        if not (t.is_cuda or t.is_pinned()):
+            raise ValueError(f"{n} must be device memory or pinned host memory")
+    if pairs.dtype != torch.int32 or not pairs.is_contiguous() or (not pairs.is_cuda and not pairs.is_pinned()):
+        raise ValueError("pairs must be a contiguous int32 device (or pinned) tensor")
+    if src_k.shape[1:] != dst_k.shape[1:] or src_k.dtype != dst_k.dtype:
+        raise ValueError("source and destination blocks differ in shape or dtype")
+    block_bytes = src_k[0].numel() * src_k.element_size()
+    dev = next((t.device for t in (src_k, dst_k, pairs) if t.is_cuda), torch.device("cuda"))
+    st = _lib.pa_copy_blocks(_ptr(src_k), _ptr(src_v), _ptr(dst_k), _ptr(dst_v), int(src_k.shape[0]),
+                             int(dst_k.shape[0]), _ptr(pairs), int(pairs.shape[0]), int(block_bytes), _ptr(d_err),
+                             _stream(dev))
+    _check(st, "pa_copy_blocks")
 
 
 def pa_attention_workspace_size(num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim, max_seq_len) -> int:

@@ -98,6 +98,23 @@ pa_status_t pa_write_kv(const void* k, const void* v, const int32_t* slot_mappin
   return hip_status(e, "pa_write_kv");
 }
 
+pa_status_t pa_copy_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
+                           int32_t src_num_blocks, int32_t dst_num_blocks, const int32_t* pairs,
+                           int32_t num_pairs, int64_t block_bytes, int32_t* d_err, void* stream) {
+  if (num_pairs < 0 || src_num_blocks < 1 || dst_num_blocks < 1 || block_bytes < 16 || block_bytes % 16)
+    return PA_ERR_SHAPE;
+  if (num_pairs == 0) return PA_OK;
+  if (num_pairs > (INT32_MAX >> 1)) return PA_ERR_SHAPE;
+  if (!src_k || !src_v || !dst_k || !dst_v || !pairs) return PA_ERR_NULL;
+  const uintptr_t align = reinterpret_cast<uintptr_t>(src_k) | reinterpret_cast<uintptr_t>(src_v) |
+                          reinterpret_cast<uintptr_t>(dst_k) | reinterpret_cast<uintptr_t>(dst_v);
+  if (align % 16) return PA_ERR_SHAPE;
+  clear_stale_error();
+  hipError_t e = pa::launch_copy_blocks(src_k, src_v, dst_k, dst_v, src_num_blocks, dst_num_blocks, pairs,
+                                        num_pairs, block_bytes, d_err, static_cast<hipStream_t>(stream));
+  return hip_status(e, "pa_copy_blocks");
+}
+
 size_t pa_attention_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
                                    int32_t num_kv_heads, int32_t head_dim, int32_t max_seq_len) {
   if (num_seqs < 0 || num_tokens < 0 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1)

@@ -26,6 +26,11 @@ hipError_t launch_write_kv(const void* k, const void* v, const int32_t* slot_map
                            int64_t row_bytes, void* k_cache, void* v_cache, int64_t num_slots,
                            int32_t* d_err, hipStream_t stream);
 
+// copy_blocks.hip
+hipError_t launch_copy_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_v, int32_t src_nb,
+                              int32_t dst_nb, const int32_t* pairs, int32_t num_pairs, int64_t block_bytes,
+                              int32_t* d_err, hipStream_t stream);
+
 // Shape of one pa_attention call, as the kernels see it.
 struct AttnArgs {
   const void* q;

@@ -54,6 +54,14 @@ def test_host_side_rejections_need_no_gpu():
     assert att() == 1                     # null pointers
     assert att(max_q=0) == 2              # size hints must be >= 1
     assert lib.pa_attention_workspace_size(4, 100, 32, 32, 128, 2001) >= 0
+    cp = lambda nsrc=4, ndst=4, n=1, bb=8192, ptr=16: lib.pa_copy_blocks(ptr, ptr, ptr, ptr, nsrc, ndst, ptr, n, bb,
+                                                                          NULL, NULL)
+    assert cp(bb=8200) == 2               # block bytes not a multiple of 16
+    assert cp(nsrc=0) == 2
+    assert cp(n=-1) == 2
+    assert cp(ptr=8) == 2                 # pools not 16-byte aligned
+    assert cp(ptr=None) == 1
+    assert cp(n=0, ptr=None) == 0         # nothing to copy
 
 
 def _attn_args(T=3, Hq=4, Hkv=2, D=16, max_q=2, S=2):

@@ -176,8 +176,57 @@ def pin_closed_form_equal_keys():
                                            rtol=0, atol=1e-13)
 
 
+def _sdpa_rows(q, k, v, scale):
+    """Attention of query rows q [n, Hq, D] over all of k/v [L, Hkv, D] (no
+    mask) via torch SDPA in float64, GQA by repeating KV heads."""
+    G = q.shape[1] // k.shape[1]
+    Q = torch.from_numpy(q).permute(1, 0, 2)[None]
+    K = torch.from_numpy(k).permute(1, 0, 2).repeat_interleave(G, dim=0)[None]
+    V = torch.from_numpy(v).permute(1, 0, 2).repeat_interleave(G, dim=0)[None]
+    return torch.nn.functional.scaled_dot_product_attention(Q, K, V, scale=scale)[0].permute(1, 0, 2).numpy()
+
+
+def pin_copy_on_write():
+    """The parallel-sampling walk-through of the vLLM principles page (§2.1):
+    A1 and A2 share physical blocks 7 and 1 holding a 7-token prompt; A1's
+    first write into shared block 1 copies it to block 3 and repoints A1's
+    table; A2 then writes into block 1 in place.  Each branch must then see
+    the prompt plus its own new token and nothing of the other's."""
+    g = _golden("copy_on_write")["parallel_sampling_cow"]
+    bs, n = g["block_size_implied"], g["prompt_tokens"]
+    assert -(-n // bs) == g["logical_blocks"] and n - (g["logical_blocks"] - 1) * bs == g["tokens_in_last_block"]
+    rng = np.random.default_rng(61)
+    Hq, Hkv, D, NB = 4, 2, 8, 8
+    kc = PA.empty_pool((NB, bs, Hkv, D), "f32", np.nan)
+    vc = PA.empty_pool((NB, bs, Hkv, D), "f32", np.nan)
+    pk = rng.standard_normal((n, Hkv, D)).astype(np.float32)
+    pv = rng.standard_normal((n, Hkv, D)).astype(np.float32)
+    shared = np.array([g["shared_physical_blocks"]], np.int32)
+    md = PA.build_metadata([n], [n], n, shared, bs, NB)
+    PA.write_kv(pk, pv, md.slot_mapping, kc, vc)
+    # A1 writes first: copy-on-write of the shared last block
+    PA.copy_blocks(kc, vc, kc, vc, [[g["cow_source_block"], g["cow_new_block"]]])
+    tables = np.array([g["a1_table_after"], g["a2_table_after"]], np.int32)
+    nk = rng.standard_normal((2, Hkv, D)).astype(np.float32)   # "fathers" (A1), "mothers" (A2)
+    nv = rng.standard_normal((2, Hkv, D)).astype(np.float32)
+    q = rng.standard_normal((2, Hq, D)).astype(np.float32)
+    md = PA.build_metadata([1, 1], [n + 1, n + 1], 2, tables, bs, NB)
+    assert md.positions.tolist() == [g["new_token_position"]] * 2
+    PA.write_kv(nk, nv, md.slot_mapping, kc, vc)
+    out = PA.attention(q, kc, vc, tables, md.query_start_loc, np.array([n + 1, n + 1]), Hkv, 0.5, "f32")
+    for b, (kk, vv) in enumerate(zip(nk, nv)):
+        k_log = np.concatenate([pk, kk[None]]).astype(np.float64)
+        v_log = np.concatenate([pv, vv[None]]).astype(np.float64)
+        np.testing.assert_allclose(out[b], _sdpa_rows(q[b:b + 1].astype(np.float64), k_log, v_log, 0.5)[0],
+                                   rtol=0, atol=1e-12)
+    # the source block still holds the prompt tail plus A2's row only
+    np.testing.assert_array_equal(kc[g["cow_source_block"], :n - bs], pk[bs:])
+    np.testing.assert_array_equal(kc[g["cow_source_block"], n - bs], nk[1])
+    np.testing.assert_array_equal(vc[g["cow_new_block"], n - bs], nv[0])
+
+
 ALL_PINS = [pin_offsets, pin_forward_shape, pin_brute_force, pin_single_key,
-            pin_closed_form_equal_keys] + [(lambda c=c: pin_dense(c)) for c in DENSE_CASES]
+            pin_closed_form_equal_keys, pin_copy_on_write] + [(lambda c=c: pin_dense(c)) for c in DENSE_CASES]
 
 
 # ---------------------------------------------------------------------------
@@ -198,6 +247,29 @@ def test_oracle_equals_dense_padded_masked(case):
 
 def test_oracle_equals_brute_force():
     pin_brute_force()
+
+
+def test_copy_on_write_walkthrough():
+    pin_copy_on_write()
+
+
+def test_copy_blocks_semantics():
+    """Whole blocks move bit for bit between pools (swap out to a host pool
+    and back in at other ids), both K and V, and nothing else changes."""
+    rng = np.random.default_rng(62)
+    kc = rng.integers(0, 2**16, (6, 4, 2, 8), dtype=np.uint16)
+    vc = rng.integers(0, 2**16, (6, 4, 2, 8), dtype=np.uint16)
+    k0, v0 = kc.copy(), vc.copy()
+    hk = np.zeros((3, 4, 2, 8), np.uint16)
+    hv = np.zeros((3, 4, 2, 8), np.uint16)
+    PA.copy_blocks(kc, vc, hk, hv, [[4, 0], [1, 2]])          # swap out
+    assert (hk[0] == k0[4]).all() and (hv[2] == v0[1]).all() and (hk[1] == 0).all()
+    PA.copy_blocks(hk, hv, kc, vc, [[0, 5], [2, 0]])          # swap in elsewhere
+    assert (kc[5] == k0[4]).all() and (vc[5] == v0[4]).all() and (kc[0] == k0[1]).all() and (vc[0] == v0[1]).all()
+    assert (kc[1:5] == k0[1:5]).all() and (vc[1:5] == v0[1:5]).all()
+    for bad in ([[0, 1], [2, 1]], [[0, 1], [1, 2]], [[6, 0]], [[0, -1]]):
+        with pytest.raises(oracle.OracleInputError):
+            PA.copy_blocks(kc, vc, kc, vc, bad)
 
 
 def test_single_key_identity():
@@ -450,7 +522,13 @@ def _bad_softmax(scores, values):
     return (w @ values) / (w.sum(axis=-1, keepdims=True) + 1e-3)
 
 
+def _bad_copy_blocks(src_k, src_v, dst_k, dst_v, pairs):
+    for a, b in np.asarray(pairs).reshape(-1, 2):
+        dst_k[int(b)] = src_k[int(a)]     # V left behind
+
+
 MUTANTS = {
+    "copy_blocks_drops_v": ("copy_blocks", _bad_copy_blocks),
     "position_off_by_one": ("position_of", _bad_position),
     "gqa_head_mapping_transposed": ("kv_head_of", _bad_kv_head),
     "slot_block_offset_swapped": ("slot_of", _bad_slot),
