@@ -15,7 +15,9 @@ inputs resident in HBM before timing.  value = T / step time (tokens/s).
 Also reported (same run): the decode batch's KV-read bandwidth (100 x
 2001-token contexts, 32/32 heads) against HBM peak and against measured read
 ceilings, the ragged prefill batch's TFLOP/s (16/128/1024/2048-token prompts),
-the shared-prefix long-context decode batch, block copies for copy-on-write
+the shared-prefix long-context decode batch, the speculative-decoding verify
+batch (64 sequences, query_len 2..8 over 2k..16k-token contexts, 32/8 heads)
+as KV-read bandwidth, block copies for copy-on-write
 (device to device) and swap (device to pinned host and back), and the
 oracle's CPU throughput on a sample of the step's rows.  Prints ONE JSON line on stdout.
 """
@@ -38,6 +40,7 @@ METRIC = "decode KV-read GB/s (% HBM peak) + mixed-batch attn tokens/s, 1 MI355X
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
     "decode_kernel": "ragged_paged_attention_amd/csrc/attn_fast.hip",
+    "decode_kernel_2t": "ragged_paged_attention_amd/csrc/attn_fast.hip",
     "merge_kernel": "ragged_paged_attention_amd/csrc/attn_fast.hip",
     "prefill_kernel": "ragged_paged_attention_amd/csrc/attn_prefill.hip",
     "write_kv_kernel": "ragged_paged_attention_amd/csrc/write_kv.hip",
@@ -51,7 +54,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["step", "decode", "prefill", "shared", "blocks"], default=None,
+    ap.add_argument("--only", choices=["step", "decode", "prefill", "shared", "verify", "blocks"], default=None,
                     help="run one leg only (for profiling)")
     ap.add_argument("--cpu-sample-rows", type=int, default=2048)
     ap.add_argument("--summarize-trace", nargs=2, metavar=("ROCPROF_DIR", "OUT_MD"),
@@ -110,7 +113,7 @@ def setup(w, torch):
 
 def workspace_for(w, rpa, torch):
     need = rpa.pa_attention_workspace_size(w.num_seqs, w.num_tokens, w.num_q_heads, w.num_kv_heads, w.head_dim,
-                                           w.max_seq_len)
+                                           w.max_query_len, w.max_seq_len)
     return torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
 
 
@@ -160,28 +163,37 @@ def cpu_baseline(w, rows_wanted, seed=0):
 
 
 def work_split(w):
-    """Algorithmic work of the step's two attention kernels: KV/Q/O bytes of
-    the decode-class sequences (query_len * G <= 16) and causal FLOPs of the
-    prefill-class ones."""
+    """Algorithmic work of each attention kernel of a call: KV/Q/O bytes of
+    the sequences each decode kernel takes (query_len * G rows per KV head:
+    up to 16 on one tile, 17..32 on two when the max_query_len hint allows
+    them) and causal FLOPs of the prefill-class rest."""
     import numpy as np
     from workloads import accounting
     G = w.num_q_heads // w.num_kv_heads
     ql, sl = w.step.query_lens.astype(np.int64), w.step.seq_lens.astype(np.int64)
-    dec = ql * G <= 16
+    cap = 32 if max(1, w.max_query_len) * G > 16 else 16
+    rows = ql * G
     es = accounting.itemsize(w.dtype)
-    dec_bytes = (accounting.kv_read_bytes(sl[dec], w.num_kv_heads, w.head_dim, w.dtype)
-                 + 2 * int(ql[dec].sum()) * w.num_q_heads * w.head_dim * es)
-    pre_flops = accounting.attention_flops(ql[~dec], sl[~dec], w.num_q_heads, w.head_dim)
-    return dec_bytes, pre_flops
+
+    def dec_bytes(sel):
+        return (accounting.kv_read_bytes(sl[sel], w.num_kv_heads, w.head_dim, w.dtype)
+                + 2 * int(ql[sel].sum()) * w.num_q_heads * w.head_dim * es)
+
+    return {"decode_kernel": dec_bytes(rows <= 16),
+            "decode_kernel_2t": dec_bytes((rows > 16) & (rows <= cap)),
+            "prefill_kernel": accounting.attention_flops(ql[rows > cap], sl[rows > cap], w.num_q_heads,
+                                                         w.head_dim)}
 
 
 def roofline_for(kernel, avg_ms, w, workload_tag):
-    dec_bytes, pre_flops = work_split(w)
+    work = work_split(w)
     if kernel == "prefill_kernel":
+        pre_flops = work[kernel]
         a = pre_flops / (avg_ms / 1e3) / 1e12
         return {"bound": "mfma", "kernel": kernel, "achieved": a, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": a / BF16_PEAK_TFLOPS, "traffic": traffic_from_profiles(kernel, workload_tag),
                 "work_per_launch": pre_flops, "avg_launch_ms": avg_ms}
+    dec_bytes = work[kernel]
     a = dec_bytes / (avg_ms / 1e3) / 1e9
     return {"bound": "hbm", "kernel": kernel, "achieved": a, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": a / HBM_PEAK_GBS, "traffic": traffic_from_profiles(kernel, workload_tag),
@@ -289,7 +301,7 @@ def main():
 
     import ragged_paged_attention_amd as rpa
     from ragged_paged_attention_amd.step import forward_step
-    from workloads import accounting, config
+    from workloads import accounting, config, verify_batch
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     timer = Timer(torch)
@@ -320,7 +332,7 @@ def main():
         ms = timer.time(step, args.steps, args.warmup)
         kern = timer.kernels(rpa, step, args.steps)
         ql = w.step.query_lens
-        dec_bytes, pre_flops = work_split(w)
+        split = work_split(w)
         result.update({
             "value": w.num_tokens / (ms / 1e3), "ms_per_step": ms, "dtype": w.dtype,
             "config": {"workload": "chunked-prefill mixed batch", "seqs": w.num_seqs, "tokens": w.num_tokens,
@@ -329,7 +341,7 @@ def main():
                        "heads_q_kv": [w.num_q_heads, w.num_kv_heads], "head_dim": w.head_dim,
                        "block_size": w.block_size, "pool_blocks": w.num_blocks, "seed": w.seed},
             "kernels_ms_per_step": {k: round(n * avg / args.steps, 5) for k, (n, avg) in kern.items()},
-            "step_work": {"decode_bytes": dec_bytes, "prefill_flops": pre_flops},
+            "step_work": {"decode_bytes": split["decode_kernel"], "prefill_flops": split["prefill_kernel"]},
         })
         weight = lambda k: kern.get(k, (0, 0.0))[0] * kern.get(k, (0, 0.0))[1]
         dominant = max(("decode_kernel", "prefill_kernel"), key=weight)
@@ -393,6 +405,38 @@ def main():
             "ms_per_call": ms5, "logical_GBps": kv5 / (ms5 / 1e3) / 1e9, "unique_GBps": uq5 / (ms5 / 1e3) / 1e9,
             "logical_bytes": kv5, "unique_bytes": uq5}
         del g5, ws5, out5
+        torch.cuda.empty_cache()
+
+    # ---------------- speculative-decoding verify batch ----------------
+    if args.only in (None, "verify"):
+        t0 = time.time()
+        w6 = verify_batch(poison=False)
+        print(f"[bench] verify batch {w6.summary()} generated in {time.time() - t0:.1f}s", file=sys.stderr,
+              flush=True)
+        g6 = setup(w6, torch).write_step_rows()
+        db = g6.db
+        ws6 = workspace_for(w6, rpa, torch)
+        out6 = torch.empty_like(db.q)
+        qsl6 = g6.meta["query_start_loc"]
+        attn6 = lambda: rpa.pa_attention(db.q, g6.k_cache, g6.v_cache, db.block_tables, qsl6, db.seq_lens,
+                                         w6.max_query_len, w6.max_seq_len, w6.scale, out=out6, workspace=ws6)
+        ms6 = timer.time(attn6, max(args.steps, 20), args.warmup)
+        kern6 = timer.kernels(rpa, attn6, 10)
+        kv6 = accounting.kv_read_bytes(w6.step.seq_lens, w6.num_kv_heads, w6.head_dim, w6.dtype)
+        result["verify_kv_read"] = {
+            "workload": "verify batch: 64 seqs, query_len 2..8 over log-uniform 2k..16k contexts, 32/8 heads, "
+                        "D 128, bs 16, bf16",
+            "tokens": w6.num_tokens, "ms_per_call": ms6, "GBps": kv6 / (ms6 / 1e3) / 1e9,
+            "frac_hbm_peak": kv6 / (ms6 / 1e3) / 1e9 / HBM_PEAK_GBS, "kv_bytes": kv6,
+            "tokens_per_s": w6.num_tokens / (ms6 / 1e3),
+            "kernels_ms": {k: round(avg, 5) for k, (n, avg) in kern6.items()}}
+        split6 = work_split(w6)
+        for kname in ("decode_kernel", "decode_kernel_2t"):
+            if kname in kern6:
+                result["verify_kv_read"][kname + "_GBps"] = split6[kname] / (kern6[kname][1] / 1e3) / 1e9
+        if args.only == "verify":
+            result["roofline"] = roofline_for("decode_kernel_2t", kern6["decode_kernel_2t"][1], w6, w6.name)
+        del g6, ws6, out6
         torch.cuda.empty_cache()
 
     # ---------------- ragged prefill batch: MFMA throughput ----------------

@@ -61,7 +61,8 @@ enum {
   PA_DERR_BLOCK_OOB = 4,       /* a block-table entry a sequence needs is < 0 or >= num_blocks,
                                   or the table is too narrow for seq_len */
   PA_DERR_SLOT_OOB = 8,        /* a slot_mapping entry >= num_blocks * block_size */
-  PA_DERR_OVERFLOW = 16        /* a prefix sum exceeds INT32_MAX */
+  PA_DERR_OVERFLOW = 16,       /* a prefix sum exceeds INT32_MAX */
+  PA_DERR_HINT = 32            /* pa_attention: a query_len exceeds the max_query_len hint */
 };
 
 /* Human-readable name of a status code (static storage). */
@@ -170,11 +171,13 @@ pa_status_t pa_copy_blocks(const void* src_k, const void* src_v, void* dst_k, vo
                            int32_t num_pairs, int64_t block_bytes, int32_t* d_err, void* stream);
 
 /*
- * Bytes of device workspace pa_attention needs for these sizes (split-K
- * partial results and the work list).  Depends only on its arguments.
+ * Bytes of device workspace pa_attention needs for these sizes and hints
+ * (split-K partial results).  Depends only on its arguments; pass the same
+ * max_query_len and max_seq_len as to pa_attention.
  */
 size_t pa_attention_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
-                                   int32_t num_kv_heads, int32_t head_dim, int32_t max_seq_len);
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t max_query_len,
+                                   int32_t max_seq_len);
 
 /*
  * pa_attention — ragged causal paged attention over the cache.
@@ -196,17 +199,22 @@ size_t pa_attention_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t
  *        ceil(seq_len / block_size) entries of a row are read
  *   query_start_loc [S+1], seq_lens [S]
  *   max_query_len, max_seq_len: host-side size hints used to shape the
- *        launch (like max_seqlen_q / max_seqlen_k in [VP] §3.7).  Results do
- *        not depend on them being tight; they must be >= 1 when T > 0.
+ *        launch (like max_seqlen_q / max_seqlen_k in [VP] §3.7); >= 1 when
+ *        T > 0.  Results do not depend on them being tight.  max_query_len
+ *        must bound every query_len: a longer one flags PA_DERR_HINT and
+ *        that sequence's rows are unspecified (computed or zero).  A
+ *        sequence longer than max_seq_len is computed correctly (its split
+ *        parts just get longer).
  *   scale  softmax scale (1/sqrt(head_dim) in the usual model)
  *   out  [T, num_q_heads, head_dim], `dtype`
  *   workspace: device memory of at least pa_attention_workspace_size() bytes;
  *        contents on entry are irrelevant, on exit unspecified.
  * Arithmetic is fp32 (inputs widened, products and sums in fp32), output
  * rounded to `dtype` (nearest-even).  Supported: num_q_heads % num_kv_heads
- * == 0, 1 <= head_dim <= 256, block_size >= 1.  bf16/fp16 with head_dim 128
- * and block_size a multiple of 16 take the MFMA fast paths; everything else
- * takes a generic fp32 kernel.
+ * == 0, 1 <= head_dim <= 256, block_size >= 1.  bf16/fp16 with head_dim 128,
+ * block_size a multiple of 16, num_q_heads / num_kv_heads <= 16 and q, the
+ * caches, out and workspace 16-byte aligned take the MFMA fast paths;
+ * everything else takes a generic fp32 kernel.
  * The caches are never written.  Rows of sequences whose metadata is invalid
  * are written as zeros and flag PA_DERR_*.
  */

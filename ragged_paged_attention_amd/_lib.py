@@ -20,6 +20,7 @@ HEADERS = [HEADER, os.path.join(os.path.dirname(PKG), "include", "pa_bench.h")]
 PA_F32, PA_BF16, PA_F16 = 0, 1, 2
 PA_POLICY_AUTO, PA_POLICY_GENERIC, PA_POLICY_FAST = 0, 1, 2
 PA_DERR_QLEN_GT_SEQLEN, PA_DERR_TOKEN_SUM, PA_DERR_BLOCK_OOB, PA_DERR_SLOT_OOB, PA_DERR_OVERFLOW = 1, 2, 4, 8, 16
+PA_DERR_HINT = 32
 
 
 class PAError(RuntimeError):
@@ -65,7 +66,7 @@ _lib.pa_write_kv.argtypes = [_p, _p, _p, _i32, _i32, _i32, _p, _p, _i32, _i32, _
 _lib.pa_copy_blocks.restype = _i32
 _lib.pa_copy_blocks.argtypes = [_p, _p, _p, _p, _i32, _i32, _p, _i32, ctypes.c_int64, _p, _p]
 _lib.pa_attention_workspace_size.restype = _size
-_lib.pa_attention_workspace_size.argtypes = [_i32] * 6
+_lib.pa_attention_workspace_size.argtypes = [_i32] * 7
 _lib.pa_bench_stream_read.restype = _i32
 _lib.pa_bench_stream_read.argtypes = [_p, _size, _p, _p]
 _lib.pa_bench_paged_read.restype = _i32
@@ -221,9 +222,11 @@ def pa_copy_blocks(src_k, src_v, dst_k, dst_v, pairs, d_err=None, stream_device=
     _check(st, "pa_copy_blocks")
 
 
-def pa_attention_workspace_size(num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim, max_seq_len) -> int:
+def pa_attention_workspace_size(num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim, max_query_len,
+                                max_seq_len) -> int:
     return int(_lib.pa_attention_workspace_size(int(num_seqs), int(num_tokens), int(num_q_heads),
-                                                int(num_kv_heads), int(head_dim), int(max_seq_len)))
+                                                int(num_kv_heads), int(head_dim), int(max_query_len),
+                                                int(max_seq_len)))
 
 
 def pa_attention(q, k_cache, v_cache, block_tables, query_start_loc, seq_lens, max_query_len: int,
@@ -241,7 +244,7 @@ def pa_attention(q, k_cache, v_cache, block_tables, query_start_loc, seq_lens, m
     S = int(seq_lens.shape[0])
     if out is None:
         out = torch.empty_like(q)
-    need = pa_attention_workspace_size(S, T, Hq, Hkv, D, max_seq_len)
+    need = pa_attention_workspace_size(S, T, Hq, Hkv, D, max_query_len, max_seq_len)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

@@ -8,11 +8,13 @@
 // "LLM 推理引擎 Continuous Batching 与 PagedAttention" §3.3, and split-K parts
 // combined by the same rescaling.
 //
-// Decode kernel (sequences with query_len * G <= 16, G = Hq / Hkv)
+// Decode kernel (sequences with query_len * G <= 32, G = Hq / Hkv)
 // -----------------------------------------------------------------
 // Work item = (sequence s, KV head g, part of the context).  One wave64 per
-// item.  All G query heads of the group (times query_len rows) form the 16
-// columns of one MFMA tile, so every K/V byte is read once per (s, g):
+// item.  All G query heads of the group (times query_len rows) form the
+// columns of one or two 16-column MFMA tiles (NT = 1 for up to 16 rows, NT = 2
+// for 17..32: a verify step of a few draft tokens), so every K/V byte is read
+// once per (s, g) whatever the row count:
 //   S^T[16 tok][16 rows] = K[16 tok][128] . Q^T[128][16 rows]
 //       4 x v_mfma_f32_16x16x32 (A = K rows straight from HBM, 16 B per lane)
 //   O^T[128][16 rows]   += V^T[128][16 tok] . P^T[16 tok][16 rows]
@@ -35,7 +37,8 @@ namespace pa {
 namespace {
 
 constexpr int kPartFloats = 132;    // per partial row: O[128], m, l, pad
-constexpr int kMaxRows = 16;        // query rows of one decode item
+constexpr int kTileRows = 16;       // query rows per MFMA column tile
+constexpr int kMaxRows = 32;        // query rows of one decode item (two tiles)
 // Compile-time tuning of the decode work split (measured on MI355X).
 constexpr int kPartChunks = 48;     // a context part is at most 48 chunks = 768 tokens
 constexpr int kMaxParts = 64;       // parts per sequence (longer parts past 48k tokens)
@@ -64,28 +67,39 @@ struct DecodeArgs {
   const int32_t* qsl;
   const int32_t* seq_lens;
   int32_t S, Hq, Hkv, G, NB, MB, bs, P, n_items, grouped;
+  int32_t rows_cap;    // 16 or 32: larger items go to the prefill kernel
+  int32_t prefill_on;  // the prefill kernel runs in this call
+  int32_t max_q;       // the caller's max_query_len hint
   float scale_log2e;
   uint16_t* out;
   float* ws;
   int32_t* d_err;
 };
 
-template <class F>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void decode_kernel(DecodeArgs a) {
+// NT = row tiles: the instance with NT tiles takes items with
+// 16 (NT - 1) < rows <= 16 NT.  The one-tile instance also checks the
+// max_query_len hint and zero-fills the rows of items no kernel of this call
+// covers (rows above rows_cap while the prefill kernel does not run).
+template <class F, int NT>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 3 : 2, 8))) void decode_kernel(
+    DecodeArgs a) {
   using M = Mma<F>;
   __shared__ __attribute__((aligned(16))) uint8_t vlds[2 * kChunk * kVRowBytes];
   const int lane = threadIdx.x;
-  const int r = lane & 15;    // MFMA column = query row of the item
+  const int r = lane & 15;    // MFMA column = query row of the item (within its tile)
   const int grp = lane >> 4;  // 16-lane group
 
   // XCD-aware mapping: workgroup b runs on XCD b % 8.  Items go out in runs of
-  // kXcdRun consecutive items per XCD, the runs rotating over the 8 XCDs: every
-  // XCD gets an even share of every part index (balance), and a run of
-  // neighbouring items lives on one XCD's L2.  The grid is a multiple of
-  // 8 * kXcdRun.
+  // kXcdRun consecutive items per XCD (a run of neighbouring items lives on
+  // one XCD's L2).  The k-th run an XCD takes is run 8k + ((xcd + k) mod 8):
+  // the XCD of a run moves on every block of 8 runs, so no stride in the item
+  // order (a layer of S x Hkv items, say, when S is a multiple of 128) can pin
+  // a sequence or a head to one XCD and leave the XCDs' loads uneven.  The
+  // grid is a multiple of 8 * kXcdRun.
   const int32_t bid = blockIdx.x;
   const int32_t xcd = bid & 7, j = bid >> 3;
-  const int32_t item = ((j / kXcdRun) * 8 + xcd) * kXcdRun + (j % kXcdRun);
+  const int32_t k = j / kXcdRun;
+  const int32_t item = (k * 8 + ((xcd + k) & 7)) * kXcdRun + (j % kXcdRun);
   if (item >= a.n_items) return;
   // item = (part, sequence, KV head), head fastest: the Hkv waves reading the
   // same token rows (all heads of a slot are one contiguous row of the cache)
@@ -117,21 +131,42 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void
 
   const int32_t q0 = a.qsl[s];
   const int32_t qlen = a.qsl[s + 1] - q0;
-  if (qlen <= 0 || qlen * a.G > kMaxRows) return;  // nothing here, or a prefill item
-  const int32_t L = a.seq_lens[s];
+  if (qlen <= 0) return;
   const int32_t rows = qlen * a.G;
-  const int32_t i_row = r / a.G;
-  const int32_t hg = r - i_row * a.G;
-  const bool rvalid = r < rows;
-  const int32_t t = q0 + i_row;
-  const int32_t h = g * a.G + hg;
-  uint16_t* orow = a.out + (static_cast<int64_t>(t) * a.Hq + h) * kD;
+  if (NT == 1 && part == 0) {
+    if (qlen > a.max_q && g == 0 && lane == 0) flag(a.d_err, PA_DERR_HINT);
+    if (rows > a.rows_cap && !a.prefill_on) {  // not covered by this call: zeros
+      for (int32_t idx = lane; idx < rows * (kD / 4); idx += 64) {
+        const int32_t rr = idx / (kD / 4), d4 = idx - rr * (kD / 4);
+        const int32_t tt = q0 + rr / a.G, hh = g * a.G + rr % a.G;
+        *reinterpret_cast<uint2*>(a.out + (static_cast<int64_t>(tt) * a.Hq + hh) * kD + 4 * d4) = make_uint2(0, 0);
+      }
+      return;
+    }
+  }
+  if (rows <= kTileRows * (NT - 1) || rows > kTileRows * NT || rows > a.rows_cap) return;  // another kernel's
+  const int32_t L = a.seq_lens[s];
+  // per tile: this lane's query row, its flat row and head, its output row
+  int32_t rt_row[NT], qpos[NT];
+  bool rvalid[NT];
+  uint16_t* orow[NT];
+#pragma unroll
+  for (int rt = 0; rt < NT; ++rt) {
+    rt_row[rt] = kTileRows * rt + r;
+    const int32_t i_row = rt_row[rt] / a.G;
+    const int32_t hg = rt_row[rt] - i_row * a.G;
+    rvalid[rt] = rt_row[rt] < rows;
+    orow[rt] = a.out + (static_cast<int64_t>(q0 + i_row) * a.Hq + g * a.G + hg) * kD;
+    qpos[rt] = rvalid[rt] ? L - qlen + i_row : -1;  // last visible position of this row
+  }
 
   if (L < qlen || ceil_div(L, a.bs) > a.MB) {
     if (part == 0) {
       if (lane == 0) flag(a.d_err, L < qlen ? PA_DERR_QLEN_GT_SEQLEN : PA_DERR_BLOCK_OOB);
-      if (rvalid)
-        for (int d = 4 * grp; d < kD; d += 16) *reinterpret_cast<uint2*>(orow + d) = make_uint2(0, 0);
+#pragma unroll
+      for (int rt = 0; rt < NT; ++rt)
+        if (rvalid[rt])
+          for (int d = 4 * grp; d < kD; d += 16) *reinterpret_cast<uint2*>(orow[rt] + d) = make_uint2(0, 0);
     }
     return;
   }
@@ -142,12 +177,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void
   const int32_t c0 = part * cpp;
   const int32_t c1 = min(nchunks, c0 + cpp);
 
-  // Q^T fragments (B operand): lane holds Q[row r][32kk + 8grp .. +8]
-  uint4 qf[4];
-  const uint16_t* qrow = a.q + (static_cast<int64_t>(t) * a.Hq + h) * kD + 8 * grp;
+  // Q^T fragments (B operand): lane holds Q[row][32kk + 8grp .. +8] of its
+  // row in each tile (the q row sits at the same offset as the output row)
+  uint4 qf[NT][4];
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) qf[kk] = rvalid ? ld16(qrow + 32 * kk) : make_uint4(0, 0, 0, 0);
-  const int32_t qpos = rvalid ? L - qlen + i_row : -1;  // last visible position of this row
+  for (int rt = 0; rt < NT; ++rt) {
+    const uint16_t* qrow = a.q + (orow[rt] - a.out) + 8 * grp;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) qf[rt][kk] = rvalid[rt] ? ld16(qrow + 32 * kk) : make_uint4(0, 0, 0, 0);
+  }
 
   const int64_t slot_stride = static_cast<int64_t>(a.Hkv) * kD;  // elements between slots
   const uint16_t* kbase = a.k_cache + static_cast<int64_t>(g) * kD;
@@ -185,7 +223,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void
   // neighbouring sequence (a shared prefix) keeps cacheable loads, so the
   // sequences sharing it hit in L2.
   bool stream = true;
-  if (a.grouped) {
+  {
     const int32_t lb0 = c0 / cpb;
     const int32_t mine = btrow[lb0];
     bool shared = false;
@@ -219,10 +257,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void
     }
   };
 
-  float m = -INFINITY, lsum = 0.f;
-  f32x4_t o[8];
+  float m[NT], lsum[NT];
+  f32x4_t o[NT][8];
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int rt = 0; rt < NT; ++rt) {
+    m[rt] = -INFINITY;
+    lsum[rt] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) o[rt][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
 
   load_pair(c0, true, true);
   const int rd_off = (4 * grp + (r >> 2)) * kVRowBytes + 8 * (r & 3);
@@ -230,12 +273,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void
     const int32_t tok0 = c * kChunk;
     const bool more = c + 2 < c1;
 
-    // scores: S^T[tok0 + 16 h2 + 4grp + j][row r]
-    f32x4_t st[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    // scores: S^T[tok0 + 16 h2 + 4grp + j][row r of tile rt]
+    f32x4_t st[NT][2];
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt) st[rt][0] = st[rt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) st[h2] = M::qk(kf[h2][kk], qf[kk], st[h2]);
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int rt = 0; rt < NT; ++rt) st[rt][h2] = M::qk(kf[h2][kk], qf[rt][kk], st[rt][h2]);
     if (more) load_pair(c + 2, true, false);
 
     // stage V; rows past the context or the part are zeroed (unwritten slots
@@ -256,118 +303,162 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void
     __asm__ volatile("" ::: "memory");
     if (more) load_pair(c + 2, false, true);
 
-    float x[2][4];
+    uint4 pb[NT];
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      const int32_t tb = tok0 + 16 * h2 + 4 * grp;
+    for (int rt = 0; rt < NT; ++rt) {
+      float x[2][4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        x[h2][j] = (tb + j <= qpos && tb + j < tok_end) ? st[h2][j] * a.scale_log2e : -INFINITY;
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int32_t tb = tok0 + 16 * h2 + 4 * grp;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          x[h2][j] = (tb + j <= qpos[rt] && tb + j < tok_end) ? st[rt][h2][j] * a.scale_log2e : -INFINITY;
+      }
+      float mx = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
+                       fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
+      mx = group_max4(mx);
+      const float m_new = fmaxf(m[rt], mx);
+      float p[2][4];
+      float alpha = 1.f;
+      if (m_new == -INFINITY) {
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) p[h2][j] = 0.f;
+      } else {
+        alpha = __builtin_amdgcn_exp2f(m[rt] - m_new);
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) p[h2][j] = __builtin_amdgcn_exp2f(x[h2][j] - m_new);
+      }
+      m[rt] = m_new;
+      lsum[rt] = lsum[rt] * alpha +
+                 (((p[0][0] + p[0][1]) + (p[0][2] + p[0][3])) + ((p[1][0] + p[1][1]) + (p[1][2] + p[1][3])));
+      if (__any(alpha != 1.f)) {  // wave-uniform: skip the rescale when no row's max moved
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) o[rt][dt] *= alpha;
+      }
+      // B = P^T for 32 tokens: k = 8grp + j holds token 4grp + j (j < 4) and
+      // 16 + 4grp + (j - 4); A = V^T uses the same token order.
+      pb[rt] = make_uint4(M::pk(p[0][0], p[0][1]), M::pk(p[0][2], p[0][3]), M::pk(p[1][0], p[1][1]),
+                          M::pk(p[1][2], p[1][3]));
     }
-    float mx = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
-                     fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
-    mx = group_max4(mx);
-    const float m_new = fmaxf(m, mx);
-    float p[2][4];
-    float alpha = 1.f;
-    if (m_new == -INFINITY) {
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) p[h2][j] = 0.f;
-    } else {
-      alpha = __builtin_amdgcn_exp2f(m - m_new);
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) p[h2][j] = __builtin_amdgcn_exp2f(x[h2][j] - m_new);
-    }
-    m = m_new;
-    lsum = lsum * alpha + (((p[0][0] + p[0][1]) + (p[0][2] + p[0][3])) + ((p[1][0] + p[1][1]) + (p[1][2] + p[1][3])));
-    if (__any(alpha != 1.f)) {  // wave-uniform: skip the rescale when no row's max moved
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
-    }
-    // B = P^T for 32 tokens: k = 8grp + j holds token 4grp + j (j < 4) and
-    // 16 + 4grp + (j - 4); A = V^T uses the same token order.
-    const uint4 pb = make_uint4(M::pk(p[0][0], p[0][1]), M::pk(p[0][2], p[0][3]),
-                                M::pk(p[1][0], p[1][1]), M::pk(p[1][2], p[1][3]));
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
       const i16x4_t lo = lds_read_tr16(vlds + rd_off + 32 * dt);
       const i16x4_t hi = lds_read_tr16(vlds + rd_off + 16 * kVRowBytes + 32 * dt);
       const uint4 va = __builtin_bit_cast(uint4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      o[dt] = M::qk(va, pb, o[dt]);
+#pragma unroll
+      for (int rt = 0; rt < NT; ++rt) o[rt][dt] = M::qk(va, pb[rt], o[rt][dt]);
     }
     __asm__ volatile("" ::: "memory");
   }
 
-  lsum = group_sum4(lsum);
-  if (np == 1) {
-    if (rvalid) {
-      const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+#pragma unroll
+  for (int rt = 0; rt < NT; ++rt) {
+    const float ls = group_sum4(lsum[rt]);
+    if (!rvalid[rt]) continue;
+    if (np == 1) {
+      const float inv = ls > 0.f ? 1.f / ls : 0.f;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
         uint2 w;
-        w.x = static_cast<uint32_t>(M::cvt(o[dt][0] * inv)) | (static_cast<uint32_t>(M::cvt(o[dt][1] * inv)) << 16);
-        w.y = static_cast<uint32_t>(M::cvt(o[dt][2] * inv)) | (static_cast<uint32_t>(M::cvt(o[dt][3] * inv)) << 16);
-        *reinterpret_cast<uint2*>(orow + 16 * dt + 4 * grp) = w;
+        w.x = static_cast<uint32_t>(M::cvt(o[rt][dt][0] * inv)) |
+              (static_cast<uint32_t>(M::cvt(o[rt][dt][1] * inv)) << 16);
+        w.y = static_cast<uint32_t>(M::cvt(o[rt][dt][2] * inv)) |
+              (static_cast<uint32_t>(M::cvt(o[rt][dt][3] * inv)) << 16);
+        *reinterpret_cast<uint2*>(orow[rt] + 16 * dt + 4 * grp) = w;
       }
-    }
-  } else if (rvalid) {
-    float* e = a.ws + ((static_cast<int64_t>(s) * a.Hkv + g) * a.P + part) * (kMaxRows * kPartFloats) +
-               r * kPartFloats;
+    } else {
+      float* e = a.ws + ((static_cast<int64_t>(s) * a.Hkv + g) * a.P + part) * (a.rows_cap * kPartFloats) +
+                 rt_row[rt] * kPartFloats;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-      *reinterpret_cast<float4*>(e + 16 * dt + 4 * grp) = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
-    if (grp == 0) {
-      e[kD] = m;
-      e[kD + 1] = lsum;
+      for (int dt = 0; dt < 8; ++dt)
+        *reinterpret_cast<float4*>(e + 16 * dt + 4 * grp) =
+            make_float4(o[rt][dt][0], o[rt][dt][1], o[rt][dt][2], o[rt][dt][3]);
+      if (grp == 0) {
+        e[kD] = m[rt];
+        e[kD + 1] = ls;
+      }
     }
   }
 }
 
 // Combine the parts of every split decode item: with m = max_p m_p,
 //   o = sum_p 2^(m_p - m) O_p / sum_p 2^(m_p - m) l_p.
-// One workgroup per (sequence, KV head); the per-(row, part) weights are
-// computed once into LDS, then each thread produces output elements.
+// One workgroup per (sequence, KV head, slice of kMergeRows rows).  Each wave
+// first forms the part weights of two rows (lane = part, one load each, wave
+// reductions) into LDS; then every thread produces four consecutive outputs
+// of one row from float4 partial loads, several parts in flight at once.
+constexpr int kMergeRows = 8;  // rows per merge workgroup (256 threads = 8 rows x 32 float4)
+
 template <class F>
 __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
-  __shared__ float wts[kMaxRows][kMaxParts];
-  __shared__ float inv_den[kMaxRows];
+  __shared__ float wts[kMergeRows][kMaxParts];
+  __shared__ float inv_den[kMergeRows];
   const int32_t s = blockIdx.x, g = blockIdx.y;
+  const int32_t r0 = blockIdx.z * kMergeRows;
   const int32_t q0 = a.qsl[s];
   const int32_t qlen = a.qsl[s + 1] - q0;
-  if (qlen <= 0 || qlen * a.G > kMaxRows) return;
+  const int32_t rows = qlen * a.G;
+  if (qlen <= 0 || rows > a.rows_cap || r0 >= rows) return;
   const int32_t L = a.seq_lens[s];
   if (L < qlen || ceil_div(L, a.bs) > a.MB) return;
   int32_t np, cpp;
   plan_parts(ceil_div(L, kChunk), a.P, &np, &cpp);
   if (np == 1) return;
-  const int32_t rows = qlen * a.G;
-  const float* base = a.ws + (static_cast<int64_t>(s) * a.Hkv + g) * a.P * (kMaxRows * kPartFloats);
-  if (threadIdx.x < rows) {
-    const int r = threadIdx.x;
-    float mm = -INFINITY;
-    for (int p = 0; p < np; ++p) mm = fmaxf(mm, base[(p * kMaxRows + r) * kPartFloats + kD]);
-    float den = 0.f;
-    for (int p = 0; p < np; ++p) {
-      const float* e = base + (p * kMaxRows + r) * kPartFloats;
-      const float w = mm == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(e[kD] - mm);
-      wts[r][p] = w;
-      den = fmaf(w, e[kD + 1], den);
-    }
-    inv_den[r] = den > 0.f ? 1.f / den : 0.f;
+  const int32_t stride = a.rows_cap * kPartFloats;  // one part's partials
+  const float* base = a.ws + (static_cast<int64_t>(s) * a.Hkv + g) * a.P * stride;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int rl = 2 * wave + k;  // row within the slice
+    const int32_t r = r0 + rl;
+    if (r >= rows) break;         // wave-uniform
+    const float* e = base + lane * stride + r * kPartFloats;
+    const float mp = lane < np ? e[kD] : -INFINITY;
+    const float lp = lane < np ? e[kD + 1] : 0.f;
+    const float mm = wave_max(mp);
+    const float w = (lane < np && mm != -INFINITY) ? __builtin_amdgcn_exp2f(mp - mm) : 0.f;
+    const float den = wave_sum(w * lp);
+    wts[rl][lane] = w;
+    if (lane == 0) inv_den[rl] = den > 0.f ? 1.f / den : 0.f;
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < rows * kD; idx += blockDim.x) {
-    const int r = idx / kD, d = idx - r * kD;
-    float num = 0.f;
-    for (int p = 0; p < np; ++p) num = fmaf(wts[r][p], base[(p * kMaxRows + r) * kPartFloats + d], num);
-    const int32_t i_row = r / a.G, hg = r - i_row * a.G;
-    const int64_t t = q0 + i_row;
-    a.out[(t * a.Hq + g * a.G + hg) * kD + d] = Mma<F>::cvt(num * inv_den[r]);
+  const int rl = threadIdx.x >> 5, d4 = threadIdx.x & 31;
+  const int32_t r = r0 + rl;
+  if (r >= rows) return;
+  const float* src = base + r * kPartFloats + 4 * d4;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  int p = 0;
+  for (; p + 4 <= np; p += 4) {
+    float4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const float4*>(src + (p + u) * stride);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float wu = wts[rl][p + u];
+      acc.x = fmaf(wu, v[u].x, acc.x);
+      acc.y = fmaf(wu, v[u].y, acc.y);
+      acc.z = fmaf(wu, v[u].z, acc.z);
+      acc.w = fmaf(wu, v[u].w, acc.w);
+    }
   }
+  for (; p < np; ++p) {
+    const float4 v = *reinterpret_cast<const float4*>(src + p * stride);
+    const float wu = wts[rl][p];
+    acc.x = fmaf(wu, v.x, acc.x);
+    acc.y = fmaf(wu, v.y, acc.y);
+    acc.z = fmaf(wu, v.z, acc.z);
+    acc.w = fmaf(wu, v.w, acc.w);
+  }
+  const float inv = inv_den[rl];
+  const int32_t i_row = r / a.G, hg = r - i_row * a.G;
+  uint2 o;
+  o.x = static_cast<uint32_t>(Mma<F>::cvt(acc.x * inv)) | (static_cast<uint32_t>(Mma<F>::cvt(acc.y * inv)) << 16);
+  o.y = static_cast<uint32_t>(Mma<F>::cvt(acc.z * inv)) | (static_cast<uint32_t>(Mma<F>::cvt(acc.w * inv)) << 16);
+  *reinterpret_cast<uint2*>(a.out + ((static_cast<int64_t>(q0) + i_row) * a.Hq + g * a.G + hg) * kD + 4 * d4) = o;
 }
 
 // Parts per sequence the launch provides for: enough for max_seq_len.  A
@@ -384,17 +475,27 @@ int32_t decode_parts(int32_t S, int32_t Hkv, int32_t max_seqlen) {
 }  // namespace
 
 bool fast_path_supported(const AttnArgs& a) {
+  // 16-byte vector loads and stores of q, the caches, out and the workspace
+  const uintptr_t align = reinterpret_cast<uintptr_t>(a.q) | reinterpret_cast<uintptr_t>(a.k_cache) |
+                          reinterpret_cast<uintptr_t>(a.v_cache) | reinterpret_cast<uintptr_t>(a.out) |
+                          reinterpret_cast<uintptr_t>(a.workspace);
   return (a.dtype == PA_BF16 || a.dtype == PA_F16) && a.D == kD && a.bs % kChunk == 0 &&
-         a.Hq / a.Hkv <= kMaxRows;
+         a.Hq / a.Hkv <= kTileRows && align % 16 == 0;
 }
 
-size_t fast_workspace_bytes(int32_t S, int32_t T, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_seqlen) {
+// Rows of the largest item the decode kernels take in a call: two tiles when
+// the max_query_len hint allows items of more than one tile, else one.
+static int32_t decode_rows_cap(int32_t G, int32_t max_q) {
+  return static_cast<int64_t>(max_q) * G > kTileRows ? kMaxRows : kTileRows;
+}
+
+size_t fast_workspace_bytes(int32_t S, int32_t T, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_q,
+                            int32_t max_seqlen) {
   (void)T;
-  (void)Hq;
-  if (D != kD) return 0;
+  if (D != kD || Hkv < 1 || Hq % Hkv) return 0;
   const int32_t P = decode_parts(S, Hkv, max_seqlen);
   if (P <= 1) return 0;
-  return static_cast<size_t>(S) * Hkv * P * kMaxRows * kPartFloats * sizeof(float);
+  return static_cast<size_t>(S) * Hkv * P * decode_rows_cap(Hq / Hkv, max_q) * kPartFloats * sizeof(float);
 }
 
 hipError_t launch_attn_fast(const AttnArgs& a, hipStream_t stream) {
@@ -413,6 +514,9 @@ hipError_t launch_attn_fast(const AttnArgs& a, hipStream_t stream) {
   d.MB = a.MB;
   d.bs = a.bs;
   d.P = decode_parts(a.S, a.Hkv, a.max_seqlen);
+  d.rows_cap = decode_rows_cap(d.G, a.max_qlen);
+  d.prefill_on = static_cast<int64_t>(a.max_qlen) * d.G > d.rows_cap ? 1 : 0;
+  d.max_q = a.max_qlen;
   d.scale_log2e = a.scale * 1.4426950408889634f;
   d.out = static_cast<uint16_t*>(a.out);
   d.ws = static_cast<float*>(a.workspace);
@@ -424,17 +528,26 @@ hipError_t launch_attn_fast(const AttnArgs& a, hipStream_t stream) {
   if (grid > INT32_MAX) return hipErrorInvalidValue;
   d.n_items = static_cast<int32_t>(items);
 
-  // prefill-class rows (query_len * G > 16): MFMA prefill kernel
-  hipError_t e = launch_attn_prefill(a, kMaxRows, stream);
-  if (e != hipSuccess) return e;
+  // prefill-class rows (query_len * G > rows_cap): MFMA prefill kernel
+  if (d.prefill_on) {
+    hipError_t e = launch_attn_prefill(a, d.rows_cap, stream);
+    if (e != hipSuccess) return e;
+  }
   launch_mark("decode_kernel", stream);
-  if (a.dtype == PA_BF16) decode_kernel<BF16><<<static_cast<uint32_t>(grid), 64, 0, stream>>>(d);
-  else decode_kernel<F16><<<static_cast<uint32_t>(grid), 64, 0, stream>>>(d);
+  if (a.dtype == PA_BF16) decode_kernel<BF16, 1><<<static_cast<uint32_t>(grid), 64, 0, stream>>>(d);
+  else decode_kernel<F16, 1><<<static_cast<uint32_t>(grid), 64, 0, stream>>>(d);
   launch_done(stream);
+  if (d.rows_cap > kTileRows) {
+    launch_mark("decode_kernel_2t", stream);
+    if (a.dtype == PA_BF16) decode_kernel<BF16, 2><<<static_cast<uint32_t>(grid), 64, 0, stream>>>(d);
+    else decode_kernel<F16, 2><<<static_cast<uint32_t>(grid), 64, 0, stream>>>(d);
+    launch_done(stream);
+  }
   if (d.P > 1) {
     launch_mark("merge_kernel", stream);
-    if (a.dtype == PA_BF16) merge_kernel<BF16><<<dim3(a.S, a.Hkv), 256, 0, stream>>>(d);
-    else merge_kernel<F16><<<dim3(a.S, a.Hkv), 256, 0, stream>>>(d);
+    const dim3 mgrid(a.S, a.Hkv, d.rows_cap / kMergeRows);
+    if (a.dtype == PA_BF16) merge_kernel<BF16><<<mgrid, 256, 0, stream>>>(d);
+    else merge_kernel<F16><<<mgrid, 256, 0, stream>>>(d);
     launch_done(stream);
   }
   return hipGetLastError();

@@ -43,7 +43,7 @@ __global__ __launch_bounds__(64) void attn_generic_kernel(
     const typename F::T* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ qsl, const int32_t* __restrict__ seq_lens, int32_t S, int32_t Hq,
     int32_t Hkv, int32_t D, int32_t bs, int32_t NB, int32_t MB, float scale,
-    typename F::T* __restrict__ out, int32_t* __restrict__ d_err, int32_t skip_rows_le) {
+    typename F::T* __restrict__ out, int32_t* __restrict__ d_err, int32_t skip_rows_le, int32_t max_q) {
   using T = typename F::T;
   const int32_t t = blockIdx.x;
   const int32_t h = blockIdx.y;
@@ -60,6 +60,7 @@ __global__ __launch_bounds__(64) void attn_generic_kernel(
     qlen = qsl[s + 1] - qsl[s];
     // rows of sequences with query_len * G <= skip_rows_le belong to another kernel
     if (qlen * (Hq / Hkv) <= skip_rows_le) return;
+    if (qlen > max_q && t == qsl[s] && h == 0 && lane == 0) flag(d_err, PA_DERR_HINT);
     L = seq_lens[s];
     if (L < 0 || qlen > L) err = PA_DERR_QLEN_GT_SEQLEN;
     else if (ceil_div(L, bs) > MB) err = PA_DERR_BLOCK_OOB;
@@ -145,7 +146,7 @@ hipError_t launch_attn_generic_rows(const AttnArgs& a, int32_t skip_rows_le, hip
   attn_generic_kernel<F><<<grid, 64, 0, stream>>>(                                                 \
       static_cast<const F::T*>(a.q), static_cast<const F::T*>(a.k_cache),                          \
       static_cast<const F::T*>(a.v_cache), a.block_tables, a.qsl, a.seq_lens, a.S, a.Hq, a.Hkv,   \
-      a.D, a.bs, a.NB, a.MB, a.scale, static_cast<F::T*>(a.out), a.d_err, skip_rows_le)
+      a.D, a.bs, a.NB, a.MB, a.scale, static_cast<F::T*>(a.out), a.d_err, skip_rows_le, a.max_qlen)
   launch_mark("attn_generic_kernel", stream);
   switch (a.dtype) {
     case PA_F32: PA_GENERIC(F32); break;

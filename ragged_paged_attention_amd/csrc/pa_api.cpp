@@ -116,11 +116,12 @@ pa_status_t pa_copy_blocks(const void* src_k, const void* src_v, void* dst_k, vo
 }
 
 size_t pa_attention_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
-                                   int32_t num_kv_heads, int32_t head_dim, int32_t max_seq_len) {
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t max_query_len,
+                                   int32_t max_seq_len) {
   if (num_seqs < 0 || num_tokens < 0 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1)
     return 0;
   return pa::fast_workspace_bytes(num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim,
-                                  max_seq_len);
+                                  max_query_len, max_seq_len);
 }
 
 pa_status_t pa_attention(const void* q, const void* k_cache, const void* v_cache,
@@ -158,7 +159,7 @@ pa_status_t pa_attention(const void* q, const void* k_cache, const void* v_cache
   } else {
     if (!fast_ok) return PA_ERR_UNSUPPORTED;
     const size_t need = pa::fast_workspace_bytes(num_seqs, num_tokens, num_q_heads, num_kv_heads,
-                                                 head_dim, max_seq_len);
+                                                 head_dim, max_query_len, max_seq_len);
     if (need > 0 && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE;
     e = pa::launch_attn_fast(a, static_cast<hipStream_t>(stream));
   }

@@ -55,7 +55,8 @@ hipError_t launch_attn_generic_rows(const AttnArgs& a, int32_t skip_rows_le, hip
 
 // attn_fast.hip: bf16/f16, head_dim 128, block_size % 16 == 0.
 bool fast_path_supported(const AttnArgs& a);
-size_t fast_workspace_bytes(int32_t S, int32_t T, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_seqlen);
+size_t fast_workspace_bytes(int32_t S, int32_t T, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_q,
+                            int32_t max_seqlen);
 hipError_t launch_attn_fast(const AttnArgs& a, hipStream_t stream);
 
 // attn_prefill.hip: rows of sequences with query_len * (Hq/Hkv) > min_rows.

@@ -53,7 +53,7 @@ def test_host_side_rejections_need_no_gpu():
     assert att(T=0) == 0                  # empty batch: nothing to do
     assert att() == 1                     # null pointers
     assert att(max_q=0) == 2              # size hints must be >= 1
-    assert lib.pa_attention_workspace_size(4, 100, 32, 32, 128, 2001) >= 0
+    assert lib.pa_attention_workspace_size(4, 100, 32, 32, 128, 1, 2001) >= 0
     cp = lambda nsrc=4, ndst=4, n=1, bb=8192, ptr=16: lib.pa_copy_blocks(ptr, ptr, ptr, ptr, nsrc, ndst, ptr, n, bb,
                                                                           NULL, NULL)
     assert cp(bb=8200) == 2               # block bytes not a multiple of 16

@@ -106,15 +106,19 @@ def test_zero_length_queries_mixed_in(dtype):
     assert max_abs_err(g.out, ref) <= tol_for(dtype)
 
 
-def test_small_max_query_len_hint_still_correct():
-    """The hints shape the launch only: a too-small max_query_len is slower,
-    not wrong."""
+def test_small_hints_flagged_and_still_correct_when_covered():
+    """A max_query_len below the true maximum flags PA_DERR_HINT.  Here it
+    still sends the long prompts to the prefill kernel (40 rows > the 32 of
+    two decode tiles), which covers any length, so the rows are right; a
+    too-small max_seq_len only makes split parts longer."""
     w = config(2, scale_down=4)
     g = GpuRun(w).fill_history().write_step_rows()
+    d_err = torch.zeros(1, dtype=torch.int32, device="cuda")
     out = rpa.pa_attention(g.db.q, g.k_cache, g.v_cache, g.db.block_tables, g.meta["query_start_loc"],
-                           g.db.seq_lens, 17, 3, w.scale)
+                           g.db.seq_lens, 40, 3, w.scale, d_err=d_err)
     torch.cuda.synchronize()
     _, _, _, ref = oracle.run_step(w)
+    assert int(d_err.item()) == rpa.PA_DERR_HINT
     assert max_abs_err(out, ref) <= tol_for(w.dtype)
 
 

@@ -186,7 +186,7 @@ def test_workspace_too_small_is_rejected():
     w = config(3, scale_down=8)
     g = GpuRun(w).fill_history()
     need = rpa.pa_attention_workspace_size(w.num_seqs, w.num_tokens, w.num_q_heads, w.num_kv_heads,
-                                           w.head_dim, w.max_seq_len)
+                                           w.head_dim, w.max_query_len, w.max_seq_len)
     if need == 0:
         pytest.skip("this shape needs no workspace")
     md = rpa.pa_build_metadata(g.db.query_lens, g.db.seq_lens, w.num_tokens, g.db.block_tables, w.block_size,

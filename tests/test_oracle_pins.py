@@ -413,6 +413,29 @@ def test_decode_equals_last_row_of_prefill():
     np.testing.assert_array_equal(o1[L - 1], o2[0])
 
 
+def test_verify_equals_sequential_decodes():
+    """Verifying q draft tokens in one pass (query_len q over a cached
+    context; "LLM 推理引擎 Continuous Batching 与 PagedAttention" §7.2) gives,
+    row for row, what q successive single-token decode steps give, each with
+    the earlier drafts already in the cache."""
+    rng = np.random.default_rng(43)
+    ctx, q, Hq, Hkv, D, bs = 9, 4, 8, 2, 8, 4
+    L = ctx + q
+    K = rng.standard_normal((L, Hkv, D)).astype(np.float32)
+    V = rng.standard_normal((L, Hkv, D)).astype(np.float32)
+    Q = rng.standard_normal((q, Hq, D)).astype(np.float32)
+    tab = [[6, 2, 0, 4]]
+    ver = _explicit("f32", Hq, Hkv, D, bs, 7, [q], [L], tab, Q, K[ctx:], V[ctx:],
+                    [ctx], [ctx], tab, K[:ctx], V[:ctx], [[0]])
+    _, _, _, o_ver = PA.run_step(ver)
+    for i in range(q):
+        n = ctx + i
+        dec = _explicit("f32", Hq, Hkv, D, bs, 7, [1], [n + 1], tab, Q[i:i + 1], K[n:n + 1], V[n:n + 1],
+                        [n], [n], tab, K[:n], V[:n], [[0]])
+        _, _, _, o_dec = PA.run_step(dec)
+        np.testing.assert_array_equal(o_ver[i], o_dec[0])
+
+
 def test_chunked_prefill_equals_one_shot():
     """Prefill in two chunks ([0:c], then [c:L] with c cached) equals one shot
     (vLLM 原理 §2.4 chunked prefill)."""

@@ -364,6 +364,28 @@ def config(n: int, seed: Optional[int] = None, dtype: Optional[str] = None, pois
     raise ValueError(f"no config {n}")
 
 
+def verify_batch(seed: int = 6, S: int = 64, q_lo: int = 2, q_hi: int = 8, ctx_lo: int = 2048,
+                 ctx_hi: int = 16384, Hq: int = 32, Hkv: int = 8, dtype: Optional[str] = None,
+                 poison: bool = True, scale_down: int = 1) -> Workload:
+    """Speculative-decoding verify batch: each of S sequences feeds its last
+    accepted token plus a few draft tokens (query_len uniform in q_lo..q_hi)
+    over a cached context of log-uniform length in [ctx_lo, ctx_hi]; 32/8
+    heads, head_dim 128, block_size 16, bf16 by default.  `scale_down` > 1
+    shrinks S and the context range for oracle-sized runs."""
+    rng = np.random.default_rng(seed)
+    f = int(scale_down)
+    bs, NB = 16, 40000
+    if f > 1:
+        S, ctx_lo, ctx_hi = max(2, S // f), max(1, ctx_lo // f), max(2, ctx_hi // f)
+    ql = rng.integers(q_lo, q_hi + 1, S)
+    ctx = np.rint(np.exp(rng.uniform(math.log(ctx_lo), math.log(ctx_hi), S))).astype(np.int64)
+    sl = [int(c) + int(q) for c, q in zip(ctx, ql)]
+    NB = _shrunk_pool(NB, [_ceil_div(L, bs) for L in sl], f)
+    tables = _place(rng, NB, [_ceil_div(L, bs) for L in sl])
+    return build_workload("spec_verify", dtype or "bf16", Hq, Hkv, 128, bs, NB, [int(q) for q in ql], sl, tables,
+                          seed, rng, poison=poison, notes=f"query_len {q_lo}..{q_hi} over {ctx_lo}..{ctx_hi} tokens")
+
+
 def random_batch(seed: int, S: int = 3, max_ctx: int = 12, max_q: int = 5, Hq: int = 4, Hkv: int = 2,
                  D: int = 16, bs: int = 4, dtype: str = "f32", extra_blocks: int = 4,
                  decode_frac: float = 0.4, poison: bool = True) -> Workload:
