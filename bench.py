@@ -38,6 +38,15 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, TFLOP/s (256 CU x 2.4 GHz x 4096 FLOP/clk)
 METRIC = "decode KV-read GB/s (% HBM peak) + mixed-batch attn tokens/s, 1 MI355X"
 PROFILES = os.path.join(ROOT, "profiles")
+# name fragment that identifies each kernel in rocprofv3 output (bf16 instances)
+KERNEL_MATCH = {
+    "decode_kernel": "decode_kernel<pa::BF16, 1>",
+    "decode_kernel_2t": "decode_kernel<pa::BF16, 2>",
+    "merge_kernel": "merge_kernel<pa::BF16>",
+    "prefill_kernel": "prefill_kernel<pa::BF16>",
+    "write_kv_kernel": "write_kv_kernel",
+    "copy_blocks_kernel": "copy_blocks_kernel",
+}
 KERNEL_SOURCES = {
     "decode_kernel": "ragged_paged_attention_amd/csrc/attn_fast.hip",
     "decode_kernel_2t": "ragged_paged_attention_amd/csrc/attn_fast.hip",
@@ -247,8 +256,8 @@ def summarize_pmc(fetch_dir, write_dir, kernel, workload, command):
     the kernel's counts."""
     fr = _csv_rows(_find(fetch_dir, "counter_collection.csv"))
     wr = _csv_rows(_find(write_dir, "counter_collection.csv"))
-    kf = _counter_per_dispatch(fr, "FETCH_SIZE", kernel)
-    kw = _counter_per_dispatch(wr, "WRITE_SIZE", kernel)
+    kf = _counter_per_dispatch(fr, "FETCH_SIZE", KERNEL_MATCH.get(kernel, kernel))
+    kw = _counter_per_dispatch(wr, "WRITE_SIZE", KERNEL_MATCH.get(kernel, kernel))
     # torch's fill_ (writes) and copy_ (reads and writes) of the calibration buffers
     cf, cw = [], []
     for cal in ("copyBuffer", "elementwise_kernel"):
