@@ -119,15 +119,52 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
   const uint16_t* kbase = a.k_cache + static_cast<int64_t>(g) * kD;
   const uint16_t* vbase = a.v_cache + static_cast<int64_t>(g) * kD;
 
-  // DMA of one tile: wave w fills rows 16w..16w+15 (one 16-token group, so one
-  // block id) of the K and V tiles, 4 rows per instruction, lane -> 16 bytes.
-  // Rows at or past the context end re-read the last valid row, so nothing
-  // unwritten (possibly NaN) ever reaches LDS; such rows are masked anyway.
+  // DMA of one tile: wave w fills rows kDmaRows*w .. (inside one 16-token
+  // group, so one block id) of the K and V tiles, 4 rows per instruction,
+  // lane -> 16 bytes.  Rows at or past the context end re-read the last valid
+  // row, so nothing unwritten (possibly NaN) ever reaches LDS; such rows are
+  // masked anyway.
   constexpr int kDmaRows = kTile / kWaves;  // tile rows each wave fills
   constexpr int kDmaInst = kDmaRows / 4;     // 4 rows per DMA instruction
-  const int row_base = kDmaRows * wave;      // within one 16-token group
+  static_assert(16 % kDmaRows == 0 || kDmaRows % 16 == 0, "a wave's rows stay inside 16-token groups");
+  const int row_base = kDmaRows * __builtin_amdgcn_readfirstlane(wave);  // wave-uniform
+  // Byte offsets of this lane's K and V sources from the first slot of the
+  // wave's rows; the same for every tile whose rows are all inside the context.
+  // (at most 15 slot rows of Hkv x 256 bytes: fits 32 bits for any Hkv the
+  // grid allows)
+  int32_t k_src_off[kDmaInst], v_src_off[kDmaInst];
+#pragma unroll
+  for (int u = 0; u < kDmaInst; ++u) {
+    const int row = row_base + 4 * u + grp;
+    const int32_t rowoff = (row & 15) * a.Hkv * kRowBytes;
+    k_src_off[u] = rowoff + 16 * (r ^ (row & 15));
+    v_src_off[u] = rowoff + 16 * (r ^ ((row & 7) << 1));
+  }
   auto issue_tile = [&](int32_t kt, int stage) {
     const int32_t t16 = kt * kTile + (row_base & ~15);
+    uint8_t* kdst = lds + stage * kStageBytes + row_base * kRowBytes;
+    uint8_t* vdst = kdst + kTileBytes;
+    if (t16 + 16 <= L) {  // all of the wave's rows inside the context: one block, fixed offsets
+      const int32_t lb = t16 / a.bs;
+      int32_t b = btrow[lb];
+      if (b < 0 || b >= a.NB) {
+        flag(a.d_err, PA_DERR_BLOCK_OOB);
+        b = 0;
+      }
+      const int64_t slot0 = static_cast<int64_t>(b) * a.bs + (t16 - lb * a.bs);  // first slot of the group
+      const uint8_t* ksrc = reinterpret_cast<const uint8_t*>(kbase + slot0 * slot_stride);
+      const uint8_t* vsrc = reinterpret_cast<const uint8_t*>(vbase + slot0 * slot_stride);
+#pragma unroll
+      for (int u = 0; u < kDmaInst; ++u) {
+        __builtin_amdgcn_global_load_lds((const void*)(ksrc + k_src_off[u]),
+                                         (__attribute__((address_space(3))) void*)(kdst + 4 * u * kRowBytes),
+                                         16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(vsrc + v_src_off[u]),
+                                         (__attribute__((address_space(3))) void*)(vdst + 4 * u * kRowBytes),
+                                         16, 0, 0);
+      }
+      return;
+    }
     const int32_t lb = (t16 < L ? t16 : L - 1) / a.bs;
     int32_t b = btrow[lb];
     if (b < 0 || b >= a.NB) {
@@ -135,8 +172,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
       b = 0;
     }
     const int64_t slot0 = static_cast<int64_t>(b) * a.bs + (t16 < L ? t16 - lb * a.bs : 0);
-    uint8_t* kdst = lds + stage * kStageBytes + row_base * kRowBytes;
-    uint8_t* vdst = kdst + kTileBytes;
 #pragma unroll
     for (int u = 0; u < kDmaInst; ++u) {
       const int row = row_base + 4 * u + grp;  // tile row this lane fills
