@@ -72,7 +72,13 @@ __device__ __forceinline__ int v_slot(int row, int chunk) { return row * kRowByt
 template <class F>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 2, kWaves / 2))) void prefill_kernel(PrefillArgs a) {
   using M = Mma<F>;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kStageBytes];  // 64 KB, two stages
+  // Two stages as two arrays: the tile loop below is unrolled by two so every
+  // LDS read and every DMA names its stage statically, and the compiler can
+  // see that the DMA into one stage does not touch the stage being read (with
+  // one array indexed by kt & 1 it waited for the next tile's DMA before the
+  // first read of the current tile, exposing every load's latency).
+  __shared__ __attribute__((aligned(1024))) uint8_t lds0[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds1[kStageBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -140,13 +146,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     k_src_off[u] = rowoff + 16 * (r ^ (row & 15));
     v_src_off[u] = rowoff + 16 * (r ^ ((row & 7) << 1));
   }
-  auto issue_tile = [&](int32_t kt, int stage) {
+  // Block id of the wave's 16-token group in tile kt when the group lies
+  // inside the context (loaded one tile ahead of its DMA, so the DMA never
+  // waits for the block table); 0 otherwise (the DMA then takes the per-row
+  // path).
+  // The table is read-only here and the index wave-uniform: read it through
+  // the constant address space, which makes it a scalar load (counted apart
+  // from the tile DMAs, so using it never waits for them).
+  const __attribute__((address_space(4))) int32_t* btrow_c =
+      (const __attribute__((address_space(4))) int32_t*)(btrow);
+  auto load_bid = [&](int32_t kt) -> int32_t {
     const int32_t t16 = kt * kTile + (row_base & ~15);
-    uint8_t* kdst = lds + stage * kStageBytes + row_base * kRowBytes;
+    return t16 + 16 <= L ? btrow_c[t16 / a.bs] : 0;
+  };
+  auto issue_tile = [&](int32_t kt, uint8_t* stage_lds, int32_t b) {
+    const int32_t t16 = kt * kTile + (row_base & ~15);
+    uint8_t* kdst = stage_lds + row_base * kRowBytes;
     uint8_t* vdst = kdst + kTileBytes;
     if (t16 + 16 <= L) {  // all of the wave's rows inside the context: one block, fixed offsets
       const int32_t lb = t16 / a.bs;
-      int32_t b = btrow[lb];
       if (b < 0 || b >= a.NB) {
         flag(a.d_err, PA_DERR_BLOCK_OOB);
         b = 0;
@@ -166,7 +184,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
       return;
     }
     const int32_t lb = (t16 < L ? t16 : L - 1) / a.bs;
-    int32_t b = btrow[lb];
+    b = btrow_c[lb];
     if (b < 0 || b >= a.NB) {
       flag(a.d_err, PA_DERR_BLOCK_OOB);
       b = 0;
@@ -180,7 +198,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
       if (tok < L) slot = slot0 + (row & 15);
       else {  // past the end: last valid token of the sequence
         const int32_t lb2 = (L - 1) / a.bs;
-        int32_t b2 = btrow[lb2];
+        int32_t b2 = btrow_c[lb2];
         b2 = (b2 < 0 || b2 >= a.NB) ? 0 : b2;
         slot = static_cast<int64_t>(b2) * a.bs + (L - 1 - lb2 * a.bs);
       }
@@ -202,7 +220,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     const int32_t last_row = min(row0 + kRowsPerWG, rows_total) - 1;
     const int32_t n_tiles = (L - qlen + last_row / a.G) / kTile + 1;
     __syncthreads();  // LDS of a previous query tile is no longer read
-    issue_tile(0, 0);
+    issue_tile(0, lds0, load_bid(0));
+    int32_t bid_next = load_bid(1);
 
     // this wave's rows and their Q^T fragments
     int32_t qpos[kNt];
@@ -247,10 +266,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
 
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    for (int32_t kt = 0; kt < n_tiles; ++kt) {
-      const int stage = kt & 1;
-      if (kt + 1 < n_tiles) issue_tile(kt + 1, stage ^ 1);
-      const uint8_t* kt_lds = lds + stage * kStageBytes;
+    auto tile = [&](int32_t kt, const uint8_t* kt_lds, uint8_t* next_lds) {
+      if (kt + 1 < n_tiles) {
+        issue_tile(kt + 1, next_lds, bid_next);
+        bid_next = load_bid(kt + 2);
+      }
       const uint8_t* vt_lds = kt_lds + kTileBytes;
       if (wave_active) {
         // S^T[16 mt + 4grp + j][row r of nt]; 8 independent MFMAs per K column block
@@ -338,6 +358,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
       }
       __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();  // next tile landed everywhere; this stage is free again
+    };
+    for (int32_t kt = 0; kt < n_tiles; kt += 2) {
+      tile(kt, lds0, lds1);
+      if (kt + 1 < n_tiles) tile(kt + 1, lds1, lds0);
     }
     if (!wave_active) continue;
 
