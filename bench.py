@@ -454,9 +454,10 @@ def main():
         g2 = setup(w2, torch).write_step_rows()
         db = g2.db
         out2 = torch.empty_like(db.q)
+        ws2 = workspace_for(w2, rpa, torch)
         qsl2 = g2.meta["query_start_loc"]
         attn2 = lambda: rpa.pa_attention(db.q, g2.k_cache, g2.v_cache, db.block_tables, qsl2, db.seq_lens,
-                                         w2.max_query_len, w2.max_seq_len, w2.scale, out=out2)
+                                         w2.max_query_len, w2.max_seq_len, w2.scale, out=out2, workspace=ws2)
         ms2 = timer.time(attn2, max(args.steps, 20), args.warmup)
         kern2 = timer.kernels(rpa, attn2, 10)
         fl2 = accounting.attention_flops(w2.step.query_lens, w2.step.seq_lens, w2.num_q_heads, w2.head_dim)

@@ -489,13 +489,23 @@ static int32_t decode_rows_cap(int32_t G, int32_t max_q) {
   return static_cast<int64_t>(max_q) * G > kTileRows ? kMaxRows : kTileRows;
 }
 
-size_t fast_workspace_bytes(int32_t S, int32_t T, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_q,
-                            int32_t max_seqlen) {
-  (void)T;
-  if (D != kD || Hkv < 1 || Hq % Hkv) return 0;
+// Workspace layout: split-K partials of the decode kernels (when a context
+// can take more than one part), then, 256-byte aligned, the prefill kernel's
+// work list (when the hint allows prefill-class rows).
+static size_t decode_ws_bytes(int32_t S, int32_t Hkv, int32_t G, int32_t max_q, int32_t max_seqlen) {
   const int32_t P = decode_parts(S, Hkv, max_seqlen);
   if (P <= 1) return 0;
-  return static_cast<size_t>(S) * Hkv * P * decode_rows_cap(Hq / Hkv, max_q) * kPartFloats * sizeof(float);
+  return (static_cast<size_t>(S) * Hkv * P * decode_rows_cap(G, max_q) * kPartFloats * sizeof(float) + 255) &
+         ~static_cast<size_t>(255);
+}
+
+size_t fast_workspace_bytes(int32_t S, int32_t T, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_q,
+                            int32_t max_seqlen) {
+  if (D != kD || Hkv < 1 || Hq % Hkv) return 0;
+  const int32_t G = Hq / Hkv;
+  size_t bytes = decode_ws_bytes(S, Hkv, G, max_q, max_seqlen);
+  if (static_cast<int64_t>(max_q) * G > decode_rows_cap(G, max_q)) bytes += prefill_plan_bytes(S, T, G);
+  return bytes;
 }
 
 hipError_t launch_attn_fast(const AttnArgs& a, hipStream_t stream) {
@@ -530,7 +540,9 @@ hipError_t launch_attn_fast(const AttnArgs& a, hipStream_t stream) {
 
   // prefill-class rows (query_len * G > rows_cap): MFMA prefill kernel
   if (d.prefill_on) {
-    hipError_t e = launch_attn_prefill(a, d.rows_cap, stream);
+    int32_t* plan = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(a.workspace) +
+                                               decode_ws_bytes(a.S, a.Hkv, d.G, a.max_qlen, a.max_seqlen));
+    hipError_t e = launch_attn_prefill(a, d.rows_cap, plan, stream);
     if (e != hipSuccess) return e;
   }
   launch_mark("decode_kernel", stream);

@@ -23,8 +23,15 @@
 //                                    accumulator of two 16-token tiles, used
 //                                    in place; V^T comes from two transposed
 //                                    LDS reads per fragment.
-// Only tiles that cross a wave's diagonal are masked.  Items are issued
-// heaviest first (last query tiles of each sequence first).
+// Only tiles that cross a wave's diagonal are masked.
+//
+// Work list: a one-workgroup planning kernel lists every (sequence, query
+// tile) of the prefill class, sorted by its number of K/V tiles, heaviest
+// first; the attention kernel's workgroups take the list in that order.  So
+// the longest items start first (the launch tail is short), and the grid,
+// sized from the batch's bound, only ever has empty items at its end: the
+// workgroup dispatcher is in order, and empty items mixed among real ones were
+// measured to hold back the real ones behind them.
 #include "mfma_common.h"
 #include "pa_common.h"
 #include "pa_internal.h"
@@ -54,11 +61,85 @@ struct PrefillArgs {
   const int32_t* block_tables;
   const int32_t* qsl;
   const int32_t* seq_lens;
-  int32_t S, Hq, Hkv, G, NB, MB, bs, n_qt, min_rows;
+  int32_t S, Hq, Hkv, G, NB, MB, bs, min_rows;
   float scale_log2e;
   uint16_t* out;
   int32_t* d_err;
+  const int32_t* plan;  // [0] = entries, then (sequence, query tile) pairs from kPlanHeader
 };
+
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanBuckets = 4096;  // K/V tile counts; larger ones share the top bucket
+constexpr int kPlanHeader = 64;     // int32 slots before the entries (count, padding)
+
+// K/V tiles query tile qt of a sequence reads (its last row's causal limit).
+__device__ __forceinline__ int32_t plan_weight(int32_t L, int32_t qlen, int32_t rows, int32_t G, int32_t qt) {
+  if (L < qlen) return 1;  // invalid: the kernel only writes zeros
+  const int32_t last_row = min(qt * kRowsPerWG + kRowsPerWG - 1, rows - 1);
+  return min((L - qlen + last_row / G) / kTile + 1, kPlanBuckets - 1);
+}
+
+// One workgroup: counting sort of the prefill-class query tiles by weight,
+// descending.  Entries of equal weight land in any order (which workgroup
+// computes a query tile does not change its result).
+// At most `cap` entries are written (more can only come from inconsistent
+// query_start_loc, which other kernels flag); a query_len outside 1..T is not
+// planned.
+__global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(const int32_t* __restrict__ qsl,
+                                                                    const int32_t* __restrict__ seq_lens,
+                                                                    int32_t S, int32_t T, int32_t G,
+                                                                    int32_t min_rows, int32_t cap,
+                                                                    int32_t* __restrict__ plan) {
+  __shared__ int32_t hist[kPlanBuckets];
+  __shared__ int32_t cursor[kPlanBuckets];
+  __shared__ int32_t wave_tot[kPlanThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < kPlanBuckets; i += kPlanThreads) hist[i] = 0;
+  __syncthreads();
+  for (int32_t s = tid; s < S; s += kPlanThreads) {
+    const int32_t qlen = qsl[s + 1] - qsl[s];
+    if (qlen <= 0 || qlen > T || qlen * G <= min_rows) continue;
+    const int32_t rows = qlen * G, L = seq_lens[s];
+    for (int32_t qt = 0; qt * kRowsPerWG < rows; ++qt) atomicAdd(&hist[plan_weight(L, qlen, rows, G, qt)], 1);
+  }
+  __syncthreads();
+  // exclusive scan in descending weight: thread t owns reversed buckets 4t..4t+3
+  constexpr int kPer = kPlanBuckets / kPlanThreads;
+  int32_t v[kPer], sum = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    v[j] = hist[kPlanBuckets - 1 - (kPer * tid + j)];
+    sum += v[j];
+  }
+  int32_t incl = sum;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t y = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) wave_tot[wave] = incl;
+  __syncthreads();
+  int32_t before = 0;
+  for (int w = 0; w < wave; ++w) before += wave_tot[w];
+  int32_t run = before + incl - sum;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int w = kPlanBuckets - 1 - (kPer * tid + j);
+    cursor[w] = run;  // first position of bucket w
+    run += v[j];
+  }
+  if (tid == kPlanThreads - 1) plan[0] = min(run, cap);  // total entries
+  __syncthreads();
+  int2* entries = reinterpret_cast<int2*>(plan + kPlanHeader);
+  for (int32_t s = tid; s < S; s += kPlanThreads) {
+    const int32_t qlen = qsl[s + 1] - qsl[s];
+    if (qlen <= 0 || qlen > T || qlen * G <= min_rows) continue;
+    const int32_t rows = qlen * G, L = seq_lens[s];
+    for (int32_t qt = 0; qt * kRowsPerWG < rows; ++qt) {
+      const int32_t pos = atomicAdd(&cursor[plan_weight(L, qlen, rows, G, qt)], 1);
+      if (pos < cap) entries[pos] = make_int2(s, qt);
+    }
+  }
+}
 
 // LDS tiles are 64 rows x 16 chunks of 16 bytes, stored without padding.
 // Chunk c of row R sits in slot c ^ swz(R):
@@ -84,36 +165,31 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
   const int lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, grp = lane >> 4;
 
-  // Items: (block of kQtRun query tiles, heaviest block first; sequence; KV
-  // head; tile in block, heaviest first).  Workgroup b runs on XCD b % 8, and
-  // runs of kQtRun consecutive items are kept on one XCD, so the query tiles
-  // of one (sequence, head) that share every K/V tile read them through the
-  // same L2 at about the same time.
+  // Items: (block of kQtRun list entries, heaviest first; KV head; entry in
+  // block).  Workgroup b runs on XCD b % 8 and runs of kQtRun consecutive
+  // items stay on one XCD: neighbouring entries of similar weight are often
+  // query tiles of the same sequence, which share every K/V tile through that
+  // XCD's L2.  The k-th run an XCD takes is run 8k + ((xcd + k) mod 8).
   const int32_t bid = blockIdx.x;
   const int32_t xcd = bid & 7, jj = bid >> 3;
-  const int32_t item = ((jj / kQtRun) * 8 + xcd) * kQtRun + (jj % kQtRun);
-  const int32_t n_qb = (a.n_qt + kQtRun - 1) / kQtRun;
-  if (item >= n_qb * kQtRun * a.S * a.Hkv) return;
-  const int32_t qi = item % kQtRun;
-  const int32_t tmp0 = item / kQtRun;
-  const int32_t g = tmp0 % a.Hkv;
-  const int32_t tmp = tmp0 / a.Hkv;
-  const int32_t s = tmp % a.S;
-  const int32_t qt_first = (n_qb - 1 - tmp / a.S) * kQtRun + (kQtRun - 1 - qi);
-  if (qt_first >= a.n_qt) return;
+  const int32_t kr = jj / kQtRun;
+  const int32_t item = (kr * 8 + ((xcd + kr) & 7)) * kQtRun + (jj % kQtRun);
+  const int32_t g = (item / kQtRun) % a.Hkv;
+  const int32_t e = (item / kQtRun / a.Hkv) * kQtRun + item % kQtRun;
+  if (e >= a.plan[0]) return;
+  const int2 ent = reinterpret_cast<const int2*>(a.plan + kPlanHeader)[e];
+  const int32_t s = ent.x, qt_first = ent.y;
 
   const int32_t q0 = a.qsl[s];
   const int32_t qlen = a.qsl[s + 1] - q0;
   const int32_t rows_total = qlen * a.G;
-  if (rows_total <= a.min_rows || qt_first * kRowsPerWG >= rows_total) return;
   const int32_t L = a.seq_lens[s];
 
   if (L < qlen || ceil_div(L, a.bs) > a.MB) {
     if (tid == 0) flag(a.d_err, L < qlen ? PA_DERR_QLEN_GT_SEQLEN : PA_DERR_BLOCK_OOB);
-    for (int64_t idx = tid + static_cast<int64_t>(qt_first) * kRowsPerWG * kD;
-         idx < static_cast<int64_t>(rows_total) * kD; idx += kThreads) {
-      if ((idx / kD) / kRowsPerWG % a.n_qt != qt_first) continue;  // another item's rows
-      const int32_t rho = static_cast<int32_t>(idx / kD);
+    const int32_t r0 = qt_first * kRowsPerWG, r1 = min(r0 + kRowsPerWG, rows_total);
+    for (int32_t idx = tid; idx < (r1 - r0) * kD; idx += kThreads) {
+      const int32_t rho = r0 + idx / kD;
       const int32_t i = rho / a.G, hg = rho - (rho / a.G) * a.G;
       a.out[((static_cast<int64_t>(q0) + i) * a.Hq + g * a.G + hg) * kD + idx % kD] = 0;
     }
@@ -213,9 +289,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     }
   };
 
-  // The launch covers max_query_len; any query tile beyond it (a too-small
-  // hint) is picked up by the same workgroup, n_qt tiles further on.
-  for (int32_t qt = qt_first; qt * kRowsPerWG < rows_total; qt += a.n_qt) {
+  {
+    const int32_t qt = qt_first;
     const int32_t row0 = qt * kRowsPerWG;
     const int32_t last_row = min(row0 + kRowsPerWG, rows_total) - 1;
     const int32_t n_tiles = (L - qlen + last_row / a.G) / kTile + 1;
@@ -363,7 +438,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
       tile(kt, lds0, lds1);
       if (kt + 1 < n_tiles) tile(kt + 1, lds1, lds0);
     }
-    if (!wave_active) continue;
+    if (!wave_active) return;
 
 #pragma unroll
     for (int nt = 0; nt < kNt; ++nt) {
@@ -383,7 +458,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
 
 }  // namespace
 
-hipError_t launch_attn_prefill(const AttnArgs& a, int32_t min_rows, hipStream_t stream) {
+int64_t prefill_plan_entries(int32_t S, int32_t T, int32_t G) {
+  return (static_cast<int64_t>(T) * G + kRowsPerWG - 1) / kRowsPerWG + S;
+}
+
+size_t prefill_plan_bytes(int32_t S, int32_t T, int32_t G) {
+  return static_cast<size_t>(kPlanHeader) * 4 + static_cast<size_t>(prefill_plan_entries(S, T, G)) * 8;
+}
+
+hipError_t launch_attn_prefill(const AttnArgs& a, int32_t min_rows, int32_t* plan, hipStream_t stream) {
   PrefillArgs p;
   p.q = static_cast<const uint16_t*>(a.q);
   p.k_cache = static_cast<const uint16_t*>(a.k_cache);
@@ -400,15 +483,21 @@ hipError_t launch_attn_prefill(const AttnArgs& a, int32_t min_rows, hipStream_t 
   p.bs = a.bs;
   const int64_t rows_max = static_cast<int64_t>(a.max_qlen) * p.G;
   if (rows_max <= min_rows) return hipSuccess;  // no prefill-class sequence can exist
-  p.n_qt = static_cast<int32_t>((rows_max + kRowsPerWG - 1) / kRowsPerWG);
   p.min_rows = min_rows;
+  p.plan = plan;
   p.scale_log2e = a.scale * 1.4426950408889634f;
   p.out = static_cast<uint16_t*>(a.out);
   p.d_err = a.d_err;
-  const int64_t n_qb = (p.n_qt + kQtRun - 1) / kQtRun;
-  const int64_t items_raw = n_qb * kQtRun * a.S * a.Hkv;
+  const int64_t n_eb = (prefill_plan_entries(a.S, a.T, p.G) + kQtRun - 1) / kQtRun;
+  const int64_t items_raw = n_eb * kQtRun * a.Hkv;
   const int64_t items = (items_raw + 8 * kQtRun - 1) / (8 * kQtRun) * (8 * kQtRun);
   if (items > INT32_MAX) return hipErrorInvalidValue;
+  launch_mark("prefill_plan_kernel", stream);
+  const int64_t cap = prefill_plan_entries(a.S, a.T, p.G);
+  if (cap > INT32_MAX) return hipErrorInvalidValue;
+  prefill_plan_kernel<<<1, kPlanThreads, 0, stream>>>(a.qsl, a.seq_lens, a.S, a.T, p.G, min_rows,
+                                                       static_cast<int32_t>(cap), plan);
+  launch_done(stream);
   launch_mark("prefill_kernel", stream);
   if (a.dtype == PA_BF16) prefill_kernel<BF16><<<static_cast<uint32_t>(items), kThreads, 0, stream>>>(p);
   else prefill_kernel<F16><<<static_cast<uint32_t>(items), kThreads, 0, stream>>>(p);

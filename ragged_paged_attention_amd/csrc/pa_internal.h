@@ -60,6 +60,8 @@ size_t fast_workspace_bytes(int32_t S, int32_t T, int32_t Hq, int32_t Hkv, int32
 hipError_t launch_attn_fast(const AttnArgs& a, hipStream_t stream);
 
 // attn_prefill.hip: rows of sequences with query_len * (Hq/Hkv) > min_rows.
-hipError_t launch_attn_prefill(const AttnArgs& a, int32_t min_rows, hipStream_t stream);
+// Plan (work list) of the prefill kernel: bytes of workspace it takes.
+size_t prefill_plan_bytes(int32_t S, int32_t T, int32_t G);
+hipError_t launch_attn_prefill(const AttnArgs& a, int32_t min_rows, int32_t* plan, hipStream_t stream);
 
 }  // namespace pa
