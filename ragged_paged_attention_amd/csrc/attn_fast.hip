@@ -36,7 +36,6 @@
 namespace pa {
 namespace {
 
-constexpr int kPartFloats = 132;    // per partial row: O[128], m, l, pad
 constexpr int kTileRows = 16;       // query rows per MFMA column tile
 constexpr int kMaxRows = 32;        // query rows of one decode item (two tiles)
 // Compile-time tuning of the decode work split (measured on MI355X).
@@ -68,6 +67,8 @@ struct DecodeArgs {
   const int32_t* seq_lens;
   int32_t S, Hq, Hkv, G, NB, MB, bs, P, n_items, grouped;
   int32_t rows_cap;    // 16 or 32: larger items go to the prefill kernel
+  const int4* seq_prefix;  // cascade prefix of each sequence (layout in pa_internal.h); null without cascade
+  const float* ws_pre;     // cascade prefix partials
   int32_t prefill_on;  // the prefill kernel runs in this call
   int32_t max_q;       // the caller's max_query_len hint
   float scale_log2e;
@@ -170,11 +171,21 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 3 
     }
     return;
   }
+  // A cascade member reads only its own suffix: the shared prefix is done once
+  // for its group by the prefill kernel, which leaves npp partials for the
+  // merge.
+  int32_t pre = 0, npp = 0;
+  if (a.seq_prefix) {
+    const int4 sp = a.seq_prefix[s];
+    pre = sp.x;
+    npp = sp.y;
+  }
   const int32_t nchunks = ceil_div(L, kChunk);
+  const int32_t cbeg = pre / kChunk;
   int32_t np, cpp;
-  plan_parts(nchunks, a.P, &np, &cpp);
+  plan_parts(nchunks - cbeg, a.P, &np, &cpp);
   if (part >= np) return;
-  const int32_t c0 = part * cpp;
+  const int32_t c0 = cbeg + part * cpp;
   const int32_t c1 = min(nchunks, c0 + cpp);
 
   // Q^T fragments (B operand): lane holds Q[row][32kk + 8grp .. +8] of its
@@ -359,7 +370,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 3 
   for (int rt = 0; rt < NT; ++rt) {
     const float ls = group_sum4(lsum[rt]);
     if (!rvalid[rt]) continue;
-    if (np == 1) {
+    if (np == 1 && npp == 0) {
       const float inv = ls > 0.f ? 1.f / ls : 0.f;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
@@ -395,7 +406,8 @@ constexpr int kMergeRows = 8;  // rows per merge workgroup (256 threads = 8 rows
 
 template <class F>
 __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
-  __shared__ float wts[kMergeRows][kMaxParts];
+  constexpr int kMaxMerge = kMaxParts + kCascadeMaxParts;  // decode parts + cascade prefix parts
+  __shared__ float wts[kMergeRows][kMaxMerge];
   __shared__ float inv_den[kMergeRows];
   const int32_t s = blockIdx.x, g = blockIdx.y;
   const int32_t r0 = blockIdx.z * kMergeRows;
@@ -405,49 +417,76 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
   if (qlen <= 0 || rows > a.rows_cap || r0 >= rows) return;
   const int32_t L = a.seq_lens[s];
   if (L < qlen || ceil_div(L, a.bs) > a.MB) return;
+  int32_t pre = 0, npp = 0, pslot = 0, prow = 0;
+  if (a.seq_prefix) {
+    const int4 sp = a.seq_prefix[s];
+    pre = sp.x;
+    npp = sp.y;
+    pslot = sp.z;
+    prow = sp.w;
+  }
   int32_t np, cpp;
-  plan_parts(ceil_div(L, kChunk), a.P, &np, &cpp);
-  if (np == 1) return;
-  const int32_t stride = a.rows_cap * kPartFloats;  // one part's partials
+  plan_parts(ceil_div(L, kChunk) - pre / kChunk, a.P, &np, &cpp);
+  if (np == 1 && npp == 0) return;  // written directly by the decode kernel
+  const int32_t ntot = np + npp;
+  const int32_t stride = a.rows_cap * kPartFloats;  // one decode part's partials
   const float* base = a.ws + (static_cast<int64_t>(s) * a.Hkv + g) * a.P * stride;
+  // partial row r of the k-th part: decode parts 0..np-1, then the group's
+  // prefix parts (slot pslot + j, this sequence's rows from prow)
+  auto part_row = [&](int32_t k, int32_t r) -> const float* {
+    return k < np ? base + k * stride + r * kPartFloats
+                  : a.ws_pre + ((static_cast<int64_t>(pslot + k - np) * a.Hkv + g) * kCascadeRows + prow + r) *
+                                   kPartFloats;
+  };
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int rl = 2 * wave + k;  // row within the slice
+  for (int k2 = 0; k2 < 2; ++k2) {
+    const int rl = 2 * wave + k2;  // row within the slice
     const int32_t r = r0 + rl;
-    if (r >= rows) break;         // wave-uniform
-    const float* e = base + lane * stride + r * kPartFloats;
-    const float mp = lane < np ? e[kD] : -INFINITY;
-    const float lp = lane < np ? e[kD + 1] : 0.f;
-    const float mm = wave_max(mp);
-    const float w = (lane < np && mm != -INFINITY) ? __builtin_amdgcn_exp2f(mp - mm) : 0.f;
-    const float den = wave_sum(w * lp);
-    wts[rl][lane] = w;
+    if (r >= rows) break;          // wave-uniform
+    float mp[2], lp[2], mm = -INFINITY;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int32_t k = 64 * c + lane;
+      const float* e = k < ntot ? part_row(k, r) : nullptr;
+      mp[c] = k < ntot ? e[kD] : -INFINITY;
+      lp[c] = k < ntot ? e[kD + 1] : 0.f;
+      mm = fmaxf(mm, mp[c]);
+    }
+    mm = wave_max(mm);
+    float den = 0.f;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int32_t k = 64 * c + lane;
+      const float w = (k < ntot && mm != -INFINITY) ? __builtin_amdgcn_exp2f(mp[c] - mm) : 0.f;
+      if (k < kMaxMerge) wts[rl][k] = w;
+      den += w * lp[c];
+    }
+    den = wave_sum(den);
     if (lane == 0) inv_den[rl] = den > 0.f ? 1.f / den : 0.f;
   }
   __syncthreads();
   const int rl = threadIdx.x >> 5, d4 = threadIdx.x & 31;
   const int32_t r = r0 + rl;
   if (r >= rows) return;
-  const float* src = base + r * kPartFloats + 4 * d4;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  int p = 0;
-  for (; p + 4 <= np; p += 4) {
+  int32_t k = 0;
+  for (; k + 4 <= ntot; k += 4) {
     float4 v[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const float4*>(src + (p + u) * stride);
+    for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const float4*>(part_row(k + u, r) + 4 * d4);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const float wu = wts[rl][p + u];
+      const float wu = wts[rl][k + u];
       acc.x = fmaf(wu, v[u].x, acc.x);
       acc.y = fmaf(wu, v[u].y, acc.y);
       acc.z = fmaf(wu, v[u].z, acc.z);
       acc.w = fmaf(wu, v[u].w, acc.w);
     }
   }
-  for (; p < np; ++p) {
-    const float4 v = *reinterpret_cast<const float4*>(src + p * stride);
-    const float wu = wts[rl][p];
+  for (; k < ntot; ++k) {
+    const float4 v = *reinterpret_cast<const float4*>(part_row(k, r) + 4 * d4);
+    const float wu = wts[rl][k];
     acc.x = fmaf(wu, v.x, acc.x);
     acc.y = fmaf(wu, v.y, acc.y);
     acc.z = fmaf(wu, v.z, acc.z);
@@ -489,26 +528,46 @@ static int32_t decode_rows_cap(int32_t G, int32_t max_q) {
   return static_cast<int64_t>(max_q) * G > kTileRows ? kMaxRows : kTileRows;
 }
 
-// Workspace layout: split-K partials of the decode kernels (when a context
-// can take more than one part), then, 256-byte aligned, the prefill kernel's
-// work list (when the hint allows prefill-class rows).
-static size_t decode_ws_bytes(int32_t S, int32_t Hkv, int32_t G, int32_t max_q, int32_t max_seqlen) {
-  const int32_t P = decode_parts(S, Hkv, max_seqlen);
-  if (P <= 1) return 0;
-  return (static_cast<size_t>(S) * Hkv * P * decode_rows_cap(G, max_q) * kPartFloats * sizeof(float) + 255) &
-         ~static_cast<size_t>(255);
+// Work split of one call, from the sizes and hints alone (the same numbers
+// give the workspace size and the launches).
+struct FastPlan {
+  int32_t G, P, rows_cap;
+  bool prefill_on, cascade_on;
+  size_t dec_bytes, pre_off, plan_off, bytes;
+};
+
+static FastPlan fast_plan(int32_t S, int32_t T, int32_t Hq, int32_t Hkv, int32_t max_q, int32_t max_seqlen) {
+  FastPlan f;
+  f.G = Hq / Hkv;
+  f.P = decode_parts(S, Hkv, max_seqlen);
+  f.rows_cap = decode_rows_cap(f.G, max_q);
+  f.prefill_on = static_cast<int64_t>(max_q) * f.G > f.rows_cap;
+  f.cascade_on = cascade_possible(S, max_seqlen);
+  // Workspace: split-K partials of the decode kernels (when a context can take
+  // more than one part, or a cascade prefix makes even one part a partial),
+  // the cascade prefix partials, then the work plan, each 256-byte aligned.
+  const size_t align = 255;
+  f.dec_bytes = (f.P > 1 || f.cascade_on)
+                    ? (static_cast<size_t>(S) * Hkv * f.P * f.rows_cap * kPartFloats * sizeof(float) + align) & ~align
+                    : 0;
+  f.pre_off = f.dec_bytes;
+  f.plan_off = f.pre_off + (f.cascade_on ? (static_cast<size_t>(kCascadeEntries) * Hkv * kCascadeRows * kPartFloats *
+                                                    sizeof(float) + align) & ~align
+                                         : 0);
+  f.bytes = f.plan_off + ((f.prefill_on || f.cascade_on)
+                              ? plan_layout(S, T, f.G, f.prefill_on, f.cascade_on).bytes
+                              : 0);
+  return f;
 }
 
 size_t fast_workspace_bytes(int32_t S, int32_t T, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_q,
                             int32_t max_seqlen) {
   if (D != kD || Hkv < 1 || Hq % Hkv) return 0;
-  const int32_t G = Hq / Hkv;
-  size_t bytes = decode_ws_bytes(S, Hkv, G, max_q, max_seqlen);
-  if (static_cast<int64_t>(max_q) * G > decode_rows_cap(G, max_q)) bytes += prefill_plan_bytes(S, T, G);
-  return bytes;
+  return fast_plan(S, T, Hq, Hkv, max_q, max_seqlen).bytes;
 }
 
 hipError_t launch_attn_fast(const AttnArgs& a, hipStream_t stream) {
+  const FastPlan f = fast_plan(a.S, a.T, a.Hq, a.Hkv, a.max_qlen, a.max_seqlen);
   DecodeArgs d;
   d.q = static_cast<const uint16_t*>(a.q);
   d.k_cache = static_cast<const uint16_t*>(a.k_cache);
@@ -519,31 +578,39 @@ hipError_t launch_attn_fast(const AttnArgs& a, hipStream_t stream) {
   d.S = a.S;
   d.Hq = a.Hq;
   d.Hkv = a.Hkv;
-  d.G = a.Hq / a.Hkv;
+  d.G = f.G;
   d.NB = a.NB;
   d.MB = a.MB;
   d.bs = a.bs;
-  d.P = decode_parts(a.S, a.Hkv, a.max_seqlen);
-  d.rows_cap = decode_rows_cap(d.G, a.max_qlen);
-  d.prefill_on = static_cast<int64_t>(a.max_qlen) * d.G > d.rows_cap ? 1 : 0;
+  d.P = f.P;
+  d.rows_cap = f.rows_cap;
+  d.prefill_on = f.prefill_on ? 1 : 0;
   d.max_q = a.max_qlen;
   d.scale_log2e = a.scale * 1.4426950408889634f;
   d.out = static_cast<uint16_t*>(a.out);
   d.ws = static_cast<float*>(a.workspace);
   d.d_err = a.d_err;
   d.grouped = a.Hkv < kGroupHeadsBelow ? 1 : 0;
+  d.seq_prefix = nullptr;
+  d.ws_pre = reinterpret_cast<const float*>(static_cast<const uint8_t*>(a.workspace) + f.pre_off);
   const int64_t s_pad = d.grouped ? (a.S + kXcdRun - 1) / kXcdRun * kXcdRun : a.S;
   const int64_t items = s_pad * a.Hkv * d.P;
   const int64_t grid = (items + 8 * kXcdRun - 1) / (8 * kXcdRun) * (8 * kXcdRun);
   if (grid > INT32_MAX) return hipErrorInvalidValue;
   d.n_items = static_cast<int32_t>(items);
 
-  // prefill-class rows (query_len * G > rows_cap): MFMA prefill kernel
-  if (d.prefill_on) {
-    int32_t* plan = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(a.workspace) +
-                                               decode_ws_bytes(a.S, a.Hkv, d.G, a.max_qlen, a.max_seqlen));
-    hipError_t e = launch_attn_prefill(a, d.rows_cap, plan, stream);
+  // plan (work list, cascade groups), then prefill query tiles and cascade
+  // prefix parts on the MFMA prefill kernel
+  if (f.prefill_on || f.cascade_on) {
+    int32_t* plan = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(a.workspace) + f.plan_off);
+    hipError_t e = launch_attn_plan(a, f.rows_cap, f.prefill_on, f.cascade_on, plan, stream);
     if (e != hipSuccess) return e;
+    e = launch_attn_prefill(a, f.rows_cap, f.prefill_on, f.cascade_on, plan,
+                            reinterpret_cast<float*>(static_cast<uint8_t*>(a.workspace) + f.pre_off), stream);
+    if (e != hipSuccess) return e;
+    if (f.cascade_on)
+      d.seq_prefix = reinterpret_cast<const int4*>(
+          reinterpret_cast<const uint8_t*>(plan) + plan_layout(a.S, a.T, f.G, f.prefill_on, f.cascade_on).seqpre_off);
   }
   launch_mark("decode_kernel", stream);
   if (a.dtype == PA_BF16) decode_kernel<BF16, 1><<<static_cast<uint32_t>(grid), 64, 0, stream>>>(d);
@@ -555,7 +622,7 @@ hipError_t launch_attn_fast(const AttnArgs& a, hipStream_t stream) {
     else decode_kernel<F16, 2><<<static_cast<uint32_t>(grid), 64, 0, stream>>>(d);
     launch_done(stream);
   }
-  if (d.P > 1) {
+  if (d.P > 1 || f.cascade_on) {
     launch_mark("merge_kernel", stream);
     const dim3 mgrid(a.S, a.Hkv, d.rows_cap / kMergeRows);
     if (a.dtype == PA_BF16) merge_kernel<BF16><<<mgrid, 256, 0, stream>>>(d);

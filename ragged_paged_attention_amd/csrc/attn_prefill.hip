@@ -65,12 +65,23 @@ struct PrefillArgs {
   float scale_log2e;
   uint16_t* out;
   int32_t* d_err;
-  const int32_t* plan;  // [0] = entries, then (sequence, query tile) pairs from kPlanHeader
+  const int32_t* plan;  // work list (layout in pa_internal.h)
+  const int4* groups;   // cascade groups
+  float* ws_pre;        // cascade prefix partials: (slot, KV head, group row)
 };
 
 constexpr int kPlanThreads = 1024;
-constexpr int kPlanBuckets = 4096;  // K/V tile counts; larger ones share the top bucket
-constexpr int kPlanHeader = 64;     // int32 slots before the entries (count, padding)
+constexpr int kPlanBuckets = 2048;  // K/V tile counts; larger ones share the top bucket
+
+struct PlanArgs {
+  const int32_t* qsl;
+  const int32_t* seq_lens;
+  const int32_t* block_tables;
+  int32_t S, T, G, MB, bs, rows_cap, prefill_on, cascade_on, cap_entries, cap_groups;
+  int32_t* plan;
+  int4* groups;
+  int4* seq_prefix;
+};
 
 // K/V tiles query tile qt of a sequence reads (its last row's causal limit).
 __device__ __forceinline__ int32_t plan_weight(int32_t L, int32_t qlen, int32_t rows, int32_t G, int32_t qt) {
@@ -79,31 +90,196 @@ __device__ __forceinline__ int32_t plan_weight(int32_t L, int32_t qlen, int32_t 
   return min((L - qlen + last_row / G) / kTile + 1, kPlanBuckets - 1);
 }
 
-// One workgroup: counting sort of the prefill-class query tiles by weight,
-// descending.  Entries of equal weight land in any order (which workgroup
-// computes a query tile does not change its result).
-// At most `cap` entries are written (more can only come from inconsistent
-// query_start_loc, which other kernels flag); a query_len outside 1..T is not
-// planned.
-__global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(const int32_t* __restrict__ qsl,
-                                                                    const int32_t* __restrict__ seq_lens,
-                                                                    int32_t S, int32_t T, int32_t G,
-                                                                    int32_t min_rows, int32_t cap,
-                                                                    int32_t* __restrict__ plan) {
+__device__ __forceinline__ int32_t wave_min_i32(int32_t v) {
+  for (int off = 32; off >= 1; off >>= 1) v = min(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+// Exclusive scan over the kPlanThreads threads of the plan workgroup (sum or
+// max, with `id` the identity); wbuf holds one value per wave.  Every thread
+// must call it.
+template <bool kMax>
+__device__ int32_t plan_block_scan(int32_t v, int32_t id, int32_t* wbuf) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int32_t incl = v;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t y = __shfl_up(incl, off, 64);
+    if (lane >= off) incl = kMax ? max(incl, y) : incl + y;
+  }
+  int32_t excl = __shfl_up(incl, 1, 64);
+  if (lane == 0) excl = id;
+  __syncthreads();
+  if (lane == 63) wbuf[wave] = incl;
+  __syncthreads();
+  int32_t before = id;
+  for (int w = 0; w < wave; ++w) before = kMax ? max(before, wbuf[w]) : before + wbuf[w];
+  return kMax ? max(before, excl) : before + excl;
+}
+
+// One workgroup plans the call.
+//
+// Cascade groups ("vLLM 原理" §2.1 and the prefix caching of
+// "LLM 推理引擎 Continuous Batching 与 PagedAttention" §5: sequences whose
+// tables map the same physical block at the same logical position share that
+// block's contents): maximal runs of consecutive single-token decode
+// sequences whose tables agree on at least kCascadeMinTiles full 64-token
+// tiles from the start, at most kRowsPerWG / G members.  The group's shared
+// prefix (the common full blocks, rounded down to whole tiles) is read once
+// for all members, in up to kCascadeMaxParts parts.
+//
+// Work list: every prefill-class (sequence, query tile) and every cascade
+// prefix part, counting-sorted by the K/V tiles it reads, heaviest first.
+// Entries of equal weight land in any order (which workgroup computes an
+// entry does not change its result).  At most cap_entries entries are written
+// (more can only come from inconsistent query_start_loc, which other kernels
+// flag); a query_len outside 1..T is not planned.
+__global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(PlanArgs a) {
   __shared__ int32_t hist[kPlanBuckets];
   __shared__ int32_t cursor[kPlanBuckets];
   __shared__ int32_t wave_tot[kPlanThreads / 64];
+  __shared__ int32_t common_blocks[kCascadeMaxSeqs];  // full blocks shared with sequence s - 1
+  __shared__ int32_t chunk_of[kCascadeMaxSeqs];       // first sequence of s's chunk
+  __shared__ int32_t n_groups;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int i = tid; i < kPlanBuckets; i += kPlanThreads) hist[i] = 0;
-  __syncthreads();
-  for (int32_t s = tid; s < S; s += kPlanThreads) {
-    const int32_t qlen = qsl[s + 1] - qsl[s];
-    if (qlen <= 0 || qlen > T || qlen * G <= min_rows) continue;
-    const int32_t rows = qlen * G, L = seq_lens[s];
-    for (int32_t qt = 0; qt * kRowsPerWG < rows; ++qt) atomicAdd(&hist[plan_weight(L, qlen, rows, G, qt)], 1);
+  if (tid == 0) n_groups = 0;
+
+  if (a.cascade_on) {
+    for (int32_t s = tid; s < a.S; s += kPlanThreads) {
+      a.seq_prefix[s] = make_int4(0, 0, 0, 0);
+      int32_t c = 0;
+      if (s > 0) {
+        const int32_t ql0 = a.qsl[s] - a.qsl[s - 1], ql1 = a.qsl[s + 1] - a.qsl[s];
+        const int32_t L0 = a.seq_lens[s - 1], L1 = a.seq_lens[s];
+        if (ql0 == 1 && ql1 == 1 && L0 >= 1 && L1 >= 1 && ceil_div(L0, a.bs) <= a.MB &&
+            ceil_div(L1, a.bs) <= a.MB) {
+          c = min(L0, L1) / a.bs;  // blocks full in both contexts
+          if (c > 0 && a.block_tables[static_cast<int64_t>(s - 1) * a.MB] !=
+                           a.block_tables[static_cast<int64_t>(s) * a.MB])
+            c = 0;
+        }
+      }
+      common_blocks[s] = c;
+    }
+    __syncthreads();
+    // first block that differs, one wave per candidate, 1024 blocks per step
+    // with all their loads in flight
+    for (int32_t s = 1 + wave; s < a.S; s += kPlanThreads / 64) {
+      const int32_t n = common_blocks[s];
+      if (n <= 1) continue;
+      const int32_t* b0 = a.block_tables + static_cast<int64_t>(s - 1) * a.MB;
+      const int32_t* b1 = a.block_tables + static_cast<int64_t>(s) * a.MB;
+      int32_t first = n;
+      for (int32_t j0 = 0; j0 < n && first == n; j0 += 1024) {
+        int32_t mn = n;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const int32_t j = j0 + 64 * u + lane;
+          if (j < n && b0[j] != b1[j]) mn = min(mn, j);
+        }
+        first = wave_min_i32(mn);
+      }
+      if (lane == 0) common_blocks[s] = first;
+    }
+    __syncthreads();
+    // Groups, in parallel: a run starts at s unless s shares at least
+    // kCascadeMinTiles tiles with s - 1; runs are cut into chunks of at most
+    // kCascadeRows / G members; a chunk of two or more is a group (the first
+    // kCascadeEntries of them), its prefix the fewest blocks any two
+    // neighbours in it share, rounded down to whole tiles.
+    constexpr int kPerS = kCascadeMaxSeqs / kPlanThreads;
+    const int32_t thr_blocks = ceil_div(kCascadeMinTiles * kTile, a.bs);
+    const int32_t max_members = max(2, kCascadeRows / a.G);
+    int32_t run_start[kPerS], m = -1;
+#pragma unroll
+    for (int j = 0; j < kPerS; ++j) {
+      const int32_t s = kPerS * tid + j;
+      if (s < a.S && (s == 0 || common_blocks[s] < thr_blocks)) m = s;
+      run_start[j] = m;  // latest start within this thread's slice
+    }
+    const int32_t before = plan_block_scan<true>(m, -1, wave_tot);
+#pragma unroll
+    for (int j = 0; j < kPerS; ++j) {
+      const int32_t s = kPerS * tid + j;
+      const int32_t rs = max(run_start[j], before);
+      if (s < a.S) chunk_of[s] = rs + (s - rs) / max_members * max_members;
+    }
+    __syncthreads();
+    int32_t is_group[kPerS], members[kPerS], common[kPerS], n_mine = 0;
+#pragma unroll
+    for (int j = 0; j < kPerS; ++j) {
+      const int32_t s = kPerS * tid + j;
+      is_group[j] = 0;
+      if (s < a.S && chunk_of[s] == s) {
+        int32_t e = s + 1, c = INT32_MAX;
+        while (e < a.S && chunk_of[e] == s) {
+          c = min(c, common_blocks[e]);
+          ++e;
+        }
+        members[j] = e - s;
+        common[j] = c;
+        is_group[j] = e - s >= 2;
+        n_mine += is_group[j];
+      }
+    }
+    int32_t gidx = plan_block_scan<false>(n_mine, 0, wave_tot);
+#pragma unroll
+    for (int j = 0; j < kPerS; ++j) {
+      if (!is_group[j]) continue;
+      if (gidx < a.cap_groups)
+        a.groups[gidx] = make_int4(kPerS * tid + j, members[j], common[j] * a.bs / kTile * kTile, 0);
+      ++gidx;
+    }
+    if (tid == kPlanThreads - 1) n_groups = min(gidx, a.cap_groups);
+    __syncthreads();
+    // parts (up to kCascadeMaxParts of at least kCascadeMinTiles tiles,
+    // kCascadeEntries over all groups) and each group's first prefix slot
+    const int32_t ngr = n_groups;
+    if (wave == 0) {
+      int32_t parts = 0;
+      int4 gr = make_int4(0, 0, 0, 0);
+      if (lane < ngr) {
+        gr = a.groups[lane];
+        parts = max(1, min(min(kCascadeMaxParts, gr.z / kTile / kCascadeMinTiles), kCascadeEntries / ngr));
+      }
+      int32_t base = parts;
+      for (int off = 1; off < 64; off <<= 1) {
+        const int32_t y = __shfl_up(base, off, 64);
+        if (lane >= off) base += y;
+      }
+      base -= parts;
+      if (lane < ngr) {
+        gr.w = parts | (base << 8);
+        a.groups[lane] = gr;
+      }
+    }
+    __syncthreads();
+    for (int32_t gi = wave; gi < ngr; gi += kPlanThreads / 64) {
+      const int4 gr = a.groups[gi];
+      for (int32_t k = lane; k < gr.y; k += 64)
+        a.seq_prefix[gr.x + k] = make_int4(gr.z, gr.w & 255, gr.w >> 8, k * a.G);
+    }
+    if (tid == 0) a.plan[1] = ngr;
   }
   __syncthreads();
-  // exclusive scan in descending weight: thread t owns reversed buckets 4t..4t+3
+  const int32_t ng = n_groups;
+
+  // histogram of weights
+  if (a.prefill_on) {
+    for (int32_t s = tid; s < a.S; s += kPlanThreads) {
+      const int32_t qlen = a.qsl[s + 1] - a.qsl[s];
+      if (qlen <= 0 || qlen > a.T || qlen * a.G <= a.rows_cap) continue;
+      const int32_t rows = qlen * a.G, L = a.seq_lens[s];
+      for (int32_t qt = 0; qt * kRowsPerWG < rows; ++qt) atomicAdd(&hist[plan_weight(L, qlen, rows, a.G, qt)], 1);
+    }
+  }
+  for (int32_t gi = tid; gi < ng; gi += kPlanThreads) {
+    const int4 gr = a.groups[gi];
+    const int32_t parts = gr.w & 255;
+    atomicAdd(&hist[min(ceil_div(gr.z / kTile, parts), kPlanBuckets - 1)], parts);
+  }
+  __syncthreads();
+  // exclusive scan in descending weight: thread t owns reversed buckets
   constexpr int kPer = kPlanBuckets / kPlanThreads;
   int32_t v[kPer], sum = 0;
 #pragma unroll
@@ -127,19 +303,31 @@ __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(const int32_
     cursor[w] = run;  // first position of bucket w
     run += v[j];
   }
-  if (tid == kPlanThreads - 1) plan[0] = min(run, cap);  // total entries
+  if (tid == kPlanThreads - 1) a.plan[0] = min(run, a.cap_entries);  // total entries
   __syncthreads();
-  int2* entries = reinterpret_cast<int2*>(plan + kPlanHeader);
-  for (int32_t s = tid; s < S; s += kPlanThreads) {
-    const int32_t qlen = qsl[s + 1] - qsl[s];
-    if (qlen <= 0 || qlen > T || qlen * G <= min_rows) continue;
-    const int32_t rows = qlen * G, L = seq_lens[s];
-    for (int32_t qt = 0; qt * kRowsPerWG < rows; ++qt) {
-      const int32_t pos = atomicAdd(&cursor[plan_weight(L, qlen, rows, G, qt)], 1);
-      if (pos < cap) entries[pos] = make_int2(s, qt);
+  int2* entries = reinterpret_cast<int2*>(a.plan + kPlanHeader);
+  if (a.prefill_on) {
+    for (int32_t s = tid; s < a.S; s += kPlanThreads) {
+      const int32_t qlen = a.qsl[s + 1] - a.qsl[s];
+      if (qlen <= 0 || qlen > a.T || qlen * a.G <= a.rows_cap) continue;
+      const int32_t rows = qlen * a.G, L = a.seq_lens[s];
+      for (int32_t qt = 0; qt * kRowsPerWG < rows; ++qt) {
+        const int32_t pos = atomicAdd(&cursor[plan_weight(L, qlen, rows, a.G, qt)], 1);
+        if (pos < a.cap_entries) entries[pos] = make_int2(s, qt);
+      }
+    }
+  }
+  for (int32_t gi = tid; gi < ng; gi += kPlanThreads) {
+    const int4 gr = a.groups[gi];
+    const int32_t parts = gr.w & 255;
+    const int32_t w = min(ceil_div(gr.z / kTile, parts), kPlanBuckets - 1);
+    for (int32_t pp = 0; pp < parts; ++pp) {
+      const int32_t pos = atomicAdd(&cursor[w], 1);
+      if (pos < a.cap_entries) entries[pos] = make_int2(-(gi + 1), pp);
     }
   }
 }
+
 
 // LDS tiles are 64 rows x 16 chunks of 16 bytes, stored without padding.
 // Chunk c of row R sits in slot c ^ swz(R):
@@ -178,14 +366,36 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
   const int32_t e = (item / kQtRun / a.Hkv) * kQtRun + item % kQtRun;
   if (e >= a.plan[0]) return;
   const int2 ent = reinterpret_cast<const int2*>(a.plan + kPlanHeader)[e];
-  const int32_t s = ent.x, qt_first = ent.y;
+  // A prefill entry is one query tile of sequence s.  A cascade entry is one
+  // part of a group's shared prefix: its rows are (member, query head) pairs,
+  // one decode row per member, all of the prefix is visible to them, K/V come
+  // through the first member's table (the same blocks as every member's), and
+  // the result is a split-K partial per row for the decode merge.
+  const bool cascade = ent.x < 0;
+  int32_t s, qt_first, q0, qlen, rows_total, L, pp = 0, slot = 0, kt_begin = 0, kt_end = 0;
+  if (!cascade) {
+    s = ent.x;
+    qt_first = ent.y;
+    q0 = a.qsl[s];
+    qlen = a.qsl[s + 1] - q0;
+    rows_total = qlen * a.G;
+    L = a.seq_lens[s];
+  } else {
+    const int4 gr = a.groups[-ent.x - 1];
+    s = gr.x;
+    qt_first = 0;
+    q0 = 0;
+    qlen = 1;
+    rows_total = gr.y * a.G;
+    L = gr.z;  // the prefix: every tile read lies inside it
+    pp = ent.y;
+    slot = (gr.w >> 8) + pp;
+    const int32_t per = ceil_div(gr.z / kTile, gr.w & 255);
+    kt_begin = pp * per;
+    kt_end = min(gr.z / kTile, kt_begin + per);
+  }
 
-  const int32_t q0 = a.qsl[s];
-  const int32_t qlen = a.qsl[s + 1] - q0;
-  const int32_t rows_total = qlen * a.G;
-  const int32_t L = a.seq_lens[s];
-
-  if (L < qlen || ceil_div(L, a.bs) > a.MB) {
+  if (!cascade && (L < qlen || ceil_div(L, a.bs) > a.MB)) {
     if (tid == 0) flag(a.d_err, L < qlen ? PA_DERR_QLEN_GT_SEQLEN : PA_DERR_BLOCK_OOB);
     const int32_t r0 = qt_first * kRowsPerWG, r1 = min(r0 + kRowsPerWG, rows_total);
     for (int32_t idx = tid; idx < (r1 - r0) * kD; idx += kThreads) {
@@ -293,10 +503,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     const int32_t qt = qt_first;
     const int32_t row0 = qt * kRowsPerWG;
     const int32_t last_row = min(row0 + kRowsPerWG, rows_total) - 1;
-    const int32_t n_tiles = (L - qlen + last_row / a.G) / kTile + 1;
-    __syncthreads();  // LDS of a previous query tile is no longer read
-    issue_tile(0, lds0, load_bid(0));
-    int32_t bid_next = load_bid(1);
+    if (!cascade) kt_end = (L - qlen + last_row / a.G) / kTile + 1;
+    // flat token index of row rho (its query head is rho mod G)
+    auto row_token = [&](int32_t rho) -> int32_t {
+      return cascade ? a.qsl[s + rho / a.G] : q0 + rho / a.G;
+    };
+    issue_tile(kt_begin, lds0, load_bid(kt_begin));
+    int32_t bid_next = load_bid(kt_begin + 1);
 
     // this wave's rows and their Q^T fragments
     int32_t qpos[kNt];
@@ -306,14 +519,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
       const int32_t rho = row0 + wave * kRowsPerWave + nt * 16 + r;
       const bool valid = rho < rows_total;
       const int32_t i = rho / a.G, hg = rho - (rho / a.G) * a.G;
-      qpos[nt] = valid ? L - qlen + i : -1;
-      const uint16_t* qp = a.q + ((static_cast<int64_t>(q0) + i) * a.Hq + g * a.G + hg) * kD + 8 * grp;
+      qpos[nt] = cascade ? INT32_MAX : (valid ? L - qlen + i : -1);
+      const int32_t t = valid ? row_token(rho) : 0;
+      const uint16_t* qp = a.q + (static_cast<int64_t>(t) * a.Hq + g * a.G + hg) * kD + 8 * grp;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) qf[nt][kk] = valid ? ld16(qp + 32 * kk) : make_uint4(0, 0, 0, 0);
     }
     const int32_t wave_row0 = row0 + wave * kRowsPerWave;
     const bool wave_active = wave_row0 < rows_total;
-    const int32_t qpos_min_wave = L - qlen + wave_row0 / a.G;
+    const int32_t qpos_min_wave = cascade ? INT32_MAX : L - qlen + wave_row0 / a.G;
 
     // Running max per row in log2 units.  It is only moved when a tile's max
     // exceeds it by more than kRescaleSlack, so p = 2^(x - m) stays <= 2^8 and
@@ -342,7 +556,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     auto tile = [&](int32_t kt, const uint8_t* kt_lds, uint8_t* next_lds) {
-      if (kt + 1 < n_tiles) {
+      if (kt + 1 < kt_end) {
         issue_tile(kt + 1, next_lds, bid_next);
         bid_next = load_bid(kt + 2);
       }
@@ -434,11 +648,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
       __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();  // next tile landed everywhere; this stage is free again
     };
-    for (int32_t kt = 0; kt < n_tiles; kt += 2) {
+    for (int32_t kt = kt_begin; kt < kt_end; kt += 2) {
       tile(kt, lds0, lds1);
-      if (kt + 1 < n_tiles) tile(kt + 1, lds1, lds0);
+      if (kt + 1 < kt_end) tile(kt + 1, lds1, lds0);
     }
     if (!wave_active) return;
+
+    if (cascade) {  // split-K partials (O unnormalised, m in log2 units, l) of every member row
+#pragma unroll
+      for (int nt = 0; nt < kNt; ++nt) {
+        const int32_t rho = wave_row0 + nt * 16 + r;
+        if (rho >= rows_total) continue;
+        float* pe = a.ws_pre + ((static_cast<int64_t>(slot) * a.Hkv + g) * kCascadeRows + rho) * kPartFloats;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+          *reinterpret_cast<float4*>(pe + 16 * dt + 4 * grp) =
+              make_float4(o[nt][dt][0], o[nt][dt][1], o[nt][dt][2], o[nt][dt][3]);
+        if (grp == 0) {
+          pe[kD] = m[nt];
+          pe[kD + 1] = osum[nt][0];
+        }
+      }
+      return;
+    }
 
 #pragma unroll
     for (int nt = 0; nt < kNt; ++nt) {
@@ -458,15 +690,54 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
 
 }  // namespace
 
-int64_t prefill_plan_entries(int32_t S, int32_t T, int32_t G) {
+static int64_t prefill_entries_cap(int32_t S, int32_t T, int32_t G) {
   return (static_cast<int64_t>(T) * G + kRowsPerWG - 1) / kRowsPerWG + S;
 }
 
-size_t prefill_plan_bytes(int32_t S, int32_t T, int32_t G) {
-  return static_cast<size_t>(kPlanHeader) * 4 + static_cast<size_t>(prefill_plan_entries(S, T, G)) * 8;
+PlanLayout plan_layout(int32_t S, int32_t T, int32_t G, bool prefill_on, bool cascade_on) {
+  PlanLayout l;
+  l.cap_groups = cascade_on ? kCascadeEntries : 0;
+  const int64_t cap = (prefill_on ? prefill_entries_cap(S, T, G) : 0) + (cascade_on ? kCascadeEntries : 0);
+  l.cap_entries = static_cast<int32_t>(cap > INT32_MAX ? INT32_MAX : cap);
+  l.groups_off = (static_cast<size_t>(kPlanHeader) * 4 + static_cast<size_t>(cap) * 8 + 15) & ~static_cast<size_t>(15);
+  l.seqpre_off = l.groups_off + static_cast<size_t>(l.cap_groups) * 16;
+  l.bytes = l.seqpre_off + (cascade_on ? static_cast<size_t>(S) * 16 : 0);
+  return l;
 }
 
-hipError_t launch_attn_prefill(const AttnArgs& a, int32_t min_rows, int32_t* plan, hipStream_t stream) {
+bool cascade_possible(int32_t S, int32_t max_seqlen) {
+  return S >= 2 && S <= kCascadeMaxSeqs && max_seqlen >= 2 * kCascadeMinTiles * kTile;
+}
+
+hipError_t launch_attn_plan(const AttnArgs& a, int32_t rows_cap, bool prefill_on, bool cascade_on,
+                            int32_t* plan, hipStream_t stream) {
+  const int32_t G = a.Hq / a.Hkv;
+  const PlanLayout l = plan_layout(a.S, a.T, G, prefill_on, cascade_on);
+  PlanArgs p;
+  p.qsl = a.qsl;
+  p.seq_lens = a.seq_lens;
+  p.block_tables = a.block_tables;
+  p.S = a.S;
+  p.T = a.T;
+  p.G = G;
+  p.MB = a.MB;
+  p.bs = a.bs;
+  p.rows_cap = rows_cap;
+  p.prefill_on = prefill_on;
+  p.cascade_on = cascade_on;
+  p.cap_entries = l.cap_entries;
+  p.cap_groups = l.cap_groups;
+  p.plan = plan;
+  p.groups = reinterpret_cast<int4*>(reinterpret_cast<uint8_t*>(plan) + l.groups_off);
+  p.seq_prefix = reinterpret_cast<int4*>(reinterpret_cast<uint8_t*>(plan) + l.seqpre_off);
+  launch_mark("attn_plan_kernel", stream);
+  attn_plan_kernel<<<1, kPlanThreads, 0, stream>>>(p);
+  launch_done(stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_prefill(const AttnArgs& a, int32_t rows_cap, bool prefill_on, bool cascade_on,
+                               const int32_t* plan, float* ws_pre, hipStream_t stream) {
   PrefillArgs p;
   p.q = static_cast<const uint16_t*>(a.q);
   p.k_cache = static_cast<const uint16_t*>(a.k_cache);
@@ -481,23 +752,19 @@ hipError_t launch_attn_prefill(const AttnArgs& a, int32_t min_rows, int32_t* pla
   p.NB = a.NB;
   p.MB = a.MB;
   p.bs = a.bs;
-  const int64_t rows_max = static_cast<int64_t>(a.max_qlen) * p.G;
-  if (rows_max <= min_rows) return hipSuccess;  // no prefill-class sequence can exist
-  p.min_rows = min_rows;
-  p.plan = plan;
+  p.min_rows = rows_cap;
   p.scale_log2e = a.scale * 1.4426950408889634f;
   p.out = static_cast<uint16_t*>(a.out);
   p.d_err = a.d_err;
-  const int64_t n_eb = (prefill_plan_entries(a.S, a.T, p.G) + kQtRun - 1) / kQtRun;
+  const PlanLayout l = plan_layout(a.S, a.T, p.G, prefill_on, cascade_on);
+  p.plan = plan;
+  p.groups = reinterpret_cast<const int4*>(reinterpret_cast<const uint8_t*>(plan) + l.groups_off);
+  p.ws_pre = ws_pre;
+  const int64_t n_eb = (static_cast<int64_t>(l.cap_entries) + kQtRun - 1) / kQtRun;
   const int64_t items_raw = n_eb * kQtRun * a.Hkv;
   const int64_t items = (items_raw + 8 * kQtRun - 1) / (8 * kQtRun) * (8 * kQtRun);
   if (items > INT32_MAX) return hipErrorInvalidValue;
-  launch_mark("prefill_plan_kernel", stream);
-  const int64_t cap = prefill_plan_entries(a.S, a.T, p.G);
-  if (cap > INT32_MAX) return hipErrorInvalidValue;
-  prefill_plan_kernel<<<1, kPlanThreads, 0, stream>>>(a.qsl, a.seq_lens, a.S, a.T, p.G, min_rows,
-                                                       static_cast<int32_t>(cap), plan);
-  launch_done(stream);
+  if (items == 0) return hipSuccess;
   launch_mark("prefill_kernel", stream);
   if (a.dtype == PA_BF16) prefill_kernel<BF16><<<static_cast<uint32_t>(items), kThreads, 0, stream>>>(p);
   else prefill_kernel<F16><<<static_cast<uint32_t>(items), kThreads, 0, stream>>>(p);

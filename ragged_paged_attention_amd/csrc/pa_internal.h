@@ -60,8 +60,39 @@ size_t fast_workspace_bytes(int32_t S, int32_t T, int32_t Hq, int32_t Hkv, int32
 hipError_t launch_attn_fast(const AttnArgs& a, hipStream_t stream);
 
 // attn_prefill.hip: rows of sequences with query_len * (Hq/Hkv) > min_rows.
-// Plan (work list) of the prefill kernel: bytes of workspace it takes.
-size_t prefill_plan_bytes(int32_t S, int32_t T, int32_t G);
-hipError_t launch_attn_prefill(const AttnArgs& a, int32_t min_rows, int32_t* plan, hipStream_t stream);
+// Work plan of one call on the MFMA paths, written to the workspace by the
+// planning kernel (attn_prefill.hip) and read by the prefill, decode and merge
+// kernels:
+//   int32 header[kPlanHeader]   [0] list entries, [1] cascade groups
+//   int2  entries[cap_entries]  (s >= 0, q-tile): a prefill query tile;
+//                               (-(group + 1), part): a part of a cascade
+//                               group's shared prefix
+//   int4  groups[cap_groups]    (first sequence, members, prefix tokens,
+//                               parts | first prefix slot << 8)
+//   int4  seq_prefix[S]         (prefix tokens, parts, first prefix slot, first
+//                               row in the group) of the sequence's cascade
+//                               group; all 0 if it has none
+// Prefix partials live in their own workspace region: kCascadeEntries slots
+// (one per prefix part) x KV heads x kCascadeRows rows x kPartFloats floats.
+constexpr int kPlanHeader = 64;
+constexpr int kPartFloats = 132;       // one split-K partial row: O[128], m (log2 units), l, pad
+constexpr int kCascadeMaxParts = 16;   // prefix parts of one group
+constexpr int kCascadeEntries = 64;    // prefix parts of one call, over all groups
+constexpr int kCascadeRows = 128;      // rows of one group: members x query heads
+constexpr int kCascadeMinTiles = 16;   // shortest shared prefix taken, in 64-token tiles
+constexpr int kCascadeMaxSeqs = 4096;  // sequences the detection handles (LDS)
+struct PlanLayout {
+  int32_t cap_entries, cap_groups;
+  size_t groups_off, seqpre_off, bytes;  // byte offsets from the plan base; total
+};
+PlanLayout plan_layout(int32_t S, int32_t T, int32_t G, bool prefill_on, bool cascade_on);
+// Shared-prefix (cascade) decode may run in this call: long enough contexts,
+// a batch small enough for the detection.
+bool cascade_possible(int32_t S, int32_t max_seqlen);
+hipError_t launch_attn_plan(const AttnArgs& a, int32_t rows_cap, bool prefill_on, bool cascade_on,
+                            int32_t* plan, hipStream_t stream);
+// Prefill query tiles and cascade prefix parts (their partials go to ws_pre).
+hipError_t launch_attn_prefill(const AttnArgs& a, int32_t rows_cap, bool prefill_on, bool cascade_on,
+                               const int32_t* plan, float* ws_pre, hipStream_t stream);
 
 }  // namespace pa

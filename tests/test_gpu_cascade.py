@@ -1,0 +1,137 @@
+"""GPU parity of shared-prefix (cascade) decode, and a guard on workspace use.
+
+Sequences whose block tables map the same physical blocks at the same logical
+positions share those blocks' contents ("vLLM 原理" §2.1; the prefix caching
+of "LLM 推理引擎 Continuous Batching 与 PagedAttention" §5).  pa_attention
+finds runs of consecutive single-token decode sequences sharing at least 1024
+tokens from the start, reads each such prefix once for the whole run, and
+merges it with every member's own suffix.  The results must be those of
+plain per-sequence attention (the oracle), whatever the grouping.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import ragged_paged_attention_amd as rpa
+from tests.gpu_path import GpuRun, max_abs_err, tol_for
+from workloads import config, verify_batch
+from workloads.generators import build_workload
+
+pytestmark = pytest.mark.gpu
+
+
+def grouped_batch(seed, segments, Hq, Hkv, dtype="bf16", bs=16):
+    """segments, in batch order: ("group", members, prefix_tokens, tail_lo,
+    tail_hi) -- decode sequences sharing `prefix_tokens` (a multiple of bs)
+    then a private tail of tail_lo..tail_hi tokens -- or ("single", query_len,
+    seq_len) -- a sequence with private blocks only."""
+    rng = np.random.default_rng(seed)
+    ql, sl, shared, plan = [], [], [], []
+    for seg in segments:
+        if seg[0] == "group":
+            _, n, prefix, lo, hi = seg
+            assert prefix % bs == 0
+            first = len(ql)
+            for _ in range(n):
+                ql.append(1)
+                sl.append(prefix + int(rng.integers(lo, hi + 1)))
+            shared.append((list(range(first, first + n)), prefix))
+            plan.append(("group", first, n, prefix))
+        else:
+            _, q, L = seg
+            ql.append(q)
+            sl.append(L)
+            plan.append(("single", len(ql) - 1))
+    need = 0
+    for p in plan:
+        if p[0] == "group":
+            _, first, n, prefix = p
+            need += prefix // bs + sum(-(-sl[k] // bs) - prefix // bs for k in range(first, first + n))
+        else:
+            need += -(-sl[p[1]] // bs)
+    NB = need + 32
+    ids = iter(int(x) for x in rng.permutation(NB))
+    tables = [None] * len(ql)
+    for p in plan:
+        if p[0] == "group":
+            _, first, n, prefix = p
+            pre = [next(ids) for _ in range(prefix // bs)]
+            for k in range(first, first + n):
+                tables[k] = pre + [next(ids) for _ in range(-(-sl[k] // bs) - prefix // bs)]
+        else:
+            tables[p[1]] = [next(ids) for _ in range(-(-sl[p[1]] // bs))]
+    return build_workload("grouped", dtype, Hq, Hkv, 128, bs, NB, ql, sl, tables, seed, rng, shared=shared)
+
+
+# the launch considers cascades only when max_seq_len >= 2048; one long
+# sequence in a batch of shorter ones makes the hint say so
+LONG = ("single", 1, 2100)
+
+CASES = {
+    # three groups of different sizes and prefix lengths (1040 and 1520 are
+    # not whole 64-token tiles: the shared part is rounded down), singles in between
+    "three_groups": dict(Hq=32, Hkv=4, segs=[("group", 5, 2048, 1, 200), ("single", 1, 900),
+                                             ("group", 2, 1040, 1, 40), ("single", 37, 1500),
+                                             ("group", 9, 1520, 30, 300)]),
+    # a run of sharing decodes interrupted by a multi-token sequence
+    "interrupted": dict(Hq=16, Hkv=2, segs=[("group", 3, 1536, 1, 64), ("single", 3, 1600),
+                                            ("group", 4, 1536, 1, 64), LONG]),
+    # G = 1: at most 128 members per group, so 150 sharing sequences make two groups
+    "g1_many_members": dict(Hq=4, Hkv=4, segs=[("group", 150, 1024, 1, 50), LONG]),
+    # more groups than prefix slots: the first 64 groups are cascaded, the rest not
+    "seventy_pairs": dict(Hq=16, Hkv=2, segs=[("group", 2, 1024, 1, 20)] * 70 + [LONG]),
+    # just under the 1024-token threshold (no cascade) next to exactly 1024
+    "threshold": dict(Hq=16, Hkv=2, segs=[("group", 4, 1008, 1, 30), ("single", 1, 50),
+                                          ("group", 4, 1024, 1, 30), LONG]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_cascade_matches_oracle(name):
+    c = CASES[name]
+    w = grouped_batch(len(name), c["segs"], c["Hq"], c["Hkv"])
+    print(f"[cascade] {name} {w.summary()}", flush=True)
+    g = GpuRun(w).run()
+    _, _, _, ref = oracle.run_step(w)
+    assert g.err() == 0
+    err = max_abs_err(g.out, ref)
+    print(f"[cascade] {name} max_abs_err={err:.3e}", flush=True)
+    assert err <= tol_for(w.dtype)
+
+
+def test_cascade_fp16_and_generic_agree():
+    w = grouped_batch(11, [("group", 6, 2048, 1, 100), ("single", 1, 3000)], 32, 4, dtype="f16")
+    g = GpuRun(w).run()
+    _, _, _, ref = oracle.run_step(w)
+    assert max_abs_err(g.out, ref) <= tol_for("f16")
+    prev = rpa.pa_set_kernel_policy(rpa.PA_POLICY_GENERIC)
+    try:
+        g2 = GpuRun(w).run()
+    finally:
+        rpa.pa_set_kernel_policy(prev)
+    assert max_abs_err(g.out, g2.out.to(torch.float64).cpu().numpy()) <= tol_for("f16")
+
+
+@pytest.mark.parametrize("make", [lambda: config(2, scale_down=2), lambda: config(4, scale_down=8),
+                                  lambda: config(5, scale_down=4), lambda: verify_batch(scale_down=4),
+                                  lambda: grouped_batch(3, [("group", 5, 2048, 1, 200)], 32, 4)],
+                         ids=["ragged_prefill", "chunked_mixed", "shared_prefix", "verify", "grouped"])
+def test_workspace_writes_stay_inside_reported_size(make):
+    """Every workspace byte pa_attention touches lies below
+    pa_attention_workspace_size(): a guard region right after it keeps its
+    pattern."""
+    w = make()
+    g = GpuRun(w).fill_history().write_step_rows()
+    need = rpa.pa_attention_workspace_size(w.num_seqs, w.num_tokens, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                                           max(1, w.max_query_len), max(1, w.max_seq_len))
+    guard = 1 << 16
+    buf = torch.full((need + guard,), 0xA5, dtype=torch.uint8, device="cuda")
+    print(f"[cascade] guard {w.name} need={need}", flush=True)
+    out = rpa.pa_attention(g.db.q, g.k_cache, g.v_cache, g.db.block_tables, g.meta["query_start_loc"],
+                           g.db.seq_lens, max(1, w.max_query_len), max(1, w.max_seq_len), w.scale,
+                           workspace=buf[:max(need, 1)])
+    torch.cuda.synchronize()
+    assert bool((buf[need:] == 0xA5).all())
+    _, _, _, ref = oracle.run_step(w, rows=[0, w.num_tokens - 1])
+    assert max_abs_err(out[[0, w.num_tokens - 1]], ref) <= tol_for(w.dtype)
