@@ -264,13 +264,18 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(PlanArgs a) {
   __syncthreads();
   const int32_t ng = n_groups;
 
-  // histogram of weights
+  // Histogram by the weight of each sequence's heaviest query tile (its
+  // last) and of each group's prefix parts.  A sequence's query tiles stay
+  // together in the list, heaviest first, so the tiles of one (sequence, KV
+  // head), which read the same K/V, run side by side on one XCD and share it
+  // through L2 (sorting single tiles by weight mixed sequences and doubled the
+  // mixed batch's HBM reads); the order stays longest-first by sequence.
   if (a.prefill_on) {
     for (int32_t s = tid; s < a.S; s += kPlanThreads) {
       const int32_t qlen = a.qsl[s + 1] - a.qsl[s];
       if (qlen <= 0 || qlen > a.T || qlen * a.G <= a.rows_cap) continue;
-      const int32_t rows = qlen * a.G, L = a.seq_lens[s];
-      for (int32_t qt = 0; qt * kRowsPerWG < rows; ++qt) atomicAdd(&hist[plan_weight(L, qlen, rows, a.G, qt)], 1);
+      const int32_t rows = qlen * a.G, L = a.seq_lens[s], nq = ceil_div(rows, kRowsPerWG);
+      atomicAdd(&hist[plan_weight(L, qlen, rows, a.G, nq - 1)], nq);
     }
   }
   for (int32_t gi = tid; gi < ng; gi += kPlanThreads) {
@@ -310,21 +315,16 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(PlanArgs a) {
     for (int32_t s = tid; s < a.S; s += kPlanThreads) {
       const int32_t qlen = a.qsl[s + 1] - a.qsl[s];
       if (qlen <= 0 || qlen > a.T || qlen * a.G <= a.rows_cap) continue;
-      const int32_t rows = qlen * a.G, L = a.seq_lens[s];
-      for (int32_t qt = 0; qt * kRowsPerWG < rows; ++qt) {
-        const int32_t pos = atomicAdd(&cursor[plan_weight(L, qlen, rows, a.G, qt)], 1);
-        if (pos < a.cap_entries) entries[pos] = make_int2(s, qt);
-      }
+      const int32_t rows = qlen * a.G, L = a.seq_lens[s], nq = ceil_div(rows, kRowsPerWG);
+      const int32_t pos = atomicAdd(&cursor[plan_weight(L, qlen, rows, a.G, nq - 1)], nq);
+      for (int32_t k = 0; k < nq && pos + k < a.cap_entries; ++k) entries[pos + k] = make_int2(s, nq - 1 - k);
     }
   }
   for (int32_t gi = tid; gi < ng; gi += kPlanThreads) {
     const int4 gr = a.groups[gi];
     const int32_t parts = gr.w & 255;
-    const int32_t w = min(ceil_div(gr.z / kTile, parts), kPlanBuckets - 1);
-    for (int32_t pp = 0; pp < parts; ++pp) {
-      const int32_t pos = atomicAdd(&cursor[w], 1);
-      if (pos < a.cap_entries) entries[pos] = make_int2(-(gi + 1), pp);
-    }
+    const int32_t pos = atomicAdd(&cursor[min(ceil_div(gr.z / kTile, parts), kPlanBuckets - 1)], parts);
+    for (int32_t pp = 0; pp < parts && pos + pp < a.cap_entries; ++pp) entries[pos + pp] = make_int2(-(gi + 1), pp);
   }
 }
 
