@@ -33,6 +33,13 @@ FLAGS = [
 ]
 
 
+# Per-source additions.  The prefill kernel never reads or produces a NaN
+# (tile rows past a context re-read its last valid row; masked scores are
+# -inf), so its row maxima need no NaN quieting: without it each fmaxf of an
+# MFMA result costs one instruction instead of three.
+FILE_FLAGS = {"attn_prefill.hip": ["-fno-honor-nans"]}
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -43,7 +50,7 @@ def hipcc() -> str:
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else ["-x", "hip"]
-    cmd = [hipcc()] + FLAGS + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + FLAGS + FILE_FLAGS.get(src, []) + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -52,7 +52,10 @@ constexpr int kRowBytes = 256;                     // one token row of one head 
 constexpr int kTileBytes = kTile * kRowBytes;      // 16 KB per K or V tile
 constexpr int kStageBytes = 2 * kTileBytes;        // K tile then V tile
 constexpr float kRescaleSlack = 8.f;               // log2 units the running max may lag
-constexpr int kQtRun = 4;                          // query tiles of one (sequence, head) per XCD run
+#ifndef PA_PREFILL_QT_RUN
+#define PA_PREFILL_QT_RUN 4
+#endif
+constexpr int kQtRun = PA_PREFILL_QT_RUN;           // query tiles of one (sequence, head) per XCD run
 
 struct PrefillArgs {
   const uint16_t* q;
@@ -423,12 +426,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
   // Byte offsets of this lane's K and V sources from the first slot of the
   // wave's rows; the same for every tile whose rows are all inside the context.
   // (at most 15 slot rows of Hkv x 256 bytes: fits 32 bits for any Hkv the
-  // grid allows)
-  int32_t k_src_off[kDmaInst], v_src_off[kDmaInst];
+  // grid allows).  Unsigned, so a DMA address is a scalar base plus a
+  // zero-extended lane offset, which the instruction takes as is.
+  uint32_t k_src_off[kDmaInst], v_src_off[kDmaInst];
 #pragma unroll
   for (int u = 0; u < kDmaInst; ++u) {
     const int row = row_base + 4 * u + grp;
-    const int32_t rowoff = (row & 15) * a.Hkv * kRowBytes;
+    const uint32_t rowoff = static_cast<uint32_t>((row & 15) * a.Hkv * kRowBytes);
     k_src_off[u] = rowoff + 16 * (r ^ (row & 15));
     v_src_off[u] = rowoff + 16 * (r ^ ((row & 7) << 1));
   }
