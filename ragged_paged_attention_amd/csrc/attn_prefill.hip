@@ -86,6 +86,11 @@ struct PlanArgs {
   int4* seq_prefix;
 };
 
+// KV heads per run slot of the prefill item order: 4 when they divide Hkv.
+__host__ __device__ __forceinline__ int32_t prefill_head_group(int32_t Hkv) {
+  return (Hkv & 3) == 0 ? 4 : ((Hkv & 1) == 0 ? 2 : 1);
+}
+
 // K/V tiles query tile qt of a sequence reads (its last row's causal limit).
 __device__ __forceinline__ int32_t plan_weight(int32_t L, int32_t qlen, int32_t rows, int32_t G, int32_t qt) {
   if (L < qlen) return 1;  // invalid: the kernel only writes zeros
@@ -356,17 +361,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
   const int lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, grp = lane >> 4;
 
-  // Items: (block of kQtRun list entries, heaviest first; KV head; entry in
-  // block).  Workgroup b runs on XCD b % 8 and runs of kQtRun consecutive
-  // items stay on one XCD: neighbouring entries of similar weight are often
-  // query tiles of the same sequence, which share every K/V tile through that
-  // XCD's L2.  The k-th run an XCD takes is run 8k + ((xcd + k) mod 8).
+  // Items.  Workgroup b runs on XCD b % 8, and an XCD hands its workgroups
+  // in order, round-robin, to its 4 shader engines, each waiting for a free
+  // slot on its own engine.  A run is kQtRun consecutive list entries (often
+  // query tiles of one sequence, which share every K/V tile through the XCD's
+  // L2) times a group of hg KV heads, ordered entry-major: consecutive
+  // workgroups are the same entry for different heads, equal in weight, so
+  // the engines stay evenly loaded (entry-minor order gave one engine every
+  // block's heaviest tile and stalled the others behind it).  The k-th run an
+  // XCD takes is run 8k + ((xcd + k) mod 8); runs go by (entry block, head
+  // group), heaviest first.
   const int32_t bid = blockIdx.x;
+  const int32_t hg = prefill_head_group(a.Hkv), run_len = kQtRun * hg;
   const int32_t xcd = bid & 7, jj = bid >> 3;
-  const int32_t kr = jj / kQtRun;
-  const int32_t item = (kr * 8 + ((xcd + kr) & 7)) * kQtRun + (jj % kQtRun);
-  const int32_t g = (item / kQtRun) % a.Hkv;
-  const int32_t e = (item / kQtRun / a.Hkv) * kQtRun + item % kQtRun;
+  const int32_t kr = jj / run_len, within = jj - kr * run_len;
+  const int32_t run = kr * 8 + ((xcd + kr) & 7);
+  const int32_t n_hg = a.Hkv / hg;
+  const int32_t e = (run / n_hg) * kQtRun + within / hg;
+  const int32_t g = (run % n_hg) * hg + within % hg;
   if (e >= a.plan[0]) return;
   const int2 ent = reinterpret_cast<const int2*>(a.plan + kPlanHeader)[e];
   // A prefill entry is one query tile of sequence s.  A cascade entry is one
@@ -766,7 +778,8 @@ hipError_t launch_attn_prefill(const AttnArgs& a, int32_t rows_cap, bool prefill
   p.ws_pre = ws_pre;
   const int64_t n_eb = (static_cast<int64_t>(l.cap_entries) + kQtRun - 1) / kQtRun;
   const int64_t items_raw = n_eb * kQtRun * a.Hkv;
-  const int64_t items = (items_raw + 8 * kQtRun - 1) / (8 * kQtRun) * (8 * kQtRun);
+  const int64_t run_len = static_cast<int64_t>(kQtRun) * prefill_head_group(a.Hkv);
+  const int64_t items = (items_raw + 8 * run_len - 1) / (8 * run_len) * (8 * run_len);
   if (items > INT32_MAX) return hipErrorInvalidValue;
   if (items == 0) return hipSuccess;
   launch_mark("prefill_kernel", stream);
