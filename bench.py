@@ -40,10 +40,10 @@ METRIC = "decode KV-read GB/s (% HBM peak) + mixed-batch attn tokens/s, 1 MI355X
 PROFILES = os.path.join(ROOT, "profiles")
 # name fragment that identifies each kernel in rocprofv3 output (bf16 instances)
 KERNEL_MATCH = {
-    "decode_kernel": "decode_kernel<pa::BF16, 1>",
-    "decode_kernel_2t": "decode_kernel<pa::BF16, 2>",
-    "merge_kernel": "merge_kernel<pa::BF16>",
-    "prefill_kernel": "prefill_kernel<pa::BF16>",
+    "decode_kernel": "decode_kernel<pa::BF16, 1, 128, true>",
+    "decode_kernel_2t": "decode_kernel<pa::BF16, 2, 128, true>",
+    "merge_kernel": "merge_kernel<pa::BF16, 128>",
+    "prefill_kernel": "prefill_kernel<pa::BF16, true>",
     "write_kv_kernel": "write_kv_kernel",
     "copy_blocks_kernel": "copy_blocks_kernel",
 }
@@ -63,7 +63,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["step", "decode", "prefill", "shared", "verify", "blocks"], default=None,
+    ap.add_argument("--only", choices=["step", "decode", "prefill", "shared", "verify", "blocks", "variants"],
+                    default=None,
                     help="run one leg only (for profiling)")
     ap.add_argument("--cpu-sample-rows", type=int, default=2048)
     ap.add_argument("--summarize-trace", nargs=2, metavar=("ROCPROF_DIR", "OUT_MD"),
@@ -310,7 +311,7 @@ def main():
 
     import ragged_paged_attention_amd as rpa
     from ragged_paged_attention_amd.step import forward_step
-    from workloads import accounting, config, verify_batch
+    from workloads import accounting, config, decode_variant, verify_batch
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     timer = Timer(torch)
@@ -394,6 +395,32 @@ def main():
             result["roofline"] = roofline_for("decode_kernel", kern3["decode_kernel"][1], w3, w3.name)
         del g3, ws3, out3
         torch.cuda.empty_cache()
+
+    # ---------------- head-dim and block-size variants of the decode batch ----------------
+    if args.only in (None, "variants"):
+        res = {}
+        for D, bs in ((64, 16), (256, 16), (128, 8)):
+            wv = decode_variant(D, bs, poison=False)
+            gv = setup(wv, torch).write_step_rows()
+            db = gv.db
+            wsv = workspace_for(wv, rpa, torch)
+            outv = torch.empty_like(db.q)
+            qslv = gv.meta["query_start_loc"]
+            attnv = lambda: rpa.pa_attention(db.q, gv.k_cache, gv.v_cache, db.block_tables, qslv, db.seq_lens,
+                                             wv.max_query_len, wv.max_seq_len, wv.scale, out=outv, workspace=wsv)
+            msv = timer.time(attnv, max(args.steps, 20), args.warmup)
+            kernv = timer.kernels(rpa, attnv, 10)
+            kvv = accounting.kv_read_bytes(wv.step.seq_lens, wv.num_kv_heads, wv.head_dim, wv.dtype)
+            res[f"D{D}_bs{bs}"] = {
+                "GBps": kvv / (msv / 1e3) / 1e9, "frac_hbm_peak": kvv / (msv / 1e3) / 1e9 / HBM_PEAK_GBS,
+                "kv_bytes": kvv, "ms_per_call": msv,
+                "decode_kernel_GBps": kvv / (kernv["decode_kernel"][1] / 1e3) / 1e9,
+                "kernels_ms": {k: round(avg, 5) for k, (n, avg) in kernv.items()}}
+            del gv, wsv, outv
+            torch.cuda.empty_cache()
+        result["decode_variants"] = {
+            "workload": "decode batch: 100 seqs x 2001 tokens, 32/32 heads, bf16, at head_dim/block_size "
+                        "64/16, 256/16 and 128/8", **res}
 
     # ---------------- shared-prefix long-context decode ----------------
     if args.only in (None, "shared"):

@@ -1,5 +1,8 @@
-// MFMA fast paths for pa_attention: bf16/f16 storage, head_dim 128, block
-// size a multiple of 16 (so every 16-token chunk lies inside one block).
+// MFMA fast paths for pa_attention: bf16/f16 storage; the decode kernel takes
+// head_dim 64, 128 or 256 and a block size that is a multiple of 16 (a
+// 16-token chunk lies inside one block) or divides 16 (each lane finds its
+// own token's block); query tiles of longer chunks go to the prefill kernel
+// (head_dim 128) or, for the other head dims, to the generic kernel.
 //
 // What is computed is the same as the generic kernel: for each new row of a
 // sequence, causal softmax attention over its own cached K/V read through its
@@ -15,12 +18,12 @@
 // columns of one or two 16-column MFMA tiles (NT = 1 for up to 16 rows, NT = 2
 // for 17..32: a verify step of a few draft tokens), so every K/V byte is read
 // once per (s, g) whatever the row count:
-//   S^T[16 tok][16 rows] = K[16 tok][128] . Q^T[128][16 rows]
-//       4 x v_mfma_f32_16x16x32 (A = K rows straight from HBM, 16 B per lane)
-//   O^T[128][16 rows]   += V^T[128][16 tok] . P^T[16 tok][16 rows]
-//       8 x v_mfma_f32_16x16x16 (B = P^T is exactly the S^T accumulator
-//       layout, so P never moves; A = V^T comes from a V tile staged in LDS
-//       and read back transposed with ds_read_b64_tr_b16).
+//   S^T[16 tok][16 rows] = K[16 tok][D] . Q^T[D][16 rows]
+//       D/32 x v_mfma_f32_16x16x32 (A = K rows straight from HBM, 16 B per lane)
+//   O^T[D][16 rows]     += V^T[D][32 tok] . P^T[32 tok][16 rows]
+//       D/16 x v_mfma_f32_16x16x32 per 32 tokens (B = P^T is exactly the S^T
+//       accumulator layout, so P never moves; A = V^T comes from a V tile
+//       staged in LDS and read back transposed with ds_read_b64_tr_b16).
 // The chunk loop keeps the next chunk's K and V loads in flight while the
 // current chunk computes.  Block ids of the part are fetched 64 at a time into
 // one VGPR and picked per chunk with readlane.  Work items are remapped so
@@ -81,11 +84,27 @@ struct DecodeArgs {
 // 16 (NT - 1) < rows <= 16 NT.  The one-tile instance also checks the
 // max_query_len hint and zero-fills the rows of items no kernel of this call
 // covers (rows above rows_cap while the prefill kernel does not run).
-template <class F, int NT>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 3 : 2, 8))) void decode_kernel(
+// D = head_dim (64, 128, 256).  kBlk16: the block size is a multiple of 16;
+// otherwise it divides 16 and each lane looks up its own token's block.
+// Waves per SIMD the register budget is set for: the pair-buffered K/V
+// fragments and the O accumulators of head_dim 256 need about twice the
+// registers (and head_dim 256 items take one row tile only).
+template <int NT, int D>
+constexpr int decode_min_waves() {
+  return D == 256 ? 1 : (NT == 1 ? 3 : 2);
+}
+
+template <class F, int NT, int D, bool kBlk16>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(decode_min_waves<NT, D>(), 8))) void decode_kernel(
     DecodeArgs a) {
   using M = Mma<F>;
-  __shared__ __attribute__((aligned(16))) uint8_t vlds[2 * kChunk * kVRowBytes];
+  constexpr int kKK = D / 32;       // 16x16x32 K steps of QK; also V loads per 16-row chunk
+  constexpr int kDT = D / 16;       // 16-wide output tiles of PV
+  constexpr int kVRow = 2 * D + 32;  // LDS row pitch of the staged V tile (32 B of padding)
+  constexpr int kLpr = D / 8;       // lanes per V row in a load (16 B each)
+  constexpr int kRpi = 64 / kLpr;   // V rows per load instruction
+  constexpr int kPF = D + 4;        // floats of one partial row: O[D], m, l, pad
+  __shared__ __attribute__((aligned(16))) uint8_t vlds[2 * kChunk * kVRow];
   const int lane = threadIdx.x;
   const int r = lane & 15;    // MFMA column = query row of the item (within its tile)
   const int grp = lane >> 4;  // 16-lane group
@@ -137,10 +156,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 3 
   if (NT == 1 && part == 0) {
     if (qlen > a.max_q && g == 0 && lane == 0) flag(a.d_err, PA_DERR_HINT);
     if (rows > a.rows_cap && !a.prefill_on) {  // not covered by this call: zeros
-      for (int32_t idx = lane; idx < rows * (kD / 4); idx += 64) {
-        const int32_t rr = idx / (kD / 4), d4 = idx - rr * (kD / 4);
+      for (int32_t idx = lane; idx < rows * (D / 4); idx += 64) {
+        const int32_t rr = idx / (D / 4), d4 = idx - rr * (D / 4);
         const int32_t tt = q0 + rr / a.G, hh = g * a.G + rr % a.G;
-        *reinterpret_cast<uint2*>(a.out + (static_cast<int64_t>(tt) * a.Hq + hh) * kD + 4 * d4) = make_uint2(0, 0);
+        *reinterpret_cast<uint2*>(a.out + (static_cast<int64_t>(tt) * a.Hq + hh) * D + 4 * d4) = make_uint2(0, 0);
       }
       return;
     }
@@ -157,7 +176,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 3 
     const int32_t i_row = rt_row[rt] / a.G;
     const int32_t hg = rt_row[rt] - i_row * a.G;
     rvalid[rt] = rt_row[rt] < rows;
-    orow[rt] = a.out + (static_cast<int64_t>(q0 + i_row) * a.Hq + g * a.G + hg) * kD;
+    orow[rt] = a.out + (static_cast<int64_t>(q0 + i_row) * a.Hq + g * a.G + hg) * D;
     qpos[rt] = rvalid[rt] ? L - qlen + i_row : -1;  // last visible position of this row
   }
 
@@ -167,7 +186,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 3 
 #pragma unroll
       for (int rt = 0; rt < NT; ++rt)
         if (rvalid[rt])
-          for (int d = 4 * grp; d < kD; d += 16) *reinterpret_cast<uint2*>(orow[rt] + d) = make_uint2(0, 0);
+          for (int d = 4 * grp; d < D; d += 16) *reinterpret_cast<uint2*>(orow[rt] + d) = make_uint2(0, 0);
     }
     return;
   }
@@ -190,37 +209,50 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 3 
 
   // Q^T fragments (B operand): lane holds Q[row][32kk + 8grp .. +8] of its
   // row in each tile (the q row sits at the same offset as the output row)
-  uint4 qf[NT][4];
+  uint4 qf[NT][kKK];
 #pragma unroll
   for (int rt = 0; rt < NT; ++rt) {
     const uint16_t* qrow = a.q + (orow[rt] - a.out) + 8 * grp;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) qf[rt][kk] = rvalid[rt] ? ld16(qrow + 32 * kk) : make_uint4(0, 0, 0, 0);
+    for (int kk = 0; kk < kKK; ++kk) qf[rt][kk] = rvalid[rt] ? ld16(qrow + 32 * kk) : make_uint4(0, 0, 0, 0);
   }
 
-  const int64_t slot_stride = static_cast<int64_t>(a.Hkv) * kD;  // elements between slots
-  const uint16_t* kbase = a.k_cache + static_cast<int64_t>(g) * kD;
-  const uint16_t* vbase = a.v_cache + static_cast<int64_t>(g) * kD;
+  const int64_t slot_stride = static_cast<int64_t>(a.Hkv) * D;  // elements between slots
+  const uint16_t* kbase = a.k_cache + static_cast<int64_t>(g) * D;
+  const uint16_t* vbase = a.v_cache + static_cast<int64_t>(g) * D;
   const int32_t* btrow = a.block_tables + static_cast<int64_t>(s) * a.MB;
-  const int32_t cpb = a.bs / kChunk;  // chunks per block
   const int32_t nblk = ceil_div(L, a.bs);
 
   // block ids of 64 consecutive logical blocks, one per lane
   int32_t ids_base = -(1 << 30);
   int32_t ids = 0;
-  auto slot_of_chunk = [&](int32_t c) -> int64_t {
-    const int32_t lb = c / cpb;
-    if (lb - ids_base >= 64 || lb < ids_base) {
-      ids_base = lb;
-      int32_t v = (lb + lane < nblk) ? btrow[lb + lane] : 0;
-      if (v < 0 || v >= a.NB) {
-        flag(a.d_err, PA_DERR_BLOCK_OOB);
-        v = 0;
-      }
-      ids = v;
+  auto fetch_ids = [&](int32_t lb) {  // wave-uniform lb
+    ids_base = lb;
+    int32_t v = (lb + lane < nblk) ? btrow[lb + lane] : 0;
+    if (v < 0 || v >= a.NB) {
+      flag(a.d_err, PA_DERR_BLOCK_OOB);
+      v = 0;
     }
+    ids = v;
+  };
+  // kBlk16: first slot of 16-token chunk c (the chunk lies in one block)
+  auto slot_of_chunk = [&](int32_t c) -> int64_t {
+    const int32_t cpb = a.bs / kChunk;  // chunks per block
+    const int32_t lb = c / cpb;
+    if (lb - ids_base >= 64 || lb < ids_base) fetch_ids(lb);
     const int32_t b = __builtin_amdgcn_readlane(ids, lb - ids_base);
     return static_cast<int64_t>(b) * a.bs + (c - lb * cpb) * kChunk;
+  };
+  // !kBlk16: make the id window cover chunks c, c + 1 (32 tokens, at most 32
+  // blocks), then each lane's slot of token t of that range
+  auto window_for = [&](int32_t c) {
+    const int32_t lb0 = (c * kChunk) / a.bs, lb1 = (c * kChunk + 2 * kChunk - 1) / a.bs;
+    if (lb0 < ids_base || lb1 - ids_base >= 64) fetch_ids(lb0);
+  };
+  auto slot_of_token = [&](int32_t t) -> int64_t {
+    const int32_t lb = t / a.bs;
+    const int32_t b = __shfl(ids, lb - ids_base, 64);
+    return static_cast<int64_t>(b) * a.bs + (t - lb * a.bs);
   };
 
   // Chunks are taken two at a time (32 tokens, 16 KB of K+V per wave in
@@ -228,39 +260,48 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 3 
   // as soon as the QK MFMAs have read the current K, the next V loads as soon
   // as the current V is in LDS.  A pair's second chunk may lie past the part
   // (odd chunk counts): it is then neither loaded nor counted.
-  uint4 kf[2][4], vf[2][4];
+  uint4 kf[2][kKK], vf[2][kKK];
   // K/V read once are streamed past the caches (6.0 vs 5.6 TB/s measured on
   // the decode batch).  A part whose first block is also mapped by a
   // neighbouring sequence (a shared prefix) keeps cacheable loads, so the
   // sequences sharing it hit in L2.
   bool stream = true;
   {
-    const int32_t lb0 = c0 / cpb;
+    const int32_t lb0 = (c0 * kChunk) / a.bs;
     const int32_t mine = btrow[lb0];
     bool shared = false;
     if (s > 0) shared |= a.block_tables[static_cast<int64_t>(s - 1) * a.MB + lb0] == mine;
     if (s + 1 < a.S) shared |= a.block_tables[static_cast<int64_t>(s + 1) * a.MB + lb0] == mine;
     stream = !shared;
   }
+  // K: lane holds row r of the chunk, columns 32 kk + 8 grp .. + 8.  V: load
+  // r4 brings rows kRpi r4 + vrow, columns 8 vcol .. + 8.
+  const int vrow = lane / kLpr, vcol = lane % kLpr;
   auto load_pair = [&](int32_t c, bool do_k, bool do_v) {
+    if (!kBlk16) window_for(c);
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
       if (c + h2 < c1) {
-        const int64_t slot0 = slot_of_chunk(c + h2);
+        const int32_t tok = (c + h2) * kChunk;
+        const int64_t slot0 = kBlk16 ? slot_of_chunk(c + h2) : 0;
         if (do_k) {
-          const uint16_t* kp = kbase + (slot0 + r) * slot_stride + 8 * grp;
+          const int64_t sl = kBlk16 ? slot0 + r : slot_of_token(tok + r);
+          const uint16_t* kp = kbase + sl * slot_stride + 8 * grp;
 #pragma unroll
-          for (int kk = 0; kk < 4; ++kk) kf[h2][kk] = stream ? ld16_nt(kp + 32 * kk) : ld16(kp + 32 * kk);
+          for (int kk = 0; kk < kKK; ++kk) kf[h2][kk] = stream ? ld16_nt(kp + 32 * kk) : ld16(kp + 32 * kk);
         }
         if (do_v) {
-          const uint16_t* vp = vbase + (slot0 + grp) * slot_stride + 8 * r;
 #pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4)
-            vf[h2][r4] = stream ? ld16_nt(vp + 4 * r4 * slot_stride) : ld16(vp + 4 * r4 * slot_stride);
+          for (int r4 = 0; r4 < kKK; ++r4) {
+            const int32_t row = kRpi * r4 + vrow;
+            const int64_t sl = kBlk16 ? slot0 + row : slot_of_token(tok + row);
+            const uint16_t* vp = vbase + sl * slot_stride + 8 * vcol;
+            vf[h2][r4] = stream ? ld16_nt(vp) : ld16(vp);
+          }
         }
       } else {
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
+        for (int x = 0; x < kKK; ++x) {
           if (do_k) kf[h2][x] = make_uint4(0, 0, 0, 0);
           if (do_v) vf[h2][x] = make_uint4(0, 0, 0, 0);
         }
@@ -269,17 +310,17 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 3 
   };
 
   float m[NT], lsum[NT];
-  f32x4_t o[NT][8];
+  f32x4_t o[NT][kDT];
 #pragma unroll
   for (int rt = 0; rt < NT; ++rt) {
     m[rt] = -INFINITY;
     lsum[rt] = 0.f;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) o[rt][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int dt = 0; dt < kDT; ++dt) o[rt][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
   load_pair(c0, true, true);
-  const int rd_off = (4 * grp + (r >> 2)) * kVRowBytes + 8 * (r & 3);
+  const int rd_off = (4 * grp + (r >> 2)) * kVRow + 8 * (r & 3);
   for (int32_t c = c0; c < c1; c += 2) {
     const int32_t tok0 = c * kChunk;
     const bool more = c + 2 < c1;
@@ -289,7 +330,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 3 
 #pragma unroll
     for (int rt = 0; rt < NT; ++rt) st[rt][0] = st[rt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
+    for (int kk = 0; kk < kKK; ++kk)
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
@@ -303,14 +344,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 3 
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4)
-          if (tok0 + 16 * h2 + 4 * r4 + grp >= tok_end) vf[h2][r4] = make_uint4(0, 0, 0, 0);
+        for (int r4 = 0; r4 < kKK; ++r4)
+          if (tok0 + 16 * h2 + kRpi * r4 + vrow >= tok_end) vf[h2][r4] = make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4)
-        *reinterpret_cast<uint4*>(vlds + (16 * h2 + 4 * r4 + grp) * kVRowBytes + 16 * r) = vf[h2][r4];
+      for (int r4 = 0; r4 < kKK; ++r4)
+        *reinterpret_cast<uint4*>(vlds + (16 * h2 + kRpi * r4 + vrow) * kVRow + 16 * vcol) = vf[h2][r4];
     __asm__ volatile("" ::: "memory");
     if (more) load_pair(c + 2, false, true);
 
@@ -348,7 +389,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 3 
                  (((p[0][0] + p[0][1]) + (p[0][2] + p[0][3])) + ((p[1][0] + p[1][1]) + (p[1][2] + p[1][3])));
       if (__any(alpha != 1.f)) {  // wave-uniform: skip the rescale when no row's max moved
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) o[rt][dt] *= alpha;
+        for (int dt = 0; dt < kDT; ++dt) o[rt][dt] *= alpha;
       }
       // B = P^T for 32 tokens: k = 8grp + j holds token 4grp + j (j < 4) and
       // 16 + 4grp + (j - 4); A = V^T uses the same token order.
@@ -356,9 +397,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 3 
                           M::pk(p[1][2], p[1][3]));
     }
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
+    for (int dt = 0; dt < kDT; ++dt) {
       const i16x4_t lo = lds_read_tr16(vlds + rd_off + 32 * dt);
-      const i16x4_t hi = lds_read_tr16(vlds + rd_off + 16 * kVRowBytes + 32 * dt);
+      const i16x4_t hi = lds_read_tr16(vlds + rd_off + 16 * kVRow + 32 * dt);
       const uint4 va = __builtin_bit_cast(uint4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
       for (int rt = 0; rt < NT; ++rt) o[rt][dt] = M::qk(va, pb[rt], o[rt][dt]);
@@ -373,7 +414,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 3 
     if (np == 1 && npp == 0) {
       const float inv = ls > 0.f ? 1.f / ls : 0.f;
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
+      for (int dt = 0; dt < kDT; ++dt) {
         uint2 w;
         w.x = static_cast<uint32_t>(M::cvt(o[rt][dt][0] * inv)) |
               (static_cast<uint32_t>(M::cvt(o[rt][dt][1] * inv)) << 16);
@@ -382,15 +423,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 3 
         *reinterpret_cast<uint2*>(orow[rt] + 16 * dt + 4 * grp) = w;
       }
     } else {
-      float* e = a.ws + ((static_cast<int64_t>(s) * a.Hkv + g) * a.P + part) * (a.rows_cap * kPartFloats) +
-                 rt_row[rt] * kPartFloats;
+      float* e = a.ws + ((static_cast<int64_t>(s) * a.Hkv + g) * a.P + part) * (a.rows_cap * kPF) +
+                 rt_row[rt] * kPF;
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt)
+      for (int dt = 0; dt < kDT; ++dt)
         *reinterpret_cast<float4*>(e + 16 * dt + 4 * grp) =
             make_float4(o[rt][dt][0], o[rt][dt][1], o[rt][dt][2], o[rt][dt][3]);
       if (grp == 0) {
-        e[kD] = m[rt];
-        e[kD + 1] = ls;
+        e[D] = m[rt];
+        e[D + 1] = ls;
       }
     }
   }
@@ -404,9 +445,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 3 
 // of one row from float4 partial loads, several parts in flight at once.
 constexpr int kMergeRows = 8;  // rows per merge workgroup (256 threads = 8 rows x 32 float4)
 
-template <class F>
+template <class F, int D>
 __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
   constexpr int kMaxMerge = kMaxParts + kCascadeMaxParts;  // decode parts + cascade prefix parts
+  constexpr int kPF = D + 4;  // floats of one decode partial row
   __shared__ float wts[kMergeRows][kMaxMerge];
   __shared__ float inv_den[kMergeRows];
   const int32_t s = blockIdx.x, g = blockIdx.y;
@@ -429,12 +471,13 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
   plan_parts(ceil_div(L, kChunk) - pre / kChunk, a.P, &np, &cpp);
   if (np == 1 && npp == 0) return;  // written directly by the decode kernel
   const int32_t ntot = np + npp;
-  const int32_t stride = a.rows_cap * kPartFloats;  // one decode part's partials
+  const int32_t stride = a.rows_cap * kPF;  // one decode part's partials
   const float* base = a.ws + (static_cast<int64_t>(s) * a.Hkv + g) * a.P * stride;
   // partial row r of the k-th part: decode parts 0..np-1, then the group's
-  // prefix parts (slot pslot + j, this sequence's rows from prow)
+  // prefix parts (slot pslot + j, this sequence's rows from prow; head_dim
+  // 128 only)
   auto part_row = [&](int32_t k, int32_t r) -> const float* {
-    return k < np ? base + k * stride + r * kPartFloats
+    return k < np ? base + k * stride + r * kPF
                   : a.ws_pre + ((static_cast<int64_t>(pslot + k - np) * a.Hkv + g) * kCascadeRows + prow + r) *
                                    kPartFloats;
   };
@@ -449,8 +492,8 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
     for (int c = 0; c < 2; ++c) {
       const int32_t k = 64 * c + lane;
       const float* e = k < ntot ? part_row(k, r) : nullptr;
-      mp[c] = k < ntot ? e[kD] : -INFINITY;
-      lp[c] = k < ntot ? e[kD + 1] : 0.f;
+      mp[c] = k < ntot ? e[D] : -INFINITY;
+      lp[c] = k < ntot ? e[D + 1] : 0.f;
       mm = fmaxf(mm, mp[c]);
     }
     mm = wave_max(mm);
@@ -466,38 +509,41 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
     if (lane == 0) inv_den[rl] = den > 0.f ? 1.f / den : 0.f;
   }
   __syncthreads();
-  const int rl = threadIdx.x >> 5, d4 = threadIdx.x & 31;
+  const int rl = threadIdx.x >> 5;
   const int32_t r = r0 + rl;
   if (r >= rows) return;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  int32_t k = 0;
-  for (; k + 4 <= ntot; k += 4) {
-    float4 v[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const float4*>(part_row(k + u, r) + 4 * d4);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float wu = wts[rl][k + u];
-      acc.x = fmaf(wu, v[u].x, acc.x);
-      acc.y = fmaf(wu, v[u].y, acc.y);
-      acc.z = fmaf(wu, v[u].z, acc.z);
-      acc.w = fmaf(wu, v[u].w, acc.w);
-    }
-  }
-  for (; k < ntot; ++k) {
-    const float4 v = *reinterpret_cast<const float4*>(part_row(k, r) + 4 * d4);
-    const float wu = wts[rl][k];
-    acc.x = fmaf(wu, v.x, acc.x);
-    acc.y = fmaf(wu, v.y, acc.y);
-    acc.z = fmaf(wu, v.z, acc.z);
-    acc.w = fmaf(wu, v.w, acc.w);
-  }
   const float inv = inv_den[rl];
   const int32_t i_row = r / a.G, hg = r - i_row * a.G;
-  uint2 o;
-  o.x = static_cast<uint32_t>(Mma<F>::cvt(acc.x * inv)) | (static_cast<uint32_t>(Mma<F>::cvt(acc.y * inv)) << 16);
-  o.y = static_cast<uint32_t>(Mma<F>::cvt(acc.z * inv)) | (static_cast<uint32_t>(Mma<F>::cvt(acc.w * inv)) << 16);
-  *reinterpret_cast<uint2*>(a.out + ((static_cast<int64_t>(q0) + i_row) * a.Hq + g * a.G + hg) * kD + 4 * d4) = o;
+  // 32 threads per row, D / 4 float4 columns
+  for (int d4 = threadIdx.x & 31; d4 < D / 4; d4 += 32) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    int32_t k = 0;
+    for (; k + 4 <= ntot; k += 4) {
+      float4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const float4*>(part_row(k + u, r) + 4 * d4);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float wu = wts[rl][k + u];
+        acc.x = fmaf(wu, v[u].x, acc.x);
+        acc.y = fmaf(wu, v[u].y, acc.y);
+        acc.z = fmaf(wu, v[u].z, acc.z);
+        acc.w = fmaf(wu, v[u].w, acc.w);
+      }
+    }
+    for (; k < ntot; ++k) {
+      const float4 v = *reinterpret_cast<const float4*>(part_row(k, r) + 4 * d4);
+      const float wu = wts[rl][k];
+      acc.x = fmaf(wu, v.x, acc.x);
+      acc.y = fmaf(wu, v.y, acc.y);
+      acc.z = fmaf(wu, v.z, acc.z);
+      acc.w = fmaf(wu, v.w, acc.w);
+    }
+    uint2 o;
+    o.x = static_cast<uint32_t>(Mma<F>::cvt(acc.x * inv)) | (static_cast<uint32_t>(Mma<F>::cvt(acc.y * inv)) << 16);
+    o.y = static_cast<uint32_t>(Mma<F>::cvt(acc.z * inv)) | (static_cast<uint32_t>(Mma<F>::cvt(acc.w * inv)) << 16);
+    *reinterpret_cast<uint2*>(a.out + ((static_cast<int64_t>(q0) + i_row) * a.Hq + g * a.G + hg) * D + 4 * d4) = o;
+  }
 }
 
 // Parts per sequence the launch provides for: enough for max_seq_len.  A
@@ -518,56 +564,83 @@ bool fast_path_supported(const AttnArgs& a) {
   const uintptr_t align = reinterpret_cast<uintptr_t>(a.q) | reinterpret_cast<uintptr_t>(a.k_cache) |
                           reinterpret_cast<uintptr_t>(a.v_cache) | reinterpret_cast<uintptr_t>(a.out) |
                           reinterpret_cast<uintptr_t>(a.workspace);
-  return (a.dtype == PA_BF16 || a.dtype == PA_F16) && a.D == kD && a.bs % kChunk == 0 &&
-         a.Hq / a.Hkv <= kTileRows && align % 16 == 0;
+  return (a.dtype == PA_BF16 || a.dtype == PA_F16) && (a.D == 64 || a.D == 128 || a.D == 256) &&
+         (a.bs % kChunk == 0 || kChunk % a.bs == 0) && a.Hq / a.Hkv <= kTileRows && align % 16 == 0;
 }
 
 // Rows of the largest item the decode kernels take in a call: two tiles when
-// the max_query_len hint allows items of more than one tile, else one.
-static int32_t decode_rows_cap(int32_t G, int32_t max_q) {
-  return static_cast<int64_t>(max_q) * G > kTileRows ? kMaxRows : kTileRows;
+// the max_query_len hint allows items of more than one tile (head_dim 256:
+// always one), else one.
+static int32_t decode_rows_cap(int32_t G, int32_t max_q, int32_t D) {
+  return D != 256 && static_cast<int64_t>(max_q) * G > kTileRows ? kMaxRows : kTileRows;
 }
 
 // Work split of one call, from the sizes and hints alone (the same numbers
 // give the workspace size and the launches).
+// prefill_on: rows above rows_cap may come (the prefill kernel takes them at
+// head_dim 128, the generic kernel otherwise); mfma_prefill: the planned
+// MFMA prefill kernel runs (prefill query tiles or cascade prefix parts).
 struct FastPlan {
   int32_t G, P, rows_cap;
-  bool prefill_on, cascade_on;
+  bool prefill_on, cascade_on, mfma_prefill;
   size_t dec_bytes, pre_off, plan_off, bytes;
 };
 
-static FastPlan fast_plan(int32_t S, int32_t T, int32_t Hq, int32_t Hkv, int32_t max_q, int32_t max_seqlen) {
+static FastPlan fast_plan(int32_t S, int32_t T, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_q,
+                          int32_t max_seqlen) {
   FastPlan f;
   f.G = Hq / Hkv;
   f.P = decode_parts(S, Hkv, max_seqlen);
-  f.rows_cap = decode_rows_cap(f.G, max_q);
+  f.rows_cap = decode_rows_cap(f.G, max_q, D);
   f.prefill_on = static_cast<int64_t>(max_q) * f.G > f.rows_cap;
-  f.cascade_on = cascade_possible(S, max_seqlen);
+  f.cascade_on = D == kD && cascade_possible(S, max_seqlen);
+  f.mfma_prefill = D == kD && (f.prefill_on || f.cascade_on);
   // Workspace: split-K partials of the decode kernels (when a context can take
   // more than one part, or a cascade prefix makes even one part a partial),
   // the cascade prefix partials, then the work plan, each 256-byte aligned.
   const size_t align = 255;
   f.dec_bytes = (f.P > 1 || f.cascade_on)
-                    ? (static_cast<size_t>(S) * Hkv * f.P * f.rows_cap * kPartFloats * sizeof(float) + align) & ~align
+                    ? (static_cast<size_t>(S) * Hkv * f.P * f.rows_cap * (D + 4) * sizeof(float) + align) & ~align
                     : 0;
   f.pre_off = f.dec_bytes;
   f.plan_off = f.pre_off + (f.cascade_on ? (static_cast<size_t>(kCascadeEntries) * Hkv * kCascadeRows * kPartFloats *
                                                     sizeof(float) + align) & ~align
                                          : 0);
-  f.bytes = f.plan_off + ((f.prefill_on || f.cascade_on)
-                              ? plan_layout(S, T, f.G, f.prefill_on, f.cascade_on).bytes
-                              : 0);
+  f.bytes = f.plan_off + (f.mfma_prefill ? plan_layout(S, T, f.G, f.prefill_on, f.cascade_on).bytes : 0);
   return f;
 }
 
 size_t fast_workspace_bytes(int32_t S, int32_t T, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_q,
                             int32_t max_seqlen) {
-  if (D != kD || Hkv < 1 || Hq % Hkv) return 0;
-  return fast_plan(S, T, Hq, Hkv, max_q, max_seqlen).bytes;
+  if ((D != 64 && D != 128 && D != 256) || Hkv < 1 || Hq % Hkv) return 0;
+  return fast_plan(S, T, Hq, Hkv, D, max_q, max_seqlen).bytes;
+}
+
+// One decode launch for the call's head_dim and block-size class.
+template <class F, int NT>
+static void launch_decode(const DecodeArgs& d, int32_t D, bool blk16, uint32_t grid, hipStream_t stream) {
+#define PA_DECODE_D(DD)                                                          \
+  if (blk16) decode_kernel<F, NT, DD, true><<<grid, 64, 0, stream>>>(d);        \
+  else decode_kernel<F, NT, DD, false><<<grid, 64, 0, stream>>>(d);
+  if (D == 64) {
+    PA_DECODE_D(64)
+  } else if (D == 128) {
+    PA_DECODE_D(128)
+  } else if constexpr (NT == 1) {
+    PA_DECODE_D(256)
+  }
+#undef PA_DECODE_D
+}
+
+template <class F>
+static void launch_merge(const DecodeArgs& d, int32_t D, dim3 grid, hipStream_t stream) {
+  if (D == 64) merge_kernel<F, 64><<<grid, 256, 0, stream>>>(d);
+  else if (D == 256) merge_kernel<F, 256><<<grid, 256, 0, stream>>>(d);
+  else merge_kernel<F, 128><<<grid, 256, 0, stream>>>(d);
 }
 
 hipError_t launch_attn_fast(const AttnArgs& a, hipStream_t stream) {
-  const FastPlan f = fast_plan(a.S, a.T, a.Hq, a.Hkv, a.max_qlen, a.max_seqlen);
+  const FastPlan f = fast_plan(a.S, a.T, a.Hq, a.Hkv, a.D, a.max_qlen, a.max_seqlen);
   DecodeArgs d;
   d.q = static_cast<const uint16_t*>(a.q);
   d.k_cache = static_cast<const uint16_t*>(a.k_cache);
@@ -600,8 +673,13 @@ hipError_t launch_attn_fast(const AttnArgs& a, hipStream_t stream) {
   d.n_items = static_cast<int32_t>(items);
 
   // plan (work list, cascade groups), then prefill query tiles and cascade
-  // prefix parts on the MFMA prefill kernel
-  if (f.prefill_on || f.cascade_on) {
+  // prefix parts on the MFMA prefill kernel (head_dim 128); at other head
+  // dims the generic kernel takes the rows above the decode kernels' cap
+  if (f.prefill_on && !f.mfma_prefill) {
+    const hipError_t e = launch_attn_generic_rows(a, f.rows_cap, stream);
+    if (e != hipSuccess) return e;
+  }
+  if (f.mfma_prefill) {
     int32_t* plan = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(a.workspace) + f.plan_off);
     hipError_t e = launch_attn_plan(a, f.rows_cap, f.prefill_on, f.cascade_on, plan, stream);
     if (e != hipSuccess) return e;
@@ -612,21 +690,22 @@ hipError_t launch_attn_fast(const AttnArgs& a, hipStream_t stream) {
       d.seq_prefix = reinterpret_cast<const int4*>(
           reinterpret_cast<const uint8_t*>(plan) + plan_layout(a.S, a.T, f.G, f.prefill_on, f.cascade_on).seqpre_off);
   }
+  const bool blk16 = a.bs % kChunk == 0;
   launch_mark("decode_kernel", stream);
-  if (a.dtype == PA_BF16) decode_kernel<BF16, 1><<<static_cast<uint32_t>(grid), 64, 0, stream>>>(d);
-  else decode_kernel<F16, 1><<<static_cast<uint32_t>(grid), 64, 0, stream>>>(d);
+  if (a.dtype == PA_BF16) launch_decode<BF16, 1>(d, a.D, blk16, static_cast<uint32_t>(grid), stream);
+  else launch_decode<F16, 1>(d, a.D, blk16, static_cast<uint32_t>(grid), stream);
   launch_done(stream);
   if (d.rows_cap > kTileRows) {
     launch_mark("decode_kernel_2t", stream);
-    if (a.dtype == PA_BF16) decode_kernel<BF16, 2><<<static_cast<uint32_t>(grid), 64, 0, stream>>>(d);
-    else decode_kernel<F16, 2><<<static_cast<uint32_t>(grid), 64, 0, stream>>>(d);
+    if (a.dtype == PA_BF16) launch_decode<BF16, 2>(d, a.D, blk16, static_cast<uint32_t>(grid), stream);
+    else launch_decode<F16, 2>(d, a.D, blk16, static_cast<uint32_t>(grid), stream);
     launch_done(stream);
   }
   if (d.P > 1 || f.cascade_on) {
     launch_mark("merge_kernel", stream);
     const dim3 mgrid(a.S, a.Hkv, d.rows_cap / kMergeRows);
-    if (a.dtype == PA_BF16) merge_kernel<BF16><<<mgrid, 256, 0, stream>>>(d);
-    else merge_kernel<F16><<<mgrid, 256, 0, stream>>>(d);
+    if (a.dtype == PA_BF16) launch_merge<BF16>(d, a.D, mgrid, stream);
+    else launch_merge<F16>(d, a.D, mgrid, stream);
     launch_done(stream);
   }
   return hipGetLastError();

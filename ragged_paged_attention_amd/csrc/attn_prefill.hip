@@ -346,7 +346,9 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(PlanArgs a) {
 __device__ __forceinline__ int k_slot(int row, int chunk) { return row * kRowBytes + ((chunk ^ (row & 15)) << 4); }
 __device__ __forceinline__ int v_slot(int row, int chunk) { return row * kRowBytes + ((chunk ^ ((row & 7) << 1)) << 4); }
 
-template <class F>
+// kBlk16: the block size is a multiple of 16 (a wave's 16-row group lies in
+// one block); otherwise it divides 16 and each row finds its own block.
+template <class F, bool kBlk16>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 2, kWaves / 2))) void prefill_kernel(PrefillArgs a) {
   using M = Mma<F>;
   // Two stages as two arrays: the tile loop below is unrolled by two so every
@@ -455,6 +457,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
   // The table is read-only here and the index wave-uniform: read it through
   // the constant address space, which makes it a scalar load (counted apart
   // from the tile DMAs, so using it never waits for them).
+  constexpr bool blk16 = kBlk16;
   const __attribute__((address_space(4))) int32_t* btrow_c =
       (const __attribute__((address_space(4))) int32_t*)(btrow);
   auto load_bid = [&](int32_t kt) -> int32_t {
@@ -465,7 +468,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     const int32_t t16 = kt * kTile + (row_base & ~15);
     uint8_t* kdst = stage_lds + row_base * kRowBytes;
     uint8_t* vdst = kdst + kTileBytes;
-    if (t16 + 16 <= L) {  // all of the wave's rows inside the context: one block, fixed offsets
+    if (blk16 && t16 + 16 <= L) {  // all of the wave's rows inside the context: one block, fixed offsets
       const int32_t lb = t16 / a.bs;
       if (b < 0 || b >= a.NB) {
         flag(a.d_err, PA_DERR_BLOCK_OOB);
@@ -497,8 +500,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
       const int row = row_base + 4 * u + grp;  // tile row this lane fills
       const int32_t tok = kt * kTile + row;
       int64_t slot;
-      if (tok < L) slot = slot0 + (row & 15);
-      else {  // past the end: last valid token of the sequence
+      if (tok < L && blk16) slot = slot0 + (row & 15);
+      else if (tok < L) {  // a block size dividing 16: this row's own block
+        const int32_t lbr = tok / a.bs;
+        int32_t br = btrow[lbr];
+        if (br < 0 || br >= a.NB) {
+          flag(a.d_err, PA_DERR_BLOCK_OOB);
+          br = 0;
+        }
+        slot = static_cast<int64_t>(br) * a.bs + (tok - lbr * a.bs);
+      } else {  // past the end: last valid token of the sequence
         const int32_t lb2 = (L - 1) / a.bs;
         int32_t b2 = btrow_c[lb2];
         b2 = (b2 < 0 || b2 >= a.NB) ? 0 : b2;
@@ -783,8 +794,14 @@ hipError_t launch_attn_prefill(const AttnArgs& a, int32_t rows_cap, bool prefill
   if (items > INT32_MAX) return hipErrorInvalidValue;
   if (items == 0) return hipSuccess;
   launch_mark("prefill_kernel", stream);
-  if (a.dtype == PA_BF16) prefill_kernel<BF16><<<static_cast<uint32_t>(items), kThreads, 0, stream>>>(p);
-  else prefill_kernel<F16><<<static_cast<uint32_t>(items), kThreads, 0, stream>>>(p);
+  const uint32_t grid = static_cast<uint32_t>(items);
+  if (a.bs % 16 == 0) {
+    if (a.dtype == PA_BF16) prefill_kernel<BF16, true><<<grid, kThreads, 0, stream>>>(p);
+    else prefill_kernel<F16, true><<<grid, kThreads, 0, stream>>>(p);
+  } else {
+    if (a.dtype == PA_BF16) prefill_kernel<BF16, false><<<grid, kThreads, 0, stream>>>(p);
+    else prefill_kernel<F16, false><<<grid, kThreads, 0, stream>>>(p);
+  }
   launch_done(stream);
   return hipGetLastError();
 }

@@ -386,6 +386,20 @@ def verify_batch(seed: int = 6, S: int = 64, q_lo: int = 2, q_hi: int = 8, ctx_l
                           seed, rng, poison=poison, notes=f"query_len {q_lo}..{q_hi} over {ctx_lo}..{ctx_hi} tokens")
 
 
+def decode_variant(D: int, bs: int, seed: int = 3, S: int = 100, hist_len: int = 2000, Hq: int = 32,
+                   Hkv: int = 32, dtype: Optional[str] = None, poison: bool = True) -> Workload:
+    """The decode batch (S sequences, one new token over `hist_len` cached
+    ones, blocks placed at random) at another head_dim / block size: the
+    head-dim and block-size variants of the decode path."""
+    rng = np.random.default_rng(seed)
+    sl = [hist_len + 1] * S
+    counts = [_ceil_div(L, bs) for L in sl]
+    NB = int(sum(counts)) * 8 // 5
+    tables = _place(rng, NB, counts)
+    return build_workload(f"decode_d{D}_bs{bs}", dtype or "bf16", Hq, Hkv, D, bs, NB, [1] * S, sl, tables,
+                          seed, rng, poison=poison)
+
+
 def random_batch(seed: int, S: int = 3, max_ctx: int = 12, max_q: int = 5, Hq: int = 4, Hkv: int = 2,
                  D: int = 16, bs: int = 4, dtype: str = "f32", extra_blocks: int = 4,
                  decode_frac: float = 0.4, poison: bool = True) -> Workload:
