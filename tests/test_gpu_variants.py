@@ -1,9 +1,10 @@
 """GPU parity of the head-dim and block-size variants of the fast decode path.
 
-The method is the same at every head dim and block size ("vLLM 原理" §2: the
-KV cache is cut into fixed-size blocks, any size; the pages' kernels run
-head_dim 64/128/256 and block sizes 8..256), so the plain oracle is the
-reference for all of them.  The decode kernel takes head_dim 64, 128 and 256
+The method is the same at every head dim and block size: "LLM 推理引擎
+Continuous Batching 与 PagedAttention" §3.4 weighs block sizes 1/8/16/32 as a
+trade-off between waste and lookup cost, "vLLM 原理" §3.2 uses 256, and the
+head dim only sets the length of the dot products.  So the plain oracle is
+the reference for all of them.  The decode kernel takes head_dim 64, 128 and 256
 and a block size that is a multiple of 16 or divides 16 (each lane then finds
 its own token's block); query tiles of longer chunks go to the MFMA prefill
 kernel at head_dim 128 (per-row block lookup when the block size is below 16)
