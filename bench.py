@@ -311,7 +311,7 @@ def main():
 
     import ragged_paged_attention_amd as rpa
     from ragged_paged_attention_amd.step import forward_step
-    from workloads import accounting, config, decode_variant, verify_batch
+    from workloads import accounting, config, decode_variant, prefill_variant, verify_batch
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     timer = Timer(torch)
@@ -420,6 +420,28 @@ def main():
             torch.cuda.empty_cache()
         result["decode_variants"] = {
             "workload": "decode batch: 100 seqs x 2001 tokens, 32/32 heads, bf16, at head_dim/block_size "
+                        "64/16, 256/16 and 128/8", **res}
+        res = {}
+        for D, bs in ((64, 16), (256, 16), (128, 8)):
+            wp = prefill_variant(D, bs, poison=False)
+            gp = setup(wp, torch).write_step_rows()
+            db = gp.db
+            wsp = workspace_for(wp, rpa, torch)
+            outp = torch.empty_like(db.q)
+            qslp = gp.meta["query_start_loc"]
+            attnp = lambda: rpa.pa_attention(db.q, gp.k_cache, gp.v_cache, db.block_tables, qslp, db.seq_lens,
+                                             wp.max_query_len, wp.max_seq_len, wp.scale, out=outp, workspace=wsp)
+            msp = timer.time(attnp, max(args.steps, 20), args.warmup)
+            kernp = timer.kernels(rpa, attnp, 10)
+            flp = accounting.attention_flops(wp.step.query_lens, wp.step.seq_lens, wp.num_q_heads, wp.head_dim)
+            res[f"D{D}_bs{bs}"] = {
+                "TFLOPs": flp / (msp / 1e3) / 1e12, "flops": flp, "ms_per_call": msp,
+                "prefill_kernel_TFLOPs": flp / (kernp["prefill_kernel"][1] / 1e3) / 1e12,
+                "kernels_ms": {k: round(avg, 5) for k, (n, avg) in kernp.items()}}
+            del gp, wsp, outp
+            torch.cuda.empty_cache()
+        result["prefill_variants"] = {
+            "workload": "ragged prefill: prompts 16/128/1024/2048, 32/32 heads, bf16, at head_dim/block_size "
                         "64/16, 256/16 and 128/8", **res}
 
     # ---------------- shared-prefix long-context decode ----------------

@@ -1,8 +1,7 @@
-// MFMA fast paths for pa_attention: bf16/f16 storage; the decode kernel takes
-// head_dim 64, 128 or 256 and a block size that is a multiple of 16 (a
-// 16-token chunk lies inside one block) or divides 16 (each lane finds its
-// own token's block); query tiles of longer chunks go to the prefill kernel
-// (head_dim 128) or, for the other head dims, to the generic kernel.
+// MFMA fast paths for pa_attention: bf16/f16 storage, head_dim 64, 128 or
+// 256, and a block size that is a multiple of 16 (a 16-token chunk lies
+// inside one block) or divides 16 (each lane finds its own token's block);
+// query tiles of longer chunks go to the prefill kernel (attn_prefill.hip).
 //
 // What is computed is the same as the generic kernel: for each new row of a
 // sequence, causal softmax attention over its own cached K/V read through its
@@ -577,9 +576,9 @@ static int32_t decode_rows_cap(int32_t G, int32_t max_q, int32_t D) {
 
 // Work split of one call, from the sizes and hints alone (the same numbers
 // give the workspace size and the launches).
-// prefill_on: rows above rows_cap may come (the prefill kernel takes them at
-// head_dim 128, the generic kernel otherwise); mfma_prefill: the planned
-// MFMA prefill kernel runs (prefill query tiles or cascade prefix parts).
+// prefill_on: rows above rows_cap may come (the prefill kernel takes them);
+// mfma_prefill: the planned MFMA prefill kernel runs (prefill query tiles or
+// cascade prefix parts).
 struct FastPlan {
   int32_t G, P, rows_cap;
   bool prefill_on, cascade_on, mfma_prefill;
@@ -594,7 +593,7 @@ static FastPlan fast_plan(int32_t S, int32_t T, int32_t Hq, int32_t Hkv, int32_t
   f.rows_cap = decode_rows_cap(f.G, max_q, D);
   f.prefill_on = static_cast<int64_t>(max_q) * f.G > f.rows_cap;
   f.cascade_on = D == kD && cascade_possible(S, max_seqlen);
-  f.mfma_prefill = D == kD && (f.prefill_on || f.cascade_on);
+  f.mfma_prefill = f.prefill_on || f.cascade_on;
   // Workspace: split-K partials of the decode kernels (when a context can take
   // more than one part, or a cascade prefix makes even one part a partial),
   // the cascade prefix partials, then the work plan, each 256-byte aligned.
@@ -673,12 +672,7 @@ hipError_t launch_attn_fast(const AttnArgs& a, hipStream_t stream) {
   d.n_items = static_cast<int32_t>(items);
 
   // plan (work list, cascade groups), then prefill query tiles and cascade
-  // prefix parts on the MFMA prefill kernel (head_dim 128); at other head
-  // dims the generic kernel takes the rows above the decode kernels' cap
-  if (f.prefill_on && !f.mfma_prefill) {
-    const hipError_t e = launch_attn_generic_rows(a, f.rows_cap, stream);
-    if (e != hipSuccess) return e;
-  }
+  // prefix parts on the MFMA prefill kernel
   if (f.mfma_prefill) {
     int32_t* plan = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(a.workspace) + f.plan_off);
     hipError_t e = launch_attn_plan(a, f.rows_cap, f.prefill_on, f.cascade_on, plan, stream);

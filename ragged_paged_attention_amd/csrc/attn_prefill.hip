@@ -48,9 +48,6 @@ constexpr int kNt = kRowsPerWave / 16;                  // 16-row MFMA tiles per
 constexpr int kWaves = kRowsPerWG / kRowsPerWave;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 64;                          // KV tokens per tile
-constexpr int kRowBytes = 256;                     // one token row of one head (128 x 16 bit)
-constexpr int kTileBytes = kTile * kRowBytes;      // 16 KB per K or V tile
-constexpr int kStageBytes = 2 * kTileBytes;        // K tile then V tile
 constexpr float kRescaleSlack = 8.f;               // log2 units the running max may lag
 #ifndef PA_PREFILL_QT_RUN
 #define PA_PREFILL_QT_RUN 4
@@ -337,20 +334,50 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(PlanArgs a) {
 }
 
 
-// LDS tiles are 64 rows x 16 chunks of 16 bytes, stored without padding.
-// Chunk c of row R sits in slot c ^ swz(R):
-//   K: swz = R & 15 -> the 16 rows one K fragment read touches use 16
-//      different slots, i.e. all 64 banks once;
-//   V: swz = (R & 7) << 1 -> the 8 rows of a half-wave transposed read hit 8
-//      different 32-byte bank groups (chunk pairs stay adjacent).
-__device__ __forceinline__ int k_slot(int row, int chunk) { return row * kRowBytes + ((chunk ^ (row & 15)) << 4); }
-__device__ __forceinline__ int v_slot(int row, int chunk) { return row * kRowBytes + ((chunk ^ ((row & 7) << 1)) << 4); }
+// LDS tile geometry for head_dim D: a token row of one head is 2D bytes =
+// D/8 chunks of 16 bytes, 64 rows per tile, stored without padding.  Chunk c
+// of row R sits in slot c ^ swz(R):
+//   K: swz = R & min(D/8 - 1, 15) -> at head_dim 128 the 16 rows one K
+//      fragment read touches use 16 different slots, i.e. all 64 banks once;
+//   V: swz = (R & min(D/16 - 1, 7)) << 1 -> at head_dim 128 the 8 rows of a
+//      half-wave transposed read hit 8 different 32-byte bank groups (chunk
+//      pairs stay adjacent).
+template <int D>
+struct Geom {
+  static constexpr int kRowBytes = 2 * D;                 // one token row of one head
+  static constexpr int kChunks = D / 8;                   // 16-byte chunks per row
+  static constexpr int kTileBytes = kTile * kRowBytes;    // one K or V tile
+  static constexpr int kStageBytes = 2 * kTileBytes;      // K tile then V tile
+  static constexpr int kSwzK = (kChunks < 16 ? kChunks : 16) - 1;
+  static constexpr int kSwzV = (kChunks < 16 ? kChunks / 2 : 8) - 1;
+  static constexpr int kKK = D / 32;                      // 16x16x32 K steps of QK
+  static constexpr int kDT = D / 16;                      // 16-wide output tiles of PV
+  static constexpr int kRpi = 512 / D;                    // tile rows per DMA instruction
+  static __device__ __forceinline__ int k_slot(int row, int chunk) {
+    return row * kRowBytes + ((chunk ^ (row & kSwzK)) << 4);
+  }
+  static __device__ __forceinline__ int v_slot(int row, int chunk) {
+    return row * kRowBytes + ((chunk ^ ((row & kSwzV) << 1)) << 4);
+  }
+};
+
+// Waves per SIMD the register budget is set for: head_dim 256 (O of 32 rows
+// x 256 columns, twice the Q fragments) runs one wave per SIMD, and one
+// workgroup per CU (its two LDS stages take 128 KB).
+template <int D>
+constexpr int prefill_waves_per_eu() {
+  return D == 256 ? 1 : kWaves / 2;
+}
 
 // kBlk16: the block size is a multiple of 16 (a wave's 16-row group lies in
 // one block); otherwise it divides 16 and each row finds its own block.
-template <class F, bool kBlk16>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 2, kWaves / 2))) void prefill_kernel(PrefillArgs a) {
+// D: head_dim (64, 128, 256).
+template <class F, bool kBlk16, int D>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(prefill_waves_per_eu<D>(), kWaves / 2))) void prefill_kernel(PrefillArgs a) {
   using M = Mma<F>;
+  using Gm = Geom<D>;
+  constexpr int kRowBytes = Gm::kRowBytes, kTileBytes = Gm::kTileBytes, kStageBytes = Gm::kStageBytes;
+  constexpr int kKK = Gm::kKK, kDT = Gm::kDT, kRpi = Gm::kRpi;
   // Two stages as two arrays: the tile loop below is unrolled by two so every
   // LDS read and every DMA names its stage statically, and the compiler can
   // see that the DMA into one stage does not touch the stage being read (with
@@ -415,40 +442,42 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
   if (!cascade && (L < qlen || ceil_div(L, a.bs) > a.MB)) {
     if (tid == 0) flag(a.d_err, L < qlen ? PA_DERR_QLEN_GT_SEQLEN : PA_DERR_BLOCK_OOB);
     const int32_t r0 = qt_first * kRowsPerWG, r1 = min(r0 + kRowsPerWG, rows_total);
-    for (int32_t idx = tid; idx < (r1 - r0) * kD; idx += kThreads) {
-      const int32_t rho = r0 + idx / kD;
+    for (int32_t idx = tid; idx < (r1 - r0) * D; idx += kThreads) {
+      const int32_t rho = r0 + idx / D;
       const int32_t i = rho / a.G, hg = rho - (rho / a.G) * a.G;
-      a.out[((static_cast<int64_t>(q0) + i) * a.Hq + g * a.G + hg) * kD + idx % kD] = 0;
+      a.out[((static_cast<int64_t>(q0) + i) * a.Hq + g * a.G + hg) * D + idx % D] = 0;
     }
     return;
   }
 
   const int32_t* btrow = a.block_tables + static_cast<int64_t>(s) * a.MB;
-  const int64_t slot_stride = static_cast<int64_t>(a.Hkv) * kD;  // elements between slots
-  const uint16_t* kbase = a.k_cache + static_cast<int64_t>(g) * kD;
-  const uint16_t* vbase = a.v_cache + static_cast<int64_t>(g) * kD;
+  const int64_t slot_stride = static_cast<int64_t>(a.Hkv) * D;  // elements between slots
+  const uint16_t* kbase = a.k_cache + static_cast<int64_t>(g) * D;
+  const uint16_t* vbase = a.v_cache + static_cast<int64_t>(g) * D;
 
   // DMA of one tile: wave w fills rows kDmaRows*w .. (inside one 16-token
-  // group, so one block id) of the K and V tiles, 4 rows per instruction,
-  // lane -> 16 bytes.  Rows at or past the context end re-read the last valid
-  // row, so nothing unwritten (possibly NaN) ever reaches LDS; such rows are
-  // masked anyway.
-  constexpr int kDmaRows = kTile / kWaves;  // tile rows each wave fills
-  constexpr int kDmaInst = kDmaRows / 4;     // 4 rows per DMA instruction
+  // group, so one block id) of the K and V tiles, kRpi rows per instruction,
+  // lane -> 16 bytes (row lane / (D/8), slot lane % (D/8)).  Rows at or past
+  // the context end re-read the last valid row, so nothing unwritten
+  // (possibly NaN) ever reaches LDS; such rows are masked anyway.
+  constexpr int kDmaRows = kTile / kWaves;     // tile rows each wave fills
+  constexpr int kDmaInst = kDmaRows / kRpi;    // DMA instructions per wave and tile
   static_assert(16 % kDmaRows == 0 || kDmaRows % 16 == 0, "a wave's rows stay inside 16-token groups");
+  static_assert(kDmaRows % kRpi == 0, "whole DMA instructions per wave");
   const int row_base = kDmaRows * __builtin_amdgcn_readfirstlane(wave);  // wave-uniform
+  const int dma_row = lane / Gm::kChunks, dma_slot = lane % Gm::kChunks;
   // Byte offsets of this lane's K and V sources from the first slot of the
   // wave's rows; the same for every tile whose rows are all inside the context.
-  // (at most 15 slot rows of Hkv x 256 bytes: fits 32 bits for any Hkv the
+  // (at most 15 slot rows of Hkv x 2D bytes: fits 32 bits for any Hkv the
   // grid allows).  Unsigned, so a DMA address is a scalar base plus a
   // zero-extended lane offset, which the instruction takes as is.
   uint32_t k_src_off[kDmaInst], v_src_off[kDmaInst];
 #pragma unroll
   for (int u = 0; u < kDmaInst; ++u) {
-    const int row = row_base + 4 * u + grp;
+    const int row = row_base + kRpi * u + dma_row;
     const uint32_t rowoff = static_cast<uint32_t>((row & 15) * a.Hkv * kRowBytes);
-    k_src_off[u] = rowoff + 16 * (r ^ (row & 15));
-    v_src_off[u] = rowoff + 16 * (r ^ ((row & 7) << 1));
+    k_src_off[u] = rowoff + 16 * (dma_slot ^ (row & Gm::kSwzK));
+    v_src_off[u] = rowoff + 16 * (dma_slot ^ ((row & Gm::kSwzV) << 1));
   }
   // Block id of the wave's 16-token group in tile kt when the group lies
   // inside the context (loaded one tile ahead of its DMA, so the DMA never
@@ -480,10 +509,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
 #pragma unroll
       for (int u = 0; u < kDmaInst; ++u) {
         __builtin_amdgcn_global_load_lds((const void*)(ksrc + k_src_off[u]),
-                                         (__attribute__((address_space(3))) void*)(kdst + 4 * u * kRowBytes),
+                                         (__attribute__((address_space(3))) void*)(kdst + kRpi * u * kRowBytes),
                                          16, 0, 0);
         __builtin_amdgcn_global_load_lds((const void*)(vsrc + v_src_off[u]),
-                                         (__attribute__((address_space(3))) void*)(vdst + 4 * u * kRowBytes),
+                                         (__attribute__((address_space(3))) void*)(vdst + kRpi * u * kRowBytes),
                                          16, 0, 0);
       }
       return;
@@ -497,7 +526,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     const int64_t slot0 = static_cast<int64_t>(b) * a.bs + (t16 < L ? t16 - lb * a.bs : 0);
 #pragma unroll
     for (int u = 0; u < kDmaInst; ++u) {
-      const int row = row_base + 4 * u + grp;  // tile row this lane fills
+      const int row = row_base + kRpi * u + dma_row;  // tile row this lane fills
       const int32_t tok = kt * kTile + row;
       int64_t slot;
       if (tok < L && blk16) slot = slot0 + (row & 15);
@@ -515,13 +544,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
         b2 = (b2 < 0 || b2 >= a.NB) ? 0 : b2;
         slot = static_cast<int64_t>(b2) * a.bs + (L - 1 - lb2 * a.bs);
       }
-      const int kc = r ^ (row & 15);         // chunk whose data lands in slot r
-      const int vc = r ^ ((row & 7) << 1);
+      const int kc = dma_slot ^ (row & Gm::kSwzK);  // chunk whose data lands in slot dma_slot
+      const int vc = dma_slot ^ ((row & Gm::kSwzV) << 1);
       __builtin_amdgcn_global_load_lds((const void*)(kbase + slot * slot_stride + 8 * kc),
-                                       (__attribute__((address_space(3))) void*)(kdst + 4 * u * kRowBytes),
+                                       (__attribute__((address_space(3))) void*)(kdst + kRpi * u * kRowBytes),
                                        16, 0, 0);
       __builtin_amdgcn_global_load_lds((const void*)(vbase + slot * slot_stride + 8 * vc),
-                                       (__attribute__((address_space(3))) void*)(vdst + 4 * u * kRowBytes),
+                                       (__attribute__((address_space(3))) void*)(vdst + kRpi * u * kRowBytes),
                                        16, 0, 0);
     }
   };
@@ -540,7 +569,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
 
     // this wave's rows and their Q^T fragments
     int32_t qpos[kNt];
-    uint4 qf[kNt][4];
+    uint4 qf[kNt][kKK];
 #pragma unroll
     for (int nt = 0; nt < kNt; ++nt) {
       const int32_t rho = row0 + wave * kRowsPerWave + nt * 16 + r;
@@ -548,9 +577,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
       const int32_t i = rho / a.G, hg = rho - (rho / a.G) * a.G;
       qpos[nt] = cascade ? INT32_MAX : (valid ? L - qlen + i : -1);
       const int32_t t = valid ? row_token(rho) : 0;
-      const uint16_t* qp = a.q + (static_cast<int64_t>(t) * a.Hq + g * a.G + hg) * kD + 8 * grp;
+      const uint16_t* qp = a.q + (static_cast<int64_t>(t) * a.Hq + g * a.G + hg) * D + 8 * grp;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) qf[nt][kk] = valid ? ld16(qp + 32 * kk) : make_uint4(0, 0, 0, 0);
+      for (int kk = 0; kk < kKK; ++kk) qf[nt][kk] = valid ? ld16(qp + 32 * kk) : make_uint4(0, 0, 0, 0);
     }
     const int32_t wave_row0 = row0 + wave * kRowsPerWave;
     const bool wave_active = wave_row0 < rows_total;
@@ -561,23 +590,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     // the O rescale is rare; numerator and denominator always share the same
     // m, so the result is unchanged.
     float m[kNt];
-    f32x4_t o[kNt][8], osum[kNt];
+    f32x4_t o[kNt][kDT], osum[kNt];
 #pragma unroll
     for (int nt = 0; nt < kNt; ++nt) {
       m[nt] = -INFINITY;
       osum[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) o[nt][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int dt = 0; dt < kDT; ++dt) o[nt][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
     // per-lane LDS byte offsets inside a stage: K fragment (chunk 4kk + grp of
     // row r, + 16 mt rows) and transposed V read (row 4grp + r/4, + 16 / 32
     // rows, chunk 2dt + (r%4)/2, half r%2).  Row offsets that are multiples of
     // 16 (K) or 8 (V) leave the swizzle unchanged, so they fold into constants.
-    int koff[4], voff[8];
+    int koff[kKK], voff[kDT];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) koff[kk] = k_slot(r, 4 * kk + grp);
+    for (int kk = 0; kk < kKK; ++kk) koff[kk] = Gm::k_slot(r, 4 * kk + grp);
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) voff[dt] = v_slot(4 * grp + (r >> 2), 2 * dt + ((r & 3) >> 1)) + 8 * (r & 1);
+    for (int dt = 0; dt < kDT; ++dt) voff[dt] = Gm::v_slot(4 * grp + (r >> 2), 2 * dt + ((r & 3) >> 1)) + 8 * (r & 1);
     const uint4 ones = make_uint4(M::kOnePair, M::kOnePair, M::kOnePair, M::kOnePair);
 
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -596,7 +625,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
 #pragma unroll
           for (int mt = 0; mt < 4; ++mt) st[nt][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
+        for (int kk = 0; kk < kKK; ++kk) {
           uint4 ka[4];
 #pragma unroll
           for (int mt = 0; mt < 4; ++mt)
@@ -652,7 +681,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
           for (int nt = 0; nt < kNt; ++nt) {
             osum[nt] *= alpha[nt];
 #pragma unroll
-            for (int dt = 0; dt < 8; ++dt) o[nt][dt] *= alpha[nt];
+            for (int dt = 0; dt < kDT; ++dt) o[nt][dt] *= alpha[nt];
           }
         }
 
@@ -663,7 +692,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
 #pragma unroll
           for (int nt = 0; nt < kNt; ++nt) osum[nt] = M::qk(ones, pb[nt][u], osum[nt]);
 #pragma unroll
-          for (int dt = 0; dt < 8; ++dt) {
+          for (int dt = 0; dt < kDT; ++dt) {
             const i16x4_t lo = lds_read_tr16(vt_lds + voff[dt] + (32 * u) * kRowBytes);
             const i16x4_t hi = lds_read_tr16(vt_lds + voff[dt] + (32 * u + 16) * kRowBytes);
             const uint4 va = __builtin_bit_cast(uint4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -682,18 +711,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     if (!wave_active) return;
 
     if (cascade) {  // split-K partials (O unnormalised, m in log2 units, l) of every member row
+      if constexpr (D == kD) {  // cascades run at head_dim 128 only
 #pragma unroll
-      for (int nt = 0; nt < kNt; ++nt) {
-        const int32_t rho = wave_row0 + nt * 16 + r;
-        if (rho >= rows_total) continue;
-        float* pe = a.ws_pre + ((static_cast<int64_t>(slot) * a.Hkv + g) * kCascadeRows + rho) * kPartFloats;
+        for (int nt = 0; nt < kNt; ++nt) {
+          const int32_t rho = wave_row0 + nt * 16 + r;
+          if (rho >= rows_total) continue;
+          float* pe = a.ws_pre + ((static_cast<int64_t>(slot) * a.Hkv + g) * kCascadeRows + rho) * kPartFloats;
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt)
-          *reinterpret_cast<float4*>(pe + 16 * dt + 4 * grp) =
-              make_float4(o[nt][dt][0], o[nt][dt][1], o[nt][dt][2], o[nt][dt][3]);
-        if (grp == 0) {
-          pe[kD] = m[nt];
-          pe[kD + 1] = osum[nt][0];
+          for (int dt = 0; dt < kDT; ++dt)
+            *reinterpret_cast<float4*>(pe + 16 * dt + 4 * grp) =
+                make_float4(o[nt][dt][0], o[nt][dt][1], o[nt][dt][2], o[nt][dt][3]);
+          if (grp == 0) {
+            pe[D] = m[nt];
+            pe[D + 1] = osum[nt][0];
+          }
         }
       }
       return;
@@ -704,11 +735,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
       const int32_t rho = wave_row0 + nt * 16 + r;
       if (rho >= rows_total) continue;
       const int32_t i = rho / a.G, hg = rho - (rho / a.G) * a.G;
-      uint16_t* orow = a.out + ((static_cast<int64_t>(q0) + i) * a.Hq + g * a.G + hg) * kD;
+      uint16_t* orow = a.out + ((static_cast<int64_t>(q0) + i) * a.Hq + g * a.G + hg) * D;
       const float l = osum[nt][0];
       const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt)
+      for (int dt = 0; dt < kDT; ++dt)
         *reinterpret_cast<uint2*>(orow + 16 * dt + 4 * grp) =
             make_uint2(M::pk(o[nt][dt][0] * inv, o[nt][dt][1] * inv), M::pk(o[nt][dt][2] * inv, o[nt][dt][3] * inv));
     }
@@ -795,13 +826,23 @@ hipError_t launch_attn_prefill(const AttnArgs& a, int32_t rows_cap, bool prefill
   if (items == 0) return hipSuccess;
   launch_mark("prefill_kernel", stream);
   const uint32_t grid = static_cast<uint32_t>(items);
-  if (a.bs % 16 == 0) {
-    if (a.dtype == PA_BF16) prefill_kernel<BF16, true><<<grid, kThreads, 0, stream>>>(p);
-    else prefill_kernel<F16, true><<<grid, kThreads, 0, stream>>>(p);
-  } else {
-    if (a.dtype == PA_BF16) prefill_kernel<BF16, false><<<grid, kThreads, 0, stream>>>(p);
-    else prefill_kernel<F16, false><<<grid, kThreads, 0, stream>>>(p);
+  const bool blk16 = a.bs % 16 == 0;
+#define PA_PREFILL_D(DD)                                                                             \
+  if (blk16) {                                                                                       \
+    if (a.dtype == PA_BF16) prefill_kernel<BF16, true, DD><<<grid, kThreads, 0, stream>>>(p);        \
+    else prefill_kernel<F16, true, DD><<<grid, kThreads, 0, stream>>>(p);                            \
+  } else {                                                                                           \
+    if (a.dtype == PA_BF16) prefill_kernel<BF16, false, DD><<<grid, kThreads, 0, stream>>>(p);       \
+    else prefill_kernel<F16, false, DD><<<grid, kThreads, 0, stream>>>(p);                           \
   }
+  if (a.D == 64) {
+    PA_PREFILL_D(64)
+  } else if (a.D == 256) {
+    PA_PREFILL_D(256)
+  } else {
+    PA_PREFILL_D(128)
+  }
+#undef PA_PREFILL_D
   launch_done(stream);
   return hipGetLastError();
 }

@@ -400,6 +400,19 @@ def decode_variant(D: int, bs: int, seed: int = 3, S: int = 100, hist_len: int =
                           seed, rng, poison=poison)
 
 
+def prefill_variant(D: int, bs: int = 16, seed: int = 2, dtype: Optional[str] = None,
+                    poison: bool = True) -> Workload:
+    """The ragged prefill batch (prompts of 16/128/1024/2048 tokens, 32/32
+    heads, blocks placed at random) at another head_dim / block size."""
+    rng = np.random.default_rng(seed)
+    lens = [16, 128, 1024, 2048]
+    counts = [_ceil_div(L, bs) for L in lens]
+    NB = int(sum(counts)) * 5
+    tables = _place(rng, NB, counts)
+    return build_workload(f"ragged_prefill_d{D}_bs{bs}", dtype or "bf16", 32, 32, D, bs, NB, lens, lens,
+                          tables, seed, rng, poison=poison)
+
+
 def random_batch(seed: int, S: int = 3, max_ctx: int = 12, max_q: int = 5, Hq: int = 4, Hkv: int = 2,
                  D: int = 16, bs: int = 4, dtype: str = "f32", extra_blocks: int = 4,
                  decode_frac: float = 0.4, poison: bool = True) -> Workload:
