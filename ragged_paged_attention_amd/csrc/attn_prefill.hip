@@ -42,8 +42,11 @@ namespace {
 #ifndef PA_PREFILL_ROWS_PER_WAVE
 #define PA_PREFILL_ROWS_PER_WAVE 32
 #endif
-constexpr int kRowsPerWG = 128;                         // query rows per workgroup
-constexpr int kRowsPerWave = PA_PREFILL_ROWS_PER_WAVE;  // 16 or 32
+#ifndef PA_PREFILL_ROWS_PER_WG
+#define PA_PREFILL_ROWS_PER_WG 128
+#endif
+constexpr int kRowsPerWG = PA_PREFILL_ROWS_PER_WG;      // query rows per workgroup
+constexpr int kRowsPerWave = PA_PREFILL_ROWS_PER_WAVE;  // a multiple of 16
 constexpr int kNt = kRowsPerWave / 16;                  // 16-row MFMA tiles per wave
 constexpr int kWaves = kRowsPerWG / kRowsPerWave;
 constexpr int kThreads = 64 * kWaves;
@@ -364,16 +367,19 @@ struct Geom {
 // Waves per SIMD the register budget is set for: head_dim 256 (O of 32 rows
 // x 256 columns, twice the Q fragments) runs one wave per SIMD, and one
 // workgroup per CU (its two LDS stages take 128 KB).
+#ifndef PA_PREFILL_WAVES_PER_EU
+#define PA_PREFILL_WAVES_PER_EU (kWaves / 2)  // two workgroups per CU
+#endif
 template <int D>
 constexpr int prefill_waves_per_eu() {
-  return D == 256 ? 1 : kWaves / 2;
+  return D == 256 ? 1 : PA_PREFILL_WAVES_PER_EU;
 }
 
 // kBlk16: the block size is a multiple of 16 (a wave's 16-row group lies in
 // one block); otherwise it divides 16 and each row finds its own block.
 // D: head_dim (64, 128, 256).
 template <class F, bool kBlk16, int D>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(prefill_waves_per_eu<D>(), kWaves / 2))) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(prefill_waves_per_eu<D>(), PA_PREFILL_WAVES_PER_EU))) void prefill_kernel(PrefillArgs a) {
   using M = Mma<F>;
   using Gm = Geom<D>;
   constexpr int kRowBytes = Gm::kRowBytes, kTileBytes = Gm::kTileBytes, kStageBytes = Gm::kStageBytes;
@@ -676,7 +682,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(prefil
                                    M::pk(p[2 * u + 1][0], p[2 * u + 1][1]),
                                    M::pk(p[2 * u + 1][2], p[2 * u + 1][3]));
         }
-        if (__any(kNt == 1 ? alpha[0] != 1.f : (alpha[0] != 1.f || alpha[kNt - 1] != 1.f))) {  // wave-uniform, rare after the first tiles
+        bool moved = false;
+#pragma unroll
+        for (int nt = 0; nt < kNt; ++nt) moved |= alpha[nt] != 1.f;
+        if (__any(moved)) {  // wave-uniform, rare after the first tiles
 #pragma unroll
           for (int nt = 0; nt < kNt; ++nt) {
             osum[nt] *= alpha[nt];
