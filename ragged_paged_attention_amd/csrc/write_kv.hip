@@ -7,9 +7,9 @@
 // With the cache laid out [num_blocks, block_size, Hkv, D], all heads of one
 // slot are one contiguous row of Hkv*D elements, exactly like a row of the
 // new k/v [T, Hkv, D].  So the scatter is a copy of T rows of row_bytes each:
-// every thread moves VEC bytes (16 when the row size and pointers allow),
-// consecutive threads cover consecutive bytes of a row, so both the loads and
-// the stores are fully coalesced.  HBM-bound: 2 x 2 x T x row_bytes bytes.
+// one wave per row, lanes on consecutive VEC-byte chunks (16 when the row size
+// and pointers allow), so both the loads and the stores are fully coalesced.
+// HBM-bound: 2 x 2 x T x row_bytes bytes.
 #include "pa_common.h"
 #include "pa_internal.h"
 
@@ -23,28 +23,43 @@ template <> struct Vec<8> { using T = uint2; };
 template <> struct Vec<4> { using T = uint32_t; };
 template <> struct Vec<2> { using T = uint16_t; };
 
+// One wave per token row: the row's slot is one scalar load, then each lane
+// copies VEC-byte chunks of the row, two K and two V loads in flight per pass.
 template <int VEC>
 __global__ __launch_bounds__(256) void write_kv_kernel(
     const char* __restrict__ k, const char* __restrict__ v, const int32_t* __restrict__ slot_mapping,
     int32_t T, int64_t row_bytes, char* __restrict__ k_cache, char* __restrict__ v_cache,
     int64_t num_slots, int32_t* __restrict__ d_err) {
   using V = typename Vec<VEC>::T;
+  const int lane = threadIdx.x & 63;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (t >= T) return;
+  const int32_t slot = slot_mapping[t];
+  if (slot < 0) return;
+  if (slot >= num_slots) {
+    if (lane == 0) flag(d_err, PA_DERR_SLOT_OOB);
+    return;
+  }
   const int64_t per_row = row_bytes / VEC;
-  const int64_t total = static_cast<int64_t>(T) * per_row;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-  for (int64_t c = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; c < total; c += stride) {
-    const int64_t t = c / per_row;
-    const int64_t off = (c - t * per_row) * VEC;
-    const int32_t slot = slot_mapping[t];
-    if (slot < 0) continue;
-    if (slot >= num_slots) {
-      if (off == 0) flag(d_err, PA_DERR_SLOT_OOB);
-      continue;
+  const V* ks = reinterpret_cast<const V*>(k + t * row_bytes);
+  const V* vs = reinterpret_cast<const V*>(v + t * row_bytes);
+  V* kd = reinterpret_cast<V*>(k_cache + static_cast<int64_t>(slot) * row_bytes);
+  V* vd = reinterpret_cast<V*>(v_cache + static_cast<int64_t>(slot) * row_bytes);
+  // two chunks per lane per pass, both loads of a pass issued before its stores
+  for (int64_t c = lane; c < per_row; c += 128) {
+    const bool two = c + 64 < per_row;
+    const V k0 = ks[c], v0 = vs[c];
+    V k1 = k0, v1 = v0;
+    if (two) {
+      k1 = ks[c + 64];
+      v1 = vs[c + 64];
     }
-    const int64_t src = t * row_bytes + off;
-    const int64_t dst = static_cast<int64_t>(slot) * row_bytes + off;
-    *reinterpret_cast<V*>(k_cache + dst) = *reinterpret_cast<const V*>(k + src);
-    *reinterpret_cast<V*>(v_cache + dst) = *reinterpret_cast<const V*>(v + src);
+    kd[c] = k0;
+    vd[c] = v0;
+    if (two) {
+      kd[c + 64] = k1;
+      vd[c + 64] = v1;
+    }
   }
 }
 
@@ -59,10 +74,7 @@ hipError_t launch_write_kv(const void* k, const void* v, const int32_t* slot_map
                           static_cast<uintptr_t>(row_bytes);
   int vec = 16;
   while (vec > 2 && (align % vec) != 0) vec >>= 1;
-  const int64_t chunks = static_cast<int64_t>(T) * (row_bytes / vec);
-  int64_t blocks = (chunks + 255) / 256;
-  if (blocks > 16384) blocks = 16384;
-  const dim3 grid(static_cast<unsigned>(blocks));
+  const dim3 grid(static_cast<unsigned>((static_cast<int64_t>(T) + 3) / 4));  // 4 token rows per workgroup
   const char* kc = static_cast<const char*>(k);
   const char* vc = static_cast<const char*>(v);
   char* kd = static_cast<char*>(k_cache);
