@@ -31,12 +31,16 @@
 // A part writes (m, l, O) partials to the workspace; a merge kernel combines
 // parts with the rescaling algebra.  A sequence with one part writes out
 // directly.
+#include <algorithm>
 #include <mutex>
 
 #include "mfma_common.h"
 #include "pa_common.h"
 #include "pa_internal.h"
 
+#ifndef PA_DECODE_LIST
+#define PA_DECODE_LIST 1  // decode kernels take the plan's work lists when the plan runs
+#endif
 #ifndef PA_DECODE_2T_SIDE_STREAM
 #define PA_DECODE_2T_SIDE_STREAM 1
 #endif
@@ -46,25 +50,10 @@ namespace {
 
 constexpr int kTileRows = 16;       // query rows per MFMA column tile
 constexpr int kMaxRows = 32;        // query rows of one decode item (two tiles)
-// Compile-time tuning of the decode work split (measured on MI355X).
-constexpr int kPartChunks = 48;     // a context part is at most 48 chunks = 768 tokens
-constexpr int kMaxParts = 64;       // parts per sequence (longer parts past 48k tokens)
+// Compile-time tuning of the decode work order (measured on MI355X); the
+// part split (kPartChunks, plan_parts) is in pa_internal.h.
 constexpr int kXcdRun = 16;         // consecutive decode items kept on one XCD
 constexpr int kGroupHeadsBelow = 16;  // item order: head-grouped when Hkv < this
-
-// Split of a context of `nchunks` 16-token chunks into parts of about
-// kPartChunks chunks: at most P parts, none empty.  Equal-sized parts keep the
-// tail of the launch short however uneven the context lengths are.
-__host__ __device__ __forceinline__ void plan_parts(int32_t nchunks, int32_t P, int32_t* nparts,
-                                                    int32_t* cpp) {
-  int32_t np = (nchunks + kPartChunks - 1) / kPartChunks;
-  if (np > P) np = P;
-  if (np < 1) np = 1;
-  int32_t c = (nchunks + np - 1) / np;
-  if (c < 1) c = 1;
-  *cpp = c;
-  *nparts = (nchunks + c - 1) / c;
-}
 
 struct DecodeArgs {
   const uint16_t* q;
@@ -79,6 +68,10 @@ struct DecodeArgs {
   const float* ws_pre;     // cascade prefix partials
   int32_t prefill_on;  // the prefill kernel runs in this call
   int32_t max_q;       // the caller's max_query_len hint
+  // Decode work lists of the plan (one-tile, two-tile items; null without a
+  // plan): entries (sequence, part), heaviest first; counts in dec_n[0..1].
+  const int2* dec_list[2];
+  const int32_t* dec_n;
   float scale_log2e;
   uint16_t* out;
   float* ws;
@@ -122,6 +115,27 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(decode_min_w
   // a sequence or a head to one XCD and leave the XCDs' loads uneven.  The
   // grid is a multiple of 8 * kXcdRun.
   const int32_t bid = blockIdx.x;
+  int32_t s, g, part;
+  if (a.dec_list[0]) {
+    // the plan's list in XCD runs: (block of kXcdRun entries, KV head, entry
+    // in block), the k-th run an XCD takes being run 8k + ((xcd + k) mod 8).
+    // Entries are the real (sequence, part) items of this instance, heaviest
+    // first, so neighbouring entries weigh about the same and the grid's empty
+    // workgroups all come after the real ones (measured against the mapping
+    // below on the mixed batch: decode 419 -> 389 us; verify batch 0.51 ->
+    // 0.46 ms; ordering the list head-fastest instead of in runs was slower
+    // than either)
+    const int32_t xcd = bid & 7, j = bid >> 3;
+    const int32_t k = j / kXcdRun;
+    const int32_t item = (k * 8 + ((xcd + k) & 7)) * kXcdRun + (j % kXcdRun);
+    const int32_t tmp = item / kXcdRun;
+    g = tmp % a.Hkv;
+    const int32_t e = (tmp / a.Hkv) * kXcdRun + item % kXcdRun;
+    if (e >= a.dec_n[NT - 1]) return;
+    const int2 en = a.dec_list[NT - 1][e];
+    s = en.x;
+    part = en.y;
+  } else {
   const int32_t xcd = bid & 7, j = bid >> 3;
   const int32_t k = j / kXcdRun;
   const int32_t item = (k * 8 + ((xcd + k) & 7)) * kXcdRun + (j % kXcdRun);
@@ -129,7 +143,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(decode_min_w
   // item = (part, sequence, KV head), head fastest: the Hkv waves reading the
   // same token rows (all heads of a slot are one contiguous row of the cache)
   // run side by side.
-  int32_t s, g, part;
   if (a.grouped) {
     // (part, block of kXcdRun sequences, head, sequence in block): a run is the
     // same (part, head) of kXcdRun neighbouring sequences on one XCD (shared
@@ -152,6 +165,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(decode_min_w
     const int32_t tmp = item / a.S;
     g = tmp % a.Hkv;
     part = tmp / a.Hkv;
+  }
   }
 
   const int32_t q0 = a.qsl[s];
@@ -611,7 +625,7 @@ static FastPlan fast_plan(int32_t S, int32_t T, int32_t Hq, int32_t Hkv, int32_t
   f.plan_off = f.pre_off + (f.cascade_on ? (static_cast<size_t>(kCascadeEntries) * Hkv * kCascadeRows * kPartFloats *
                                                     sizeof(float) + align) & ~align
                                          : 0);
-  f.bytes = f.plan_off + (f.mfma_prefill ? plan_layout(S, T, f.G, f.prefill_on, f.cascade_on).bytes : 0);
+  f.bytes = f.plan_off + (f.mfma_prefill ? plan_layout(S, T, f.G, f.P, f.prefill_on, f.cascade_on).bytes : 0);
   return f;
 }
 
@@ -703,10 +717,15 @@ hipError_t launch_attn_fast(const AttnArgs& a, hipStream_t stream) {
   d.d_err = a.d_err;
   d.grouped = a.Hkv < kGroupHeadsBelow ? 1 : 0;
   d.seq_prefix = nullptr;
+  d.dec_list[0] = d.dec_list[1] = nullptr;
+  d.dec_n = nullptr;
   d.ws_pre = reinterpret_cast<const float*>(static_cast<const uint8_t*>(a.workspace) + f.pre_off);
   const int64_t s_pad = d.grouped ? (a.S + kXcdRun - 1) / kXcdRun * kXcdRun : a.S;
   const int64_t items = s_pad * a.Hkv * d.P;
-  const int64_t grid = (items + 8 * kXcdRun - 1) / (8 * kXcdRun) * (8 * kXcdRun);
+  // with the plan's lists: whole blocks of kXcdRun entries for every head
+  const int64_t list_items = (static_cast<int64_t>(a.S) * d.P + kXcdRun - 1) / kXcdRun * kXcdRun * a.Hkv;
+  const int64_t grid_items = f.mfma_prefill && PA_DECODE_LIST ? std::max(items, list_items) : items;
+  const int64_t grid = (grid_items + 8 * kXcdRun - 1) / (8 * kXcdRun) * (8 * kXcdRun);
   if (grid > INT32_MAX) return hipErrorInvalidValue;
   d.n_items = static_cast<int32_t>(items);
 
@@ -714,14 +733,19 @@ hipError_t launch_attn_fast(const AttnArgs& a, hipStream_t stream) {
   // prefix parts on the MFMA prefill kernel
   if (f.mfma_prefill) {
     int32_t* plan = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(a.workspace) + f.plan_off);
-    hipError_t e = launch_attn_plan(a, f.rows_cap, f.prefill_on, f.cascade_on, plan, stream);
+    hipError_t e = launch_attn_plan(a, f.rows_cap, f.P, f.prefill_on, f.cascade_on, plan, stream);
     if (e != hipSuccess) return e;
-    e = launch_attn_prefill(a, f.rows_cap, f.prefill_on, f.cascade_on, plan,
+    e = launch_attn_prefill(a, f.rows_cap, f.P, f.prefill_on, f.cascade_on, plan,
                             reinterpret_cast<float*>(static_cast<uint8_t*>(a.workspace) + f.pre_off), stream);
     if (e != hipSuccess) return e;
-    if (f.cascade_on)
-      d.seq_prefix = reinterpret_cast<const int4*>(
-          reinterpret_cast<const uint8_t*>(plan) + plan_layout(a.S, a.T, f.G, f.prefill_on, f.cascade_on).seqpre_off);
+    const PlanLayout l = plan_layout(a.S, a.T, f.G, f.P, f.prefill_on, f.cascade_on);
+    if (f.cascade_on) d.seq_prefix = reinterpret_cast<const int4*>(reinterpret_cast<const uint8_t*>(plan) + l.seqpre_off);
+    const int2* dec = reinterpret_cast<const int2*>(reinterpret_cast<const uint8_t*>(plan) + l.dec_off);
+    if (PA_DECODE_LIST) {
+      d.dec_list[0] = dec;
+      d.dec_list[1] = dec + l.cap_dec;
+      d.dec_n = plan + 2;
+    }
   }
   const bool blk16 = a.bs % kChunk == 0;
   std::unique_lock<std::mutex> side_lock(g_side_mu, std::defer_lock);

@@ -81,10 +81,16 @@ struct PlanArgs {
   const int32_t* seq_lens;
   const int32_t* block_tables;
   int32_t S, T, G, MB, bs, rows_cap, prefill_on, cascade_on, cap_entries, cap_groups;
+  int32_t P, max_q;  // decode parts per sequence at most; the max_query_len hint
+  int64_t cap_dec;   // entries of each decode list
   int32_t* plan;
   int4* groups;
   int4* seq_prefix;
+  int2* dec;         // decode lists: one-tile at dec, two-tile at dec + cap_dec
+  int32_t* d_err;
 };
+
+constexpr int kDecBuckets = 1024;  // decode list weights: chunks of a part, larger ones share the top bucket
 
 // KV heads per run slot of the prefill item order: 4 when they divide Hkv.
 __host__ __device__ __forceinline__ int32_t prefill_head_group(int32_t Hkv) {
@@ -333,6 +339,74 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(PlanArgs a) {
     const int32_t parts = gr.w & 255;
     const int32_t pos = atomicAdd(&cursor[min(ceil_div(gr.z / kTile, parts), kPlanBuckets - 1)], parts);
     for (int32_t pp = 0; pp < parts && pos + pp < a.cap_entries; ++pp) entries[pos + pp] = make_int2(-(gi + 1), pp);
+  }
+
+  // Decode work lists: every (sequence, part) item of the one-tile and of the
+  // two-tile decode instance, each list counting-sorted by the chunks the part
+  // reads, heaviest first, so the decode grids hold no empty item before a
+  // real one.  A sequence the decode kernels only zero-fill (a violated hint,
+  // an invalid length or table) gets one part-0 entry in the one-tile list,
+  // last.  The max_query_len hint is checked here for every sequence.
+  __shared__ int32_t dhist[2][kDecBuckets];
+  __shared__ int32_t dcur[2][kDecBuckets];
+  for (int i = tid; i < kDecBuckets; i += kPlanThreads) {
+    dhist[0][i] = 0;
+    dhist[1][i] = 0;
+  }
+  __syncthreads();
+  // list c, parts np of cpp chunks over nch chunks; special: one weight-0 part
+  auto dec_item = [&](int32_t s, int32_t& c, int32_t& np, int32_t& cpp, int32_t& nch, bool& special) -> bool {
+    const int32_t qlen = a.qsl[s + 1] - a.qsl[s];
+    if (qlen <= 0 || qlen > a.T) return false;
+    const int32_t rows = qlen * a.G;
+    c = 0;
+    np = 1;
+    cpp = 0;
+    nch = 0;
+    special = true;
+    if (rows > a.rows_cap) return !a.prefill_on;
+    c = rows > 16 ? 1 : 0;
+    const int32_t L = a.seq_lens[s];
+    if (L < qlen || ceil_div(L, a.bs) > a.MB) return true;
+    const int32_t pre = a.cascade_on ? a.seq_prefix[s].x : 0;
+    nch = ceil_div(L, 16) - pre / 16;
+    plan_parts(nch, a.P, &np, &cpp);
+    special = false;
+    return true;
+  };
+  auto part_weight = [&](int32_t p, int32_t cpp, int32_t nch, bool special) {
+    return special ? 0 : min(min(cpp, nch - p * cpp), kDecBuckets - 1);
+  };
+  for (int32_t s = tid; s < a.S; s += kPlanThreads) {
+    const int32_t qlen = a.qsl[s + 1] - a.qsl[s];
+    if (qlen > a.max_q) flag(a.d_err, PA_DERR_HINT);
+    int32_t c, np, cpp, nch;
+    bool special;
+    if (!dec_item(s, c, np, cpp, nch, special)) continue;
+    for (int32_t p = 0; p < np; ++p) atomicAdd(&dhist[c][part_weight(p, cpp, nch, special)], 1);
+  }
+  __syncthreads();
+  static_assert(kDecBuckets == kPlanThreads, "one bucket per thread in the scan");
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int32_t v = dhist[c][kDecBuckets - 1 - tid];  // descending weight
+    const int32_t excl = plan_block_scan<false>(v, 0, wave_tot);
+    dcur[c][kDecBuckets - 1 - tid] = excl;
+    if (tid == kPlanThreads - 1) {
+      const int64_t total = static_cast<int64_t>(excl) + v;
+      a.plan[2 + c] = static_cast<int32_t>(total < a.cap_dec ? total : a.cap_dec);
+    }
+  }
+  __syncthreads();
+  for (int32_t s = tid; s < a.S; s += kPlanThreads) {
+    int32_t c, np, cpp, nch;
+    bool special;
+    if (!dec_item(s, c, np, cpp, nch, special)) continue;
+    int2* list = a.dec + c * a.cap_dec;
+    for (int32_t p = 0; p < np; ++p) {
+      const int32_t pos = atomicAdd(&dcur[c][part_weight(p, cpp, nch, special)], 1);
+      if (pos < a.cap_dec) list[pos] = make_int2(s, p);
+    }
   }
 }
 
@@ -761,14 +835,16 @@ static int64_t prefill_entries_cap(int32_t S, int32_t T, int32_t G) {
   return (static_cast<int64_t>(T) * G + kRowsPerWG - 1) / kRowsPerWG + S;
 }
 
-PlanLayout plan_layout(int32_t S, int32_t T, int32_t G, bool prefill_on, bool cascade_on) {
+PlanLayout plan_layout(int32_t S, int32_t T, int32_t G, int32_t P, bool prefill_on, bool cascade_on) {
   PlanLayout l;
   l.cap_groups = cascade_on ? kCascadeEntries : 0;
   const int64_t cap = (prefill_on ? prefill_entries_cap(S, T, G) : 0) + (cascade_on ? kCascadeEntries : 0);
   l.cap_entries = static_cast<int32_t>(cap > INT32_MAX ? INT32_MAX : cap);
   l.groups_off = (static_cast<size_t>(kPlanHeader) * 4 + static_cast<size_t>(cap) * 8 + 15) & ~static_cast<size_t>(15);
   l.seqpre_off = l.groups_off + static_cast<size_t>(l.cap_groups) * 16;
-  l.bytes = l.seqpre_off + (cascade_on ? static_cast<size_t>(S) * 16 : 0);
+  l.dec_off = (l.seqpre_off + (cascade_on ? static_cast<size_t>(S) * 16 : 0) + 15) & ~static_cast<size_t>(15);
+  l.cap_dec = static_cast<int64_t>(S) * P;
+  l.bytes = l.dec_off + static_cast<size_t>(2 * l.cap_dec) * 8;
   return l;
 }
 
@@ -776,10 +852,10 @@ bool cascade_possible(int32_t S, int32_t max_seqlen) {
   return S >= 2 && S <= kCascadeMaxSeqs && max_seqlen >= 2 * kCascadeMinTiles * kTile;
 }
 
-hipError_t launch_attn_plan(const AttnArgs& a, int32_t rows_cap, bool prefill_on, bool cascade_on,
+hipError_t launch_attn_plan(const AttnArgs& a, int32_t rows_cap, int32_t P, bool prefill_on, bool cascade_on,
                             int32_t* plan, hipStream_t stream) {
   const int32_t G = a.Hq / a.Hkv;
-  const PlanLayout l = plan_layout(a.S, a.T, G, prefill_on, cascade_on);
+  const PlanLayout l = plan_layout(a.S, a.T, G, P, prefill_on, cascade_on);
   PlanArgs p;
   p.qsl = a.qsl;
   p.seq_lens = a.seq_lens;
@@ -797,13 +873,18 @@ hipError_t launch_attn_plan(const AttnArgs& a, int32_t rows_cap, bool prefill_on
   p.plan = plan;
   p.groups = reinterpret_cast<int4*>(reinterpret_cast<uint8_t*>(plan) + l.groups_off);
   p.seq_prefix = reinterpret_cast<int4*>(reinterpret_cast<uint8_t*>(plan) + l.seqpre_off);
+  p.P = P;
+  p.max_q = a.max_qlen;
+  p.cap_dec = l.cap_dec;
+  p.dec = reinterpret_cast<int2*>(reinterpret_cast<uint8_t*>(plan) + l.dec_off);
+  p.d_err = a.d_err;
   launch_mark("attn_plan_kernel", stream);
   attn_plan_kernel<<<1, kPlanThreads, 0, stream>>>(p);
   launch_done(stream);
   return hipGetLastError();
 }
 
-hipError_t launch_attn_prefill(const AttnArgs& a, int32_t rows_cap, bool prefill_on, bool cascade_on,
+hipError_t launch_attn_prefill(const AttnArgs& a, int32_t rows_cap, int32_t P, bool prefill_on, bool cascade_on,
                                const int32_t* plan, float* ws_pre, hipStream_t stream) {
   PrefillArgs p;
   p.q = static_cast<const uint16_t*>(a.q);
@@ -823,7 +904,7 @@ hipError_t launch_attn_prefill(const AttnArgs& a, int32_t rows_cap, bool prefill
   p.scale_log2e = a.scale * 1.4426950408889634f;
   p.out = static_cast<uint16_t*>(a.out);
   p.d_err = a.d_err;
-  const PlanLayout l = plan_layout(a.S, a.T, p.G, prefill_on, cascade_on);
+  const PlanLayout l = plan_layout(a.S, a.T, p.G, P, prefill_on, cascade_on);
   p.plan = plan;
   p.groups = reinterpret_cast<const int4*>(reinterpret_cast<const uint8_t*>(plan) + l.groups_off);
   p.ws_pre = ws_pre;

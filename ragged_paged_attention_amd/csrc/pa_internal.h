@@ -63,7 +63,8 @@ hipError_t launch_attn_fast(const AttnArgs& a, hipStream_t stream);
 // Work plan of one call on the MFMA paths, written to the workspace by the
 // planning kernel (attn_prefill.hip) and read by the prefill, decode and merge
 // kernels:
-//   int32 header[kPlanHeader]   [0] list entries, [1] cascade groups
+//   int32 header[kPlanHeader]   [0] list entries, [1] cascade groups,
+//                               [2], [3] one-tile / two-tile decode entries
 //   int2  entries[cap_entries]  (s >= 0, q-tile): a prefill query tile;
 //                               (-(group + 1), part): a part of a cascade
 //                               group's shared prefix
@@ -72,8 +73,28 @@ hipError_t launch_attn_fast(const AttnArgs& a, hipStream_t stream);
 //   int4  seq_prefix[S]         (prefix tokens, parts, first prefix slot, first
 //                               row in the group) of the sequence's cascade
 //                               group; all 0 if it has none
+//   int2  dec[2][S * P]         decode work lists, one-tile then two-tile:
+//                               (sequence, part), heaviest part first
 // Prefix partials live in their own workspace region: kCascadeEntries slots
 // (one per prefix part) x KV heads x kCascadeRows rows x kPartFloats floats.
+// Split-K decode: a context of `nchunks` 16-token chunks is cut into parts of
+// about kPartChunks chunks, at most P parts (P from max_seq_len, at most
+// kMaxParts), none empty.  Equal-sized parts keep the tail of the launch short
+// however uneven the context lengths are.  The plan and the decode kernels
+// call the same function, so their part ranges agree.
+constexpr int kPartChunks = 48;  // a context part is at most 48 chunks = 768 tokens
+constexpr int kMaxParts = 64;    // parts per sequence (longer parts past 48k tokens)
+__host__ __device__ __forceinline__ void plan_parts(int32_t nchunks, int32_t P, int32_t* nparts,
+                                                    int32_t* cpp) {
+  int32_t np = (nchunks + kPartChunks - 1) / kPartChunks;
+  if (np > P) np = P;
+  if (np < 1) np = 1;
+  int32_t c = (nchunks + np - 1) / np;
+  if (c < 1) c = 1;
+  *cpp = c;
+  *nparts = (nchunks + c - 1) / c;
+}
+
 constexpr int kPlanHeader = 64;
 constexpr int kPartFloats = 132;       // one split-K partial row: O[128], m (log2 units), l, pad
 constexpr int kCascadeMaxParts = 16;   // prefix parts of one group
@@ -83,16 +104,17 @@ constexpr int kCascadeMinTiles = 16;   // shortest shared prefix taken, in 64-to
 constexpr int kCascadeMaxSeqs = 4096;  // sequences the detection handles (LDS)
 struct PlanLayout {
   int32_t cap_entries, cap_groups;
-  size_t groups_off, seqpre_off, bytes;  // byte offsets from the plan base; total
+  int64_t cap_dec;                                 // entries of each decode list
+  size_t groups_off, seqpre_off, dec_off, bytes;  // byte offsets from the plan base; total
 };
-PlanLayout plan_layout(int32_t S, int32_t T, int32_t G, bool prefill_on, bool cascade_on);
+PlanLayout plan_layout(int32_t S, int32_t T, int32_t G, int32_t P, bool prefill_on, bool cascade_on);
 // Shared-prefix (cascade) decode may run in this call: long enough contexts,
 // a batch small enough for the detection.
 bool cascade_possible(int32_t S, int32_t max_seqlen);
-hipError_t launch_attn_plan(const AttnArgs& a, int32_t rows_cap, bool prefill_on, bool cascade_on,
+hipError_t launch_attn_plan(const AttnArgs& a, int32_t rows_cap, int32_t P, bool prefill_on, bool cascade_on,
                             int32_t* plan, hipStream_t stream);
 // Prefill query tiles and cascade prefix parts (their partials go to ws_pre).
-hipError_t launch_attn_prefill(const AttnArgs& a, int32_t rows_cap, bool prefill_on, bool cascade_on,
+hipError_t launch_attn_prefill(const AttnArgs& a, int32_t rows_cap, int32_t P, bool prefill_on, bool cascade_on,
                                const int32_t* plan, float* ws_pre, hipStream_t stream);
 
 }  // namespace pa
