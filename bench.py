@@ -43,7 +43,7 @@ KERNEL_MATCH = {
     "decode_kernel": "decode_kernel<pa::BF16, 1, 128, true>",
     "decode_kernel_2t": "decode_kernel<pa::BF16, 2, 128, true>",
     "merge_kernel": "merge_kernel<pa::BF16, 128>",
-    "prefill_kernel": "prefill_kernel<pa::BF16, true>",
+    "prefill_kernel": "prefill_kernel<pa::BF16, true, 128>",
     "write_kv_kernel": "write_kv_kernel",
     "copy_blocks_kernel": "copy_blocks_kernel",
 }
