@@ -47,7 +47,7 @@ namespace {
 #endif
 constexpr int kRowsPerWG = PA_PREFILL_ROWS_PER_WG;      // query rows per workgroup
 constexpr int kRowsPerWave = PA_PREFILL_ROWS_PER_WAVE;  // a multiple of 16
-constexpr int kNt = kRowsPerWave / 16;                  // 16-row MFMA tiles per wave
+static_assert(kRowsPerWave == 32, "a wave's rows are the 32 columns of its MFMA tiles");
 constexpr int kWaves = kRowsPerWG / kRowsPerWave;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 64;                          // KV tokens per tile
@@ -426,15 +426,20 @@ struct Geom {
   static constexpr int kTileBytes = kTile * kRowBytes;    // one K or V tile
   static constexpr int kStageBytes = 2 * kTileBytes;      // K tile then V tile
   static constexpr int kSwzK = (kChunks < 16 ? kChunks : 16) - 1;
-  static constexpr int kSwzV = (kChunks < 16 ? kChunks / 2 : 8) - 1;
-  static constexpr int kKK = D / 32;                      // 16x16x32 K steps of QK
-  static constexpr int kDT = D / 16;                      // 16-wide output tiles of PV
+  static constexpr int kVSh = D >= 128 ? 2 : 1;           // V swizzle: chunk ^ ((row & 3) << kVSh)
+  static constexpr int kKK = D / 16;                      // 32x32x16 K steps of QK
+  static constexpr int kDB = D / 32;                      // 32-wide output blocks of PV
   static constexpr int kRpi = 512 / D;                    // tile rows per DMA instruction
+  // K rows: 8 (16) consecutive rows read one chunk each, so their chunks are
+  // spread over the banks by XOR with the row's low bits.
   static __device__ __forceinline__ int k_slot(int row, int chunk) {
     return row * kRowBytes + ((chunk ^ (row & kSwzK)) << 4);
   }
+  // V rows: a transposed read takes 4 consecutive rows x 32 (or 64) bytes, so
+  // the 4 rows' chunks are moved apart by XOR with (row & 3) times 2 (4) chunks.
+  static __device__ __forceinline__ int v_swz(int row) { return (row & 3) << kVSh; }
   static __device__ __forceinline__ int v_slot(int row, int chunk) {
-    return row * kRowBytes + ((chunk ^ ((row & kSwzV) << 1)) << 4);
+    return row * kRowBytes + ((chunk ^ v_swz(row)) << 4);
   }
 };
 
@@ -457,7 +462,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(prefil
   using M = Mma<F>;
   using Gm = Geom<D>;
   constexpr int kRowBytes = Gm::kRowBytes, kTileBytes = Gm::kTileBytes, kStageBytes = Gm::kStageBytes;
-  constexpr int kKK = Gm::kKK, kDT = Gm::kDT, kRpi = Gm::kRpi;
+  constexpr int kKK = Gm::kKK, kDB = Gm::kDB, kRpi = Gm::kRpi;
   // Two stages as two arrays: the tile loop below is unrolled by two so every
   // LDS read and every DMA names its stage statically, and the compiler can
   // see that the DMA into one stage does not touch the stage being read (with
@@ -468,7 +473,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(prefil
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int r = lane & 15, grp = lane >> 4;
+  const int n = lane & 31, h = lane >> 5;  // the lane's row of the wave, and its half
 
   // Items.  Workgroup b runs on XCD b % 8, and an XCD hands its workgroups
   // in order, round-robin, to its 4 shader engines, each waiting for a free
@@ -557,7 +562,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(prefil
     const int row = row_base + kRpi * u + dma_row;
     const uint32_t rowoff = static_cast<uint32_t>((row & 15) * a.Hkv * kRowBytes);
     k_src_off[u] = rowoff + 16 * (dma_slot ^ (row & Gm::kSwzK));
-    v_src_off[u] = rowoff + 16 * (dma_slot ^ ((row & Gm::kSwzV) << 1));
+    v_src_off[u] = rowoff + 16 * (dma_slot ^ Gm::v_swz(row));
   }
   // Block id of the wave's 16-token group in tile kt when the group lies
   // inside the context (loaded one tile ahead of its DMA, so the DMA never
@@ -625,7 +630,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(prefil
         slot = static_cast<int64_t>(b2) * a.bs + (L - 1 - lb2 * a.bs);
       }
       const int kc = dma_slot ^ (row & Gm::kSwzK);  // chunk whose data lands in slot dma_slot
-      const int vc = dma_slot ^ ((row & Gm::kSwzV) << 1);
+      const int vc = dma_slot ^ Gm::v_swz(row);
       __builtin_amdgcn_global_load_lds((const void*)(kbase + slot * slot_stride + 8 * kc),
                                        (__attribute__((address_space(3))) void*)(kdst + kRpi * u * kRowBytes),
                                        16, 0, 0);
@@ -647,47 +652,50 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(prefil
     issue_tile(kt_begin, lds0, load_bid(kt_begin));
     int32_t bid_next = load_bid(kt_begin + 1);
 
-    // this wave's rows and their Q^T fragments
-    int32_t qpos[kNt];
-    uint4 qf[kNt][kKK];
-#pragma unroll
-    for (int nt = 0; nt < kNt; ++nt) {
-      const int32_t rho = row0 + wave * kRowsPerWave + nt * 16 + r;
-      const bool valid = rho < rows_total;
-      const int32_t i = rho / a.G, hg = rho - (rho / a.G) * a.G;
-      qpos[nt] = cascade ? INT32_MAX : (valid ? L - qlen + i : -1);
-      const int32_t t = valid ? row_token(rho) : 0;
-      const uint16_t* qp = a.q + (static_cast<int64_t>(t) * a.Hq + g * a.G + hg) * D + 8 * grp;
-#pragma unroll
-      for (int kk = 0; kk < kKK; ++kk) qf[nt][kk] = valid ? ld16(qp + 32 * kk) : make_uint4(0, 0, 0, 0);
-    }
+    // The wave's 32 rows are the columns of its MFMA tiles: lane (n, h) works
+    // on row n, and the two halves h hold different tokens (S^T, P^T) or head
+    // dims (O^T) of it.  Q^T fragment kk: head dims 16 kk + 8 h .. + 7 of row n.
     const int32_t wave_row0 = row0 + wave * kRowsPerWave;
     const bool wave_active = wave_row0 < rows_total;
     const int32_t qpos_min_wave = cascade ? INT32_MAX : L - qlen + wave_row0 / a.G;
+    const int32_t rho_n = wave_row0 + n;
+    const bool row_valid = rho_n < rows_total;
+    const int32_t qpos = cascade ? INT32_MAX : (row_valid ? L - qlen + rho_n / a.G : -1);
+    uint4 qf[kKK];
+    {
+      const int32_t hg = rho_n - (rho_n / a.G) * a.G;
+      const int32_t t = row_valid ? row_token(rho_n) : 0;
+      const uint16_t* qp = a.q + (static_cast<int64_t>(t) * a.Hq + g * a.G + hg) * D + 8 * h;
+#pragma unroll
+      for (int kk = 0; kk < kKK; ++kk) qf[kk] = row_valid ? ld16(qp + 16 * kk) : make_uint4(0, 0, 0, 0);
+    }
 
-    // Running max per row in log2 units.  It is only moved when a tile's max
+    // Running max of row n in log2 units.  It is only moved when a tile's max
     // exceeds it by more than kRescaleSlack, so p = 2^(x - m) stays <= 2^8 and
     // the O rescale is rare; numerator and denominator always share the same
-    // m, so the result is unchanged.
-    float m[kNt];
-    f32x4_t o[kNt][kDT], osum[kNt];
+    // m, so the result is unchanged.  lsum: this half's share of the row sum
+    // of P (the halves are added at the end).
+    float m = -INFINITY, lsum = 0.f;
+    f32x16_t o[kDB];
 #pragma unroll
-    for (int nt = 0; nt < kNt; ++nt) {
-      m[nt] = -INFINITY;
-      osum[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int db = 0; db < kDB; ++db)
 #pragma unroll
-      for (int dt = 0; dt < kDT; ++dt) o[nt][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int v = 0; v < 16; ++v) o[db][v] = 0.f;
+    // Per-lane LDS byte offsets inside a stage.  K fragment kk: row n, chunk
+    // 2 kk + h (+ 32 rows for the second token block).  Transposed V read for
+    // output block db: the lane supplies 4 head dims (chunk 4 db + 2 dhalf +
+    // c/2, half c%2) of row 4 h + jrow, where (dhalf, jrow, c) are lane bits
+    // 4, 3-2 and 1-0 (+ 32 b + 16 s and + 8 rows per read).  Row offsets that
+    // are multiples of 16 (K) or 4 (V) leave the swizzle unchanged, so they
+    // fold into constants.
+    int koff[kKK], voff[kDB];
+#pragma unroll
+    for (int kk = 0; kk < kKK; ++kk) koff[kk] = Gm::k_slot(n, 2 * kk + h);
+    {
+      const int dhalf = (lane >> 4) & 1, jrow = (lane >> 2) & 3, c = lane & 3;
+#pragma unroll
+      for (int db = 0; db < kDB; ++db) voff[db] = Gm::v_slot(4 * h + jrow, 4 * db + 2 * dhalf + (c >> 1)) + 8 * (c & 1);
     }
-    // per-lane LDS byte offsets inside a stage: K fragment (chunk 4kk + grp of
-    // row r, + 16 mt rows) and transposed V read (row 4grp + r/4, + 16 / 32
-    // rows, chunk 2dt + (r%4)/2, half r%2).  Row offsets that are multiples of
-    // 16 (K) or 8 (V) leave the swizzle unchanged, so they fold into constants.
-    int koff[kKK], voff[kDT];
-#pragma unroll
-    for (int kk = 0; kk < kKK; ++kk) koff[kk] = Gm::k_slot(r, 4 * kk + grp);
-#pragma unroll
-    for (int dt = 0; dt < kDT; ++dt) voff[dt] = Gm::v_slot(4 * grp + (r >> 2), 2 * dt + ((r & 3) >> 1)) + 8 * (r & 1);
-    const uint4 ones = make_uint4(M::kOnePair, M::kOnePair, M::kOnePair, M::kOnePair);
 
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -698,91 +706,94 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(prefil
       }
       const uint8_t* vt_lds = kt_lds + kTileBytes;
       if (wave_active) {
-        // S^T[16 mt + 4grp + j][row r of nt]; 8 independent MFMAs per K column block
-        f32x4_t st[kNt][4];
+        // S^T of token block b (tile tokens 32 b .. 32 b + 31): result e holds
+        // token 32 b + 8 (v / 4) + 4 h + v % 4 of row n.
+        f32x16_t st[2];
 #pragma unroll
-        for (int nt = 0; nt < kNt; ++nt)
+        for (int b = 0; b < 2; ++b)
 #pragma unroll
-          for (int mt = 0; mt < 4; ++mt) st[nt][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          for (int v = 0; v < 16; ++v) st[b][v] = 0.f;
 #pragma unroll
         for (int kk = 0; kk < kKK; ++kk) {
-          uint4 ka[4];
+          uint4 ka[2];
 #pragma unroll
-          for (int mt = 0; mt < 4; ++mt)
-            ka[mt] = *reinterpret_cast<const uint4*>(kt_lds + koff[kk] + mt * 16 * kRowBytes);
+          for (int b = 0; b < 2; ++b) ka[b] = *reinterpret_cast<const uint4*>(kt_lds + koff[kk] + 32 * b * kRowBytes);
 #pragma unroll
-          for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int nt = 0; nt < kNt; ++nt) st[nt][mt] = M::qk(ka[mt], qf[nt][kk], st[nt][mt]);
+          for (int b = 0; b < 2; ++b) st[b] = M::mm32(ka[b], qf[kk], st[b]);
         }
 
-        const bool need_mask = kt * kTile + kTile - 1 > qpos_min_wave;
-        uint4 pb[kNt][2];
-        float alpha[kNt];
+        float x[2][16];
 #pragma unroll
-        for (int nt = 0; nt < kNt; ++nt) {
-          float x[4][4];
+        for (int b = 0; b < 2; ++b)
 #pragma unroll
-          for (int mt = 0; mt < 4; ++mt)
+          for (int v = 0; v < 16; ++v) x[b][v] = st[b][v];
+        if (kt * kTile + kTile - 1 > qpos_min_wave) {  // the tile crosses the wave's diagonal
+          const int32_t lim = qpos - (kt * kTile + 4 * h);  // visible iff 32 b + 8 (v / 4) + v % 4 <= lim
 #pragma unroll
-            for (int j = 0; j < 4; ++j) x[mt][j] = st[nt][mt][j];
-          if (need_mask) {
-            const int32_t lim = qpos[nt] - (kt * kTile + 4 * grp);  // visible iff 16 mt + j <= lim
+          for (int b = 0; b < 2; ++b)
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-              for (int j = 0; j < 4; ++j)
-                if (16 * mt + j > lim) x[mt][j] = -INFINITY;
-          }
-          float mx = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
-                           fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
-          mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(x[2][0], x[2][1]), fmaxf(x[2][2], x[2][3])),
-                               fmaxf(fmaxf(x[3][0], x[3][1]), fmaxf(x[3][2], x[3][3]))));
-          mx = group_max4(mx) * a.scale_log2e;
-          alpha[nt] = 1.f;
-          if (mx > m[nt] + kRescaleSlack) {
-            alpha[nt] = __builtin_amdgcn_exp2f(m[nt] - mx);  // 0 on the first visible tile
-            m[nt] = mx;
-          }
-          const float msub = m[nt] == -INFINITY ? 0.f : m[nt];
-          float p[4][4];
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) p[mt][j] = __builtin_amdgcn_exp2f(fmaf(x[mt][j], a.scale_log2e, -msub));
-#pragma unroll
-          for (int u = 0; u < 2; ++u)
-            pb[nt][u] = make_uint4(M::pk(p[2 * u][0], p[2 * u][1]), M::pk(p[2 * u][2], p[2 * u][3]),
-                                   M::pk(p[2 * u + 1][0], p[2 * u + 1][1]),
-                                   M::pk(p[2 * u + 1][2], p[2 * u + 1][3]));
+            for (int v = 0; v < 16; ++v)
+              if (32 * b + 8 * (v >> 2) + (v & 3) > lim) x[b][v] = -INFINITY;
         }
-        bool moved = false;
+        float mx[8];
 #pragma unroll
-        for (int nt = 0; nt < kNt; ++nt) moved |= alpha[nt] != 1.f;
-        if (__any(moved)) {  // wave-uniform, rare after the first tiles
-#pragma unroll
-          for (int nt = 0; nt < kNt; ++nt) {
-            osum[nt] *= alpha[nt];
-#pragma unroll
-            for (int dt = 0; dt < kDT; ++dt) o[nt][dt] *= alpha[nt];
-          }
+        for (int u = 0; u < 8; ++u)
+          mx[u] = fmaxf(fmaxf(x[u >> 2][4 * (u & 3)], x[u >> 2][4 * (u & 3) + 1]),
+                        fmaxf(x[u >> 2][4 * (u & 3) + 2], x[u >> 2][4 * (u & 3) + 3]));
+        float tmax = fmaxf(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3])), fmaxf(fmaxf(mx[4], mx[5]), fmaxf(mx[6], mx[7])));
+        {
+          const uint32_t u = __float_as_uint(tmax);
+          const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);  // the other half's max
+          tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * a.scale_log2e;
         }
+        float alpha = 1.f;
+        if (tmax > m + kRescaleSlack) {
+          alpha = __builtin_amdgcn_exp2f(m - tmax);  // 0 on the first visible tile
+          m = tmax;
+        }
+        const float msub = m == -INFINITY ? 0.f : m;
+        // P^T operand of PV step (b, s): tile tokens 32 b + 16 s .. + 15, the
+        // lane's 8 being results 8 s .. 8 s + 7 of S^T block b.
+        uint4 pb[2][2];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          float p[16];
+#pragma unroll
+          for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(fmaf(x[b][v], a.scale_log2e, -msub));
+#pragma unroll
+          for (int sq = 0; sq < 2; ++sq)
+            pb[b][sq] = make_uint4(M::pk(p[8 * sq], p[8 * sq + 1]), M::pk(p[8 * sq + 2], p[8 * sq + 3]),
+                                   M::pk(p[8 * sq + 4], p[8 * sq + 5]), M::pk(p[8 * sq + 6], p[8 * sq + 7]));
+        }
+        if (__any(alpha != 1.f)) {  // wave-uniform, rare after the first tiles
+          lsum *= alpha;
+#pragma unroll
+          for (int db = 0; db < kDB; ++db) o[db] *= alpha;
+        }
+        // the row sum of the rounded P that enters PV
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int sq = 0; sq < 2; ++sq) {
+            lsum = M::dot1(pb[b][sq].x, lsum);
+            lsum = M::dot1(pb[b][sq].y, lsum);
+            lsum = M::dot1(pb[b][sq].z, lsum);
+            lsum = M::dot1(pb[b][sq].w, lsum);
+          }
 
-        // O^T += V^T . P^T over the two 32-token halves; the row sums of P ride
-        // along as one more MFMA against a tile of ones.
+        // O^T += V^T . P^T: for step (b, s) the lane's V^T operand is head dim
+        // 32 db + n of tokens 32 b + 16 s + 4 h + 0..3 and + 8 (two transposed reads).
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int b = 0; b < 2; ++b)
 #pragma unroll
-          for (int nt = 0; nt < kNt; ++nt) osum[nt] = M::qk(ones, pb[nt][u], osum[nt]);
+          for (int sq = 0; sq < 2; ++sq)
 #pragma unroll
-          for (int dt = 0; dt < kDT; ++dt) {
-            const i16x4_t lo = lds_read_tr16(vt_lds + voff[dt] + (32 * u) * kRowBytes);
-            const i16x4_t hi = lds_read_tr16(vt_lds + voff[dt] + (32 * u + 16) * kRowBytes);
-            const uint4 va = __builtin_bit_cast(uint4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-            for (int nt = 0; nt < kNt; ++nt) o[nt][dt] = M::qk(va, pb[nt][u], o[nt][dt]);
-          }
-        }
+            for (int db = 0; db < kDB; ++db) {
+              const i16x4_t lo = lds_read_tr16(vt_lds + voff[db] + (32 * b + 16 * sq) * kRowBytes);
+              const i16x4_t hi = lds_read_tr16(vt_lds + voff[db] + (32 * b + 16 * sq + 8) * kRowBytes);
+              const uint4 va = __builtin_bit_cast(uint4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+              o[db] = M::mm32(va, pb[b][sq], o[db]);
+            }
       }
       __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();  // next tile landed everywhere; this stage is free again
@@ -793,39 +804,37 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(prefil
     }
     if (!wave_active) return;
 
+    // O^T block db result v: head dim 32 db + 8 (v / 4) + 4 h + v % 4 of row n
+    const uint32_t lu = __float_as_uint(lsum);
+    const auto lsw = __builtin_amdgcn_permlane32_swap(lu, lu, false, false);
+    const float l = __uint_as_float(lsw[0]) + __uint_as_float(lsw[1]);
+    if (!row_valid) return;
     if (cascade) {  // split-K partials (O unnormalised, m in log2 units, l) of every member row
       if constexpr (D == kD) {  // cascades run at head_dim 128 only
+        float* pe = a.ws_pre + ((static_cast<int64_t>(slot) * a.Hkv + g) * kCascadeRows + rho_n) * kPartFloats;
 #pragma unroll
-        for (int nt = 0; nt < kNt; ++nt) {
-          const int32_t rho = wave_row0 + nt * 16 + r;
-          if (rho >= rows_total) continue;
-          float* pe = a.ws_pre + ((static_cast<int64_t>(slot) * a.Hkv + g) * kCascadeRows + rho) * kPartFloats;
+        for (int db = 0; db < kDB; ++db)
 #pragma unroll
-          for (int dt = 0; dt < kDT; ++dt)
-            *reinterpret_cast<float4*>(pe + 16 * dt + 4 * grp) =
-                make_float4(o[nt][dt][0], o[nt][dt][1], o[nt][dt][2], o[nt][dt][3]);
-          if (grp == 0) {
-            pe[D] = m[nt];
-            pe[D + 1] = osum[nt][0];
-          }
+          for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<float4*>(pe + 32 * db + 8 * i + 4 * h) =
+                make_float4(o[db][4 * i], o[db][4 * i + 1], o[db][4 * i + 2], o[db][4 * i + 3]);
+        if (h == 0) {
+          pe[D] = m;
+          pe[D + 1] = l;
         }
       }
       return;
     }
-
+    const int32_t i_q = rho_n / a.G, hg = rho_n - (rho_n / a.G) * a.G;
+    uint16_t* orow = a.out + ((static_cast<int64_t>(q0) + i_q) * a.Hq + g * a.G + hg) * D;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
-    for (int nt = 0; nt < kNt; ++nt) {
-      const int32_t rho = wave_row0 + nt * 16 + r;
-      if (rho >= rows_total) continue;
-      const int32_t i = rho / a.G, hg = rho - (rho / a.G) * a.G;
-      uint16_t* orow = a.out + ((static_cast<int64_t>(q0) + i) * a.Hq + g * a.G + hg) * D;
-      const float l = osum[nt][0];
-      const float inv = l > 0.f ? 1.f / l : 0.f;
+    for (int db = 0; db < kDB; ++db)
 #pragma unroll
-      for (int dt = 0; dt < kDT; ++dt)
-        *reinterpret_cast<uint2*>(orow + 16 * dt + 4 * grp) =
-            make_uint2(M::pk(o[nt][dt][0] * inv, o[nt][dt][1] * inv), M::pk(o[nt][dt][2] * inv, o[nt][dt][3] * inv));
-    }
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<uint2*>(orow + 32 * db + 8 * i + 4 * h) =
+            make_uint2(M::pk(o[db][4 * i] * inv, o[db][4 * i + 1] * inv),
+                       M::pk(o[db][4 * i + 2] * inv, o[db][4 * i + 3] * inv));
   }
 }
 

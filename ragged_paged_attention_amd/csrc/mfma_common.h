@@ -13,6 +13,7 @@ typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kD = 128;          // head_dim of the fast paths
 constexpr int kChunk = 16;       // tokens per MFMA tile edge
@@ -20,9 +21,14 @@ constexpr int kVRowBytes = 288;  // LDS row pitch of a staged V tile: 256 B + 32
                                  // 16 rows one transposed read touches start in distinct banks
 
 // Per-dtype MFMA.  qk: v_mfma_f32_16x16x32 (8 elements per lane per operand);
-// pv16: v_mfma_f32_16x16x16 (4 per lane).
+// pv16: v_mfma_f32_16x16x16 (4 per lane); mm32: v_mfma_f32_32x32x16 (8 per
+// lane, 16 results).
 //   A[m = lane%16][k = 8*(lane/16) + j]  (16x16x32)   A[m][k = 4*(lane/16) + j]  (16x16x16)
 //   B[k = same][n = lane%16]             D[m = 4*(lane/16) + j][n = lane%16]
+//   32x32x16: A[m = lane%32][k = 8*(lane/32) + j], B[k = same][n = lane%32],
+//             result r: D[m = 8*(r/4) + 4*(lane/32) + r%4][n = lane%32]
+// (all layouts checked on the GPU with small integer operands).
+// dot1: the sum of a packed pair plus c, in one v_dot2 against (1, 1).
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -41,6 +47,14 @@ template <> struct Mma<BF16> {
   static __device__ __forceinline__ f32x4_t pv(i16x4_t a, i16x4_t b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
   }
+  static __device__ __forceinline__ f32x16_t mm32(uint4 a, uint4 b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ float dot1(uint32_t p, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, p), __builtin_bit_cast(bf16x2_t, kOnePair),
+                                           c, false);
+  }
   static __device__ __forceinline__ uint16_t cvt(float x) {
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
   }
@@ -57,6 +71,13 @@ template <> struct Mma<F16> {
   static __device__ __forceinline__ f32x4_t pv(i16x4_t a, i16x4_t b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a),
                                                  __builtin_bit_cast(f16x4_t, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x16_t mm32(uint4 a, uint4 b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ float dot1(uint32_t p, float c) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, p), __builtin_bit_cast(f16x2_t, kOnePair), c, false);
   }
   static __device__ __forceinline__ uint16_t cvt(float x) {
     return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
