@@ -353,6 +353,16 @@ def main():
             "kernels_ms_per_step": {k: round(n * avg / args.steps, 5) for k, (n, avg) in kern.items()},
             "step_work": {"decode_bytes": split["decode_kernel"], "prefill_flops": split["prefill_kernel"]},
         })
+        # the whole step against the two rooflines: the time the decode bytes
+        # need at peak HBM bandwidth and the prefill flops at peak MFMA rate,
+        # if the two overlapped perfectly (the larger) or ran one after the
+        # other (the sum)
+        t_hbm = split["decode_kernel"] / (HBM_PEAK_GBS * 1e9) * 1e3
+        t_mfma = split["prefill_kernel"] / (BF16_PEAK_TFLOPS * 1e12) * 1e3
+        result["step_roofline"] = {
+            "decode_at_hbm_peak_ms": round(t_hbm, 5), "prefill_at_mfma_peak_ms": round(t_mfma, 5),
+            "overlap_bound_ms": round(max(t_hbm, t_mfma), 5), "serial_bound_ms": round(t_hbm + t_mfma, 5),
+            "frac_overlap": max(t_hbm, t_mfma) / ms, "frac_serial": (t_hbm + t_mfma) / ms}
         weight = lambda k: kern.get(k, (0, 0.0))[0] * kern.get(k, (0, 0.0))[1]
         dominant = max(("decode_kernel", "prefill_kernel"), key=weight)
         result["roofline"] = roofline_for(dominant, kern[dominant][1], w, w.name)
