@@ -1,5 +1,7 @@
-// MFMA prefill / chunk kernel for pa_attention (bf16/f16, head_dim 128,
-// block_size % 16 == 0): sequences with query_len * G > 16.
+// MFMA prefill / chunk kernel for pa_attention (bf16/f16, head_dim 64, 128
+// or 256, block size a multiple or a divisor of 16): sequences with
+// query_len * G above the decode kernels' rows, and the shared-prefix parts of
+// cascade groups.
 //
 // "vLLM Continuous Batching：从 Forward Shape 理解两个核心参数" §2.3: the rows of
 // a prefill chunk at positions p = seq_len - query_len + i each see positions
@@ -16,14 +18,16 @@
 // global_load_lds_dwordx4 (no register staging); two LDS stages, so the next
 // tile's loads are in flight while the current tile computes, one barrier per
 // tile.
-//   S^T[64 tok][32 rows] = K . Q^T : 4 x 2 tiles of v_mfma_f32_16x16x32,
-//                                    A = K rows from LDS (ds_read_b128)
-//   O^T[128][32 rows]   += V^T . P^T : 8 x 2 tiles of v_mfma_f32_16x16x32
-//                                    per 32 tokens; P^T is the S^T
-//                                    accumulator of two 16-token tiles, used
-//                                    in place; V^T comes from two transposed
-//                                    LDS reads per fragment.
-// Only tiles that cross a wave's diagonal are masked.
+//   S^T[64 tok][32 rows] = K . Q^T : 2 token blocks x D/16 steps of
+//                                    v_mfma_f32_32x32x16, A = K rows from LDS
+//                                    (ds_read_b128), B = the wave's Q^T
+//                                    fragments held in registers
+//   O^T[D][32 rows]     += V^T . P^T : D/32 output blocks x 4 steps of 16
+//                                    tokens; P^T is 8 consecutive S^T results
+//                                    of a lane, converted in place; V^T comes
+//                                    from two transposed LDS reads per operand.
+// Each lane holds one row of its wave, so the softmax of a tile is in-lane
+// work plus one lane swap.  Only tiles that cross a wave's diagonal are masked.
 //
 // Work list: a one-workgroup planning kernel lists every (sequence, query
 // tile) of the prefill class, sorted by its number of K/V tiles, heaviest
