@@ -78,6 +78,10 @@ struct PrefillArgs {
 };
 
 constexpr int kPlanThreads = 1024;
+#ifndef PA_PLAN_CMP_STEP
+#define PA_PLAN_CMP_STEP 1024
+#endif
+constexpr int kCmpStep = PA_PLAN_CMP_STEP;  // block ids a wave compares per step
 constexpr int kPlanBuckets = 2048;  // K/V tile counts; larger ones share the top bucket
 
 struct PlanArgs {
@@ -180,20 +184,31 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(PlanArgs a) {
       common_blocks[s] = c;
     }
     __syncthreads();
-    // first block that differs, one wave per candidate, 1024 blocks per step
-    // with all their loads in flight
+    // first block that differs, one wave per candidate, kCmpStep blocks per
+    // step with all their loads in flight
     for (int32_t s = 1 + wave; s < a.S; s += kPlanThreads / 64) {
       const int32_t n = common_blocks[s];
       if (n <= 1) continue;
       const int32_t* b0 = a.block_tables + static_cast<int64_t>(s - 1) * a.MB;
       const int32_t* b1 = a.block_tables + static_cast<int64_t>(s) * a.MB;
       int32_t first = n;
-      for (int32_t j0 = 0; j0 < n && first == n; j0 += 1024) {
+      for (int32_t j0 = 0; j0 < n && first == n; j0 += kCmpStep) {
+        // unconditional loads (index clamped into the row) first, then the
+        // compares: with the loads under the j < n test the compiler issued
+        // them one pair at a time, waiting for each
+        constexpr int kU = kCmpStep / 64;
+        int32_t x0[kU], x1[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const int32_t j = min(j0 + 64 * u + lane, n - 1);
+          x0[u] = b0[j];
+          x1[u] = b1[j];
+        }
         int32_t mn = n;
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
+        for (int u = 0; u < kU; ++u) {
           const int32_t j = j0 + 64 * u + lane;
-          if (j < n && b0[j] != b1[j]) mn = min(mn, j);
+          if (j < n && x0[u] != x1[u]) mn = min(mn, j);
         }
         first = wave_min_i32(mn);
       }
