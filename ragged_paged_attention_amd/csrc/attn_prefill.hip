@@ -435,9 +435,9 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(PlanArgs a) {
 // of row R sits in slot c ^ swz(R):
 //   K: swz = R & min(D/8 - 1, 15) -> at head_dim 128 the 16 rows one K
 //      fragment read touches use 16 different slots, i.e. all 64 banks once;
-//   V: swz = (R & min(D/16 - 1, 7)) << 1 -> at head_dim 128 the 8 rows of a
-//      half-wave transposed read hit 8 different 32-byte bank groups (chunk
-//      pairs stay adjacent).
+//   V: swz = (R & 3) << 2 (<< 1 at head_dim 64) -> a transposed read takes
+//      4 consecutive rows x 32 bytes per 16 lanes (x 64 bytes per 32 lanes),
+//      and the XOR moves the 4 rows' chunks onto different banks.
 template <int D>
 struct Geom {
   static constexpr int kRowBytes = 2 * D;                 // one token row of one head
