@@ -172,11 +172,14 @@ def cpu_baseline(w, rows_wanted, seed=0):
                       f"NumPy with BLAS pinned to 1 thread"}
 
 
-def work_split(w):
+def work_split(w, one_decode_launch=False):
     """Algorithmic work of each attention kernel of a call: KV/Q/O bytes of
     the sequences each decode kernel takes (query_len * G rows per KV head:
     up to 16 on one tile, 17..32 on two when the max_query_len hint allows
-    them) and causal FLOPs of the prefill-class rest."""
+    them) and causal FLOPs of the prefill-class rest.  one_decode_launch:
+    the call ran only the one-tile decode kernel (with the planning kernel's
+    work list it takes every decode item, those of more than 16 rows in two
+    passes), so it gets all the decode bytes."""
     import numpy as np
     from workloads import accounting
     G = w.num_q_heads // w.num_kv_heads
@@ -189,14 +192,18 @@ def work_split(w):
         return (accounting.kv_read_bytes(sl[sel], w.num_kv_heads, w.head_dim, w.dtype)
                 + 2 * int(ql[sel].sum()) * w.num_q_heads * w.head_dim * es)
 
+    if one_decode_launch:
+        return {"decode_kernel": dec_bytes(rows <= cap), "decode_kernel_2t": 0,
+                "prefill_kernel": accounting.attention_flops(ql[rows > cap], sl[rows > cap], w.num_q_heads,
+                                                             w.head_dim)}
     return {"decode_kernel": dec_bytes(rows <= 16),
             "decode_kernel_2t": dec_bytes((rows > 16) & (rows <= cap)),
             "prefill_kernel": accounting.attention_flops(ql[rows > cap], sl[rows > cap], w.num_q_heads,
                                                          w.head_dim)}
 
 
-def roofline_for(kernel, avg_ms, w, workload_tag):
-    work = work_split(w)
+def roofline_for(kernel, avg_ms, w, workload_tag, one_decode_launch=False):
+    work = work_split(w, one_decode_launch)
     if kernel == "prefill_kernel":
         pre_flops = work[kernel]
         a = pre_flops / (avg_ms / 1e3) / 1e12
@@ -342,7 +349,9 @@ def main():
         ms = timer.time(step, args.steps, args.warmup)
         kern = timer.kernels(rpa, step, args.steps)
         ql = w.step.query_lens
-        split = work_split(w)
+        one = "decode_kernel_2t" not in kern
+        split = work_split(w, one)
+        dec_bytes = split["decode_kernel"] + split["decode_kernel_2t"]
         result.update({
             "value": w.num_tokens / (ms / 1e3), "ms_per_step": ms, "dtype": w.dtype,
             "config": {"workload": "chunked-prefill mixed batch", "seqs": w.num_seqs, "tokens": w.num_tokens,
@@ -351,13 +360,13 @@ def main():
                        "heads_q_kv": [w.num_q_heads, w.num_kv_heads], "head_dim": w.head_dim,
                        "block_size": w.block_size, "pool_blocks": w.num_blocks, "seed": w.seed},
             "kernels_ms_per_step": {k: round(n * avg / args.steps, 5) for k, (n, avg) in kern.items()},
-            "step_work": {"decode_bytes": split["decode_kernel"], "prefill_flops": split["prefill_kernel"]},
+            "step_work": {"decode_bytes": dec_bytes, "prefill_flops": split["prefill_kernel"]},
         })
         # the whole step against the two rooflines: the time the decode bytes
         # need at peak HBM bandwidth and the prefill flops at peak MFMA rate,
         # if the two overlapped perfectly (the larger) or ran one after the
         # other (the sum)
-        t_hbm = split["decode_kernel"] / (HBM_PEAK_GBS * 1e9) * 1e3
+        t_hbm = dec_bytes / (HBM_PEAK_GBS * 1e9) * 1e3
         t_mfma = split["prefill_kernel"] / (BF16_PEAK_TFLOPS * 1e12) * 1e3
         result["step_roofline"] = {
             "decode_at_hbm_peak_ms": round(t_hbm, 5), "prefill_at_mfma_peak_ms": round(t_mfma, 5),
@@ -365,10 +374,10 @@ def main():
             "frac_overlap": max(t_hbm, t_mfma) / ms, "frac_serial": (t_hbm + t_mfma) / ms}
         weight = lambda k: kern.get(k, (0, 0.0))[0] * kern.get(k, (0, 0.0))[1]
         dominant = max(("decode_kernel", "prefill_kernel"), key=weight)
-        result["roofline"] = roofline_for(dominant, kern[dominant][1], w, w.name)
+        result["roofline"] = roofline_for(dominant, kern[dominant][1], w, w.name, one)
         other = "prefill_kernel" if dominant == "decode_kernel" else "decode_kernel"
         if other in kern:
-            result["roofline_other_kernel"] = roofline_for(other, kern[other][1], w, w.name)
+            result["roofline_other_kernel"] = roofline_for(other, kern[other][1], w, w.name, one)
         if not args.no_cpu_baseline:
             result["cpu_baseline"] = cpu_baseline(config(4, poison=False), args.cpu_sample_rows)
         del g, ws, out
@@ -498,12 +507,14 @@ def main():
             "frac_hbm_peak": kv6 / (ms6 / 1e3) / 1e9 / HBM_PEAK_GBS, "kv_bytes": kv6,
             "tokens_per_s": w6.num_tokens / (ms6 / 1e3),
             "kernels_ms": {k: round(avg, 5) for k, (n, avg) in kern6.items()}}
-        split6 = work_split(w6)
+        one6 = "decode_kernel_2t" not in kern6
+        split6 = work_split(w6, one6)
         for kname in ("decode_kernel", "decode_kernel_2t"):
             if kname in kern6:
                 result["verify_kv_read"][kname + "_GBps"] = split6[kname] / (kern6[kname][1] / 1e3) / 1e9
         if args.only == "verify":
-            result["roofline"] = roofline_for("decode_kernel_2t", kern6["decode_kernel_2t"][1], w6, w6.name)
+            k6 = "decode_kernel" if one6 else "decode_kernel_2t"
+            result["roofline"] = roofline_for(k6, kern6[k6][1], w6, w6.name, one6)
         del g6, ws6, out6
         torch.cuda.empty_cache()
 
