@@ -78,10 +78,7 @@ struct PrefillArgs {
 };
 
 constexpr int kPlanThreads = 1024;
-#ifndef PA_PLAN_CMP_STEP
-#define PA_PLAN_CMP_STEP 1024
-#endif
-constexpr int kCmpStep = PA_PLAN_CMP_STEP;  // block ids a wave compares per step
+constexpr int kCmpStep = 2048;  // block ids a wave compares per step (64 registers of loads in flight)
 constexpr int kPlanBuckets = 2048;  // K/V tile counts; larger ones share the top bucket
 
 struct PlanArgs {
@@ -162,13 +159,25 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(PlanArgs a) {
   __shared__ int32_t common_blocks[kCascadeMaxSeqs];  // full blocks shared with sequence s - 1
   __shared__ int32_t chunk_of[kCascadeMaxSeqs];       // first sequence of s's chunk
   __shared__ int32_t n_groups;
+  __shared__ int32_t dhist[2][kDecBuckets];
+  __shared__ int32_t dcur[2][kDecBuckets];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int i = tid; i < kPlanBuckets; i += kPlanThreads) hist[i] = 0;
+  for (int i = tid; i < kDecBuckets; i += kPlanThreads) {
+    dhist[0][i] = 0;
+    dhist[1][i] = 0;
+  }
   if (tid == 0) n_groups = 0;
 
+  // Barriers order global stores too (each waits for this workgroup's stores
+  // to complete), so the stores are placed where little follows them: the
+  // per-sequence prefix records are zeroed up front only when a group is
+  // possible at all, else once at the very end.
+  bool prefix_zero_late = false;
   if (a.cascade_on) {
+    const int32_t thr_blocks = ceil_div(kCascadeMinTiles * kTile, a.bs);
+    bool candidate = false;
     for (int32_t s = tid; s < a.S; s += kPlanThreads) {
-      a.seq_prefix[s] = make_int4(0, 0, 0, 0);
       int32_t c = 0;
       if (s > 0) {
         const int32_t ql0 = a.qsl[s] - a.qsl[s - 1], ql1 = a.qsl[s + 1] - a.qsl[s];
@@ -182,117 +191,122 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(PlanArgs a) {
         }
       }
       common_blocks[s] = c;
+      candidate |= c >= thr_blocks;
     }
-    __syncthreads();
-    // first block that differs, one wave per candidate, kCmpStep blocks per
-    // step with all their loads in flight
-    for (int32_t s = 1 + wave; s < a.S; s += kPlanThreads / 64) {
-      const int32_t n = common_blocks[s];
-      if (n <= 1) continue;
-      const int32_t* b0 = a.block_tables + static_cast<int64_t>(s - 1) * a.MB;
-      const int32_t* b1 = a.block_tables + static_cast<int64_t>(s) * a.MB;
-      int32_t first = n;
-      for (int32_t j0 = 0; j0 < n && first == n; j0 += kCmpStep) {
-        // unconditional loads (index clamped into the row) first, then the
-        // compares: with the loads under the j < n test the compiler issued
-        // them one pair at a time, waiting for each
-        constexpr int kU = kCmpStep / 64;
-        int32_t x0[kU], x1[kU];
+    if (!__syncthreads_or(candidate)) {  // no two neighbours can share enough: no group
+      prefix_zero_late = true;
+      if (tid == 0) a.plan[1] = 0;
+    } else {
+      for (int32_t s = tid; s < a.S; s += kPlanThreads) a.seq_prefix[s] = make_int4(0, 0, 0, 0);
+      // first block that differs, one wave per candidate, kCmpStep blocks per
+      // step with all their loads in flight
+      for (int32_t s = 1 + wave; s < a.S; s += kPlanThreads / 64) {
+        const int32_t n = common_blocks[s];
+        if (n <= 1) continue;
+        const int32_t* b0 = a.block_tables + static_cast<int64_t>(s - 1) * a.MB;
+        const int32_t* b1 = a.block_tables + static_cast<int64_t>(s) * a.MB;
+        int32_t first = n;
+        for (int32_t j0 = 0; j0 < n && first == n; j0 += kCmpStep) {
+          // unconditional loads (index clamped into the row) first, then the
+          // compares: with the loads under the j < n test the compiler issued
+          // them one pair at a time, waiting for each
+          constexpr int kU = kCmpStep / 64;
+          int32_t x0[kU], x1[kU];
 #pragma unroll
-        for (int u = 0; u < kU; ++u) {
-          const int32_t j = min(j0 + 64 * u + lane, n - 1);
-          x0[u] = b0[j];
-          x1[u] = b1[j];
+          for (int u = 0; u < kU; ++u) {
+            const int32_t j = min(j0 + 64 * u + lane, n - 1);
+            x0[u] = b0[j];
+            x1[u] = b1[j];
+          }
+          int32_t mn = n;
+#pragma unroll
+          for (int u = 0; u < kU; ++u) {
+            const int32_t j = j0 + 64 * u + lane;
+            if (j < n && x0[u] != x1[u]) mn = min(mn, j);
+          }
+          first = wave_min_i32(mn);
         }
-        int32_t mn = n;
+        if (lane == 0) common_blocks[s] = first;
+      }
+      __syncthreads();
+      // Groups, in parallel: a run starts at s unless s shares at least
+      // kCascadeMinTiles tiles with s - 1; runs are cut into chunks of at most
+      // kCascadeRows / G members; a chunk of two or more is a group (the first
+      // kCascadeEntries of them), its prefix the fewest blocks any two
+      // neighbours in it share, rounded down to whole tiles.
+      constexpr int kPerS = kCascadeMaxSeqs / kPlanThreads;
+      const int32_t max_members = max(2, kCascadeRows / a.G);
+      int32_t run_start[kPerS], m = -1;
 #pragma unroll
-        for (int u = 0; u < kU; ++u) {
-          const int32_t j = j0 + 64 * u + lane;
-          if (j < n && x0[u] != x1[u]) mn = min(mn, j);
+      for (int j = 0; j < kPerS; ++j) {
+        const int32_t s = kPerS * tid + j;
+        if (s < a.S && (s == 0 || common_blocks[s] < thr_blocks)) m = s;
+        run_start[j] = m;  // latest start within this thread's slice
+      }
+      const int32_t before = plan_block_scan<true>(m, -1, wave_tot);
+#pragma unroll
+      for (int j = 0; j < kPerS; ++j) {
+        const int32_t s = kPerS * tid + j;
+        const int32_t rs = max(run_start[j], before);
+        if (s < a.S) chunk_of[s] = rs + (s - rs) / max_members * max_members;
+      }
+      __syncthreads();
+      int32_t is_group[kPerS], members[kPerS], common[kPerS], n_mine = 0;
+#pragma unroll
+      for (int j = 0; j < kPerS; ++j) {
+        const int32_t s = kPerS * tid + j;
+        is_group[j] = 0;
+        if (s < a.S && chunk_of[s] == s) {
+          int32_t e = s + 1, c = INT32_MAX;
+          while (e < a.S && chunk_of[e] == s) {
+            c = min(c, common_blocks[e]);
+            ++e;
+          }
+          members[j] = e - s;
+          common[j] = c;
+          is_group[j] = e - s >= 2;
+          n_mine += is_group[j];
         }
-        first = wave_min_i32(mn);
       }
-      if (lane == 0) common_blocks[s] = first;
-    }
-    __syncthreads();
-    // Groups, in parallel: a run starts at s unless s shares at least
-    // kCascadeMinTiles tiles with s - 1; runs are cut into chunks of at most
-    // kCascadeRows / G members; a chunk of two or more is a group (the first
-    // kCascadeEntries of them), its prefix the fewest blocks any two
-    // neighbours in it share, rounded down to whole tiles.
-    constexpr int kPerS = kCascadeMaxSeqs / kPlanThreads;
-    const int32_t thr_blocks = ceil_div(kCascadeMinTiles * kTile, a.bs);
-    const int32_t max_members = max(2, kCascadeRows / a.G);
-    int32_t run_start[kPerS], m = -1;
+      int32_t gidx = plan_block_scan<false>(n_mine, 0, wave_tot);
 #pragma unroll
-    for (int j = 0; j < kPerS; ++j) {
-      const int32_t s = kPerS * tid + j;
-      if (s < a.S && (s == 0 || common_blocks[s] < thr_blocks)) m = s;
-      run_start[j] = m;  // latest start within this thread's slice
-    }
-    const int32_t before = plan_block_scan<true>(m, -1, wave_tot);
-#pragma unroll
-    for (int j = 0; j < kPerS; ++j) {
-      const int32_t s = kPerS * tid + j;
-      const int32_t rs = max(run_start[j], before);
-      if (s < a.S) chunk_of[s] = rs + (s - rs) / max_members * max_members;
-    }
-    __syncthreads();
-    int32_t is_group[kPerS], members[kPerS], common[kPerS], n_mine = 0;
-#pragma unroll
-    for (int j = 0; j < kPerS; ++j) {
-      const int32_t s = kPerS * tid + j;
-      is_group[j] = 0;
-      if (s < a.S && chunk_of[s] == s) {
-        int32_t e = s + 1, c = INT32_MAX;
-        while (e < a.S && chunk_of[e] == s) {
-          c = min(c, common_blocks[e]);
-          ++e;
+      for (int j = 0; j < kPerS; ++j) {
+        if (!is_group[j]) continue;
+        if (gidx < a.cap_groups)
+          a.groups[gidx] = make_int4(kPerS * tid + j, members[j], common[j] * a.bs / kTile * kTile, 0);
+        ++gidx;
+      }
+      if (tid == kPlanThreads - 1) n_groups = min(gidx, a.cap_groups);
+      __syncthreads();
+      // parts (up to kCascadeMaxParts of at least kCascadeMinTiles tiles,
+      // kCascadeEntries over all groups) and each group's first prefix slot
+      const int32_t ngr = n_groups;
+      if (wave == 0) {
+        int32_t parts = 0;
+        int4 gr = make_int4(0, 0, 0, 0);
+        if (lane < ngr) {
+          gr = a.groups[lane];
+          parts = max(1, min(min(kCascadeMaxParts, gr.z / kTile / kCascadeMinTiles), kCascadeEntries / ngr));
         }
-        members[j] = e - s;
-        common[j] = c;
-        is_group[j] = e - s >= 2;
-        n_mine += is_group[j];
+        int32_t base = parts;
+        for (int off = 1; off < 64; off <<= 1) {
+          const int32_t y = __shfl_up(base, off, 64);
+          if (lane >= off) base += y;
+        }
+        base -= parts;
+        if (lane < ngr) {
+          gr.w = parts | (base << 8);
+          a.groups[lane] = gr;
+        }
       }
-    }
-    int32_t gidx = plan_block_scan<false>(n_mine, 0, wave_tot);
-#pragma unroll
-    for (int j = 0; j < kPerS; ++j) {
-      if (!is_group[j]) continue;
-      if (gidx < a.cap_groups)
-        a.groups[gidx] = make_int4(kPerS * tid + j, members[j], common[j] * a.bs / kTile * kTile, 0);
-      ++gidx;
-    }
-    if (tid == kPlanThreads - 1) n_groups = min(gidx, a.cap_groups);
-    __syncthreads();
-    // parts (up to kCascadeMaxParts of at least kCascadeMinTiles tiles,
-    // kCascadeEntries over all groups) and each group's first prefix slot
-    const int32_t ngr = n_groups;
-    if (wave == 0) {
-      int32_t parts = 0;
-      int4 gr = make_int4(0, 0, 0, 0);
-      if (lane < ngr) {
-        gr = a.groups[lane];
-        parts = max(1, min(min(kCascadeMaxParts, gr.z / kTile / kCascadeMinTiles), kCascadeEntries / ngr));
+      __syncthreads();
+      for (int32_t gi = wave; gi < ngr; gi += kPlanThreads / 64) {
+        const int4 gr = a.groups[gi];
+        for (int32_t k = lane; k < gr.y; k += 64)
+          a.seq_prefix[gr.x + k] = make_int4(gr.z, gr.w & 255, gr.w >> 8, k * a.G);
       }
-      int32_t base = parts;
-      for (int off = 1; off < 64; off <<= 1) {
-        const int32_t y = __shfl_up(base, off, 64);
-        if (lane >= off) base += y;
-      }
-      base -= parts;
-      if (lane < ngr) {
-        gr.w = parts | (base << 8);
-        a.groups[lane] = gr;
-      }
+      if (tid == 0) a.plan[1] = ngr;
     }
-    __syncthreads();
-    for (int32_t gi = wave; gi < ngr; gi += kPlanThreads / 64) {
-      const int4 gr = a.groups[gi];
-      for (int32_t k = lane; k < gr.y; k += 64)
-        a.seq_prefix[gr.x + k] = make_int4(gr.z, gr.w & 255, gr.w >> 8, k * a.G);
-    }
-    if (tid == 0) a.plan[1] = ngr;
   }
   __syncthreads();
   const int32_t ng = n_groups;
@@ -366,13 +380,8 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(PlanArgs a) {
   // real one.  A sequence the decode kernels only zero-fill (a violated hint,
   // an invalid length or table) gets one part-0 entry in the one-tile list,
   // last.  The max_query_len hint is checked here for every sequence.
-  __shared__ int32_t dhist[2][kDecBuckets];
-  __shared__ int32_t dcur[2][kDecBuckets];
-  for (int i = tid; i < kDecBuckets; i += kPlanThreads) {
-    dhist[0][i] = 0;
-    dhist[1][i] = 0;
-  }
-  __syncthreads();
+  // (dhist was cleared at the start; no barrier here, so the list entries'
+  // stores above need not complete before the decode histogram is built)
   // list c, parts np of cpp chunks over nch chunks; special: one weight-0 part
   auto dec_item = [&](int32_t s, int32_t& c, int32_t& np, int32_t& cpp, int32_t& nch, bool& special) -> bool {
     const int32_t qlen = a.qsl[s + 1] - a.qsl[s];
@@ -387,7 +396,7 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(PlanArgs a) {
     c = rows > 16 ? 1 : 0;
     const int32_t L = a.seq_lens[s];
     if (L < qlen || ceil_div(L, a.bs) > a.MB) return true;
-    const int32_t pre = a.cascade_on ? a.seq_prefix[s].x : 0;
+    const int32_t pre = a.cascade_on && !prefix_zero_late ? a.seq_prefix[s].x : 0;
     nch = ceil_div(L, 16) - pre / 16;
     plan_parts(nch, a.P, &np, &cpp);
     special = false;
@@ -427,6 +436,8 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(PlanArgs a) {
       if (pos < a.cap_dec) list[pos] = make_int2(s, p);
     }
   }
+  if (prefix_zero_late)
+    for (int32_t s = tid; s < a.S; s += kPlanThreads) a.seq_prefix[s] = make_int4(0, 0, 0, 0);
 }
 
 
