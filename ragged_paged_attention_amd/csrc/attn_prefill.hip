@@ -43,15 +43,11 @@
 namespace pa {
 namespace {
 
-#ifndef PA_PREFILL_ROWS_PER_WAVE
-#define PA_PREFILL_ROWS_PER_WAVE 32
-#endif
 #ifndef PA_PREFILL_ROWS_PER_WG
 #define PA_PREFILL_ROWS_PER_WG 128
 #endif
-constexpr int kRowsPerWG = PA_PREFILL_ROWS_PER_WG;      // query rows per workgroup
-constexpr int kRowsPerWave = PA_PREFILL_ROWS_PER_WAVE;  // a multiple of 16
-static_assert(kRowsPerWave == 32, "a wave's rows are the 32 columns of its MFMA tiles");
+constexpr int kRowsPerWG = PA_PREFILL_ROWS_PER_WG;  // query rows per workgroup
+constexpr int kRowsPerWave = 32;                    // the 32 columns of a wave's MFMA tiles
 constexpr int kWaves = kRowsPerWG / kRowsPerWave;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 64;                          // KV tokens per tile
