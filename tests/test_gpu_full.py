@@ -148,3 +148,36 @@ def test_other_shapes(shape):
     _, _, _, ref = oracle.run_step(w)
     assert g.err() == 0
     assert max_abs_err(g.out, ref) <= tol_for("bf16")
+
+
+def test_invalid_block_ids_on_the_mfma_paths():
+    """Block-table entries out of range (-1 and >= num_blocks) in a bf16 batch
+    that runs the decode and prefill kernels: PA_DERR_BLOCK_OOB is raised,
+    every access stays inside the pool (the kernels clamp a bad id to block
+    0 after flagging it), and the sequences whose tables are valid still
+    match the oracle.  The rows of the two damaged sequences are
+    unspecified and not compared."""
+    w = config(4, scale_down=8)
+    g = GpuRun(w).fill_history().write_step_rows()
+    ql, sl = w.step.query_lens, w.step.seq_lens
+    G = w.num_q_heads // w.num_kv_heads
+    dec = [s for s in range(w.num_seqs) if ql[s] == 1]
+    pre = [s for s in range(w.num_seqs) if ql[s] * G > 32]
+    sd = max(dec, key=lambda s: sl[s])                  # a decode row with a long context
+    sp = max(pre, key=lambda s: sl[s])                  # a chunk on the prefill kernel
+    assert sl[sd] > 2 * w.block_size and pre
+    bt = g.db.block_tables.clone()
+    bt[sd, (int(sl[sd]) - 1) // w.block_size // 2] = -1
+    bt[sp, 0] = w.num_blocks + 7
+    print(f"[invalid ids] decode seq {sd} (len {sl[sd]}), prefill seq {sp} (len {sl[sp]})", flush=True)
+    d_err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = rpa.pa_attention(g.db.q, g.k_cache, g.v_cache, bt, g.meta["query_start_loc"], g.db.seq_lens,
+                           max(1, w.max_query_len), max(1, w.max_seq_len), w.scale, d_err=d_err)
+    torch.cuda.synchronize()
+    assert int(d_err.item()) & rpa.PA_DERR_BLOCK_OOB
+    _, _, _, ref = oracle.run_step(w)
+    offs = w.new_row_offsets()
+    keep = np.ones(w.num_tokens, dtype=bool)
+    for s in (sd, sp):
+        keep[int(offs[s]):int(offs[s + 1])] = False
+    assert max_abs_err(out[torch.from_numpy(keep).to("cuda")], ref[keep]) <= tol_for(w.dtype)
