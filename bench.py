@@ -311,7 +311,7 @@ def main():
         summarize_pmc(*args.summarize_pmc, args.command)
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (--gpus {args.gpus} was asked for): this build has no multi-GPU "
+        print(f"bench.py measures one GPU only (--gpus {args.gpus} was asked for): the library has no multi-GPU "
               "path; run it with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch
