@@ -33,7 +33,9 @@ design notes with its justification):
 
 Nothing here is parity-unpinned: tests/test_oracle_pins.py pins every
 function against the pages' worked examples, closed forms, a library routine
-(dense padded masked attention) and brute force.
+(dense padded masked attention) and brute force; the 16-bit widening is
+pinned on all 65,536 bit patterns against the bfloat16 / binary16 bit-field
+definitions and torch's own conversions.
 """
 from __future__ import annotations
 

@@ -225,13 +225,65 @@ def pin_copy_on_write():
     np.testing.assert_array_equal(vc[g["cow_new_block"], n - bs], nv[0])
 
 
-ALL_PINS = [pin_offsets, pin_forward_shape, pin_brute_force, pin_single_key,
+def _decode_16bit(bits: np.ndarray, exp_bits: int, man_bits: int) -> np.ndarray:
+    """Value of each 16-bit pattern from the format's definition: sign bit,
+    `exp_bits` biased exponent bits, `man_bits` stored mantissa bits;
+    exponent field 0 is subnormal (no implicit 1, minimum exponent), the
+    all-ones field is infinity (mantissa 0) or NaN.  Written with integer
+    arithmetic and np.ldexp, so every value is exact in float64."""
+    b = bits.astype(np.int64)
+    sign = np.where(b >> 15, -1.0, 1.0)
+    e = (b >> man_bits) & ((1 << exp_bits) - 1)
+    m = b & ((1 << man_bits) - 1)
+    bias = (1 << (exp_bits - 1)) - 1
+    normal = np.ldexp((m + (1 << man_bits)).astype(np.float64), (e - bias - man_bits).astype(np.int32))
+    sub = np.ldexp(m.astype(np.float64), np.full(b.shape, 1 - bias - man_bits, dtype=np.int32))
+    inf_nan = np.where(m == 0, np.inf, np.nan)
+    top = (1 << exp_bits) - 1
+    return sign * np.where(e == 0, sub, np.where(e == top, inf_nan, normal))
+
+
+def pin_widen():
+    """The exact widening of stored 16-bit values (the pages keep K/V in 16
+    bits, "LLM 推理引擎 Continuous Batching 与 PagedAttention" §1.2): known bit
+    patterns from the bfloat16 (8 exponent, 7 mantissa bits) and IEEE binary16
+    (5, 10) definitions, then every one of the 65,536 patterns against the
+    definition decoded from the bit fields and against torch's own
+    conversion, compared as float64 bit patterns (so -0.0 and 0.0 differ)."""
+    known_bf16 = {0x3F80: 1.0, 0xC040: -3.0, 0x7F7F: float.fromhex("0x1.fep127"), 0x0001: 2.0 ** -133,
+                  0x8000: -0.0, 0x0080: 2.0 ** -126, 0x3E80: 0.25, 0x4049: 3.140625, 0x7F80: np.inf,
+                  0xFF80: -np.inf}
+    known_f16 = {0x3C00: 1.0, 0xC200: -3.0, 0x7BFF: 65504.0, 0x0001: 2.0 ** -24, 0x8000: -0.0,
+                 0x0400: 2.0 ** -14, 0x3555: float.fromhex("0x1.554p-2"), 0x7C00: np.inf, 0xFC00: -np.inf}
+    for dtype, known in (("bf16", known_bf16), ("f16", known_f16)):
+        bits = np.array(sorted(known), dtype=np.uint16)
+        got = PA.widen(bits, dtype)
+        want = np.array([known[int(b)] for b in bits], dtype=np.float64)
+        assert np.array_equal(got.view(np.uint64), want.view(np.uint64)), dtype
+    allbits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    as_i16 = torch.from_numpy(allbits.view(np.int16).copy())
+    for dtype, eb, mb, tdt in (("bf16", 8, 7, torch.bfloat16), ("f16", 5, 10, torch.float16)):
+        with np.errstate(invalid="ignore"):   # signalling-NaN patterns warn when widened
+            got = PA.widen(allbits, dtype)
+        want = _decode_16bit(allbits, eb, mb)
+        lib = as_i16.view(tdt).to(torch.float64).numpy()
+        ok = ~np.isnan(want)
+        assert np.array_equal(np.isnan(got), ~ok), dtype
+        assert np.array_equal(got[ok].view(np.uint64), want[ok].view(np.uint64)), dtype
+        assert np.array_equal(got[ok].view(np.uint64), lib[ok].view(np.uint64)), dtype
+
+
+ALL_PINS = [pin_widen, pin_offsets, pin_forward_shape, pin_brute_force, pin_single_key,
             pin_closed_form_equal_keys, pin_copy_on_write] + [(lambda c=c: pin_dense(c)) for c in DENSE_CASES]
 
 
 # ---------------------------------------------------------------------------
 # tests
 # ---------------------------------------------------------------------------
+def test_widen_16bit_exact():
+    pin_widen()
+
+
 def test_offsets_pages():
     pin_offsets()
 
@@ -550,7 +602,23 @@ def _bad_copy_blocks(src_k, src_v, dst_k, dst_v, pairs):
         dst_k[int(b)] = src_k[int(a)]     # V left behind
 
 
+def _bad_widen_bf16(a, dtype):
+    out = _GOOD_WIDEN(a, dtype)
+    return out * 1.01 if dtype == "bf16" else out
+
+
+def _bad_widen_f16(a, dtype):
+    if dtype != "f16":
+        return _GOOD_WIDEN(a, dtype)
+    # read as bfloat16 bits: a plausible mix-up of the two 16-bit formats
+    return _GOOD_WIDEN(a, "bf16")
+
+
+_GOOD_WIDEN = PA.widen
+
 MUTANTS = {
+    "widen_bf16_one_percent_off": ("widen", _bad_widen_bf16),
+    "widen_f16_read_as_bf16": ("widen", _bad_widen_f16),
     "copy_blocks_drops_v": ("copy_blocks", _bad_copy_blocks),
     "position_off_by_one": ("position_of", _bad_position),
     "gqa_head_mapping_transposed": ("kv_head_of", _bad_kv_head),
