@@ -15,10 +15,19 @@
  *
  * Conventions for every entry point:
  *   - All array arguments are DEVICE pointers to caller-owned, contiguous,
- *     row-major memory.  The library never allocates, frees or synchronises;
- *     all work is enqueued on `stream` (a hipStream_t; NULL = default stream)
- *     and is complete when that stream is.  The caller owns the KV cache (the
- *     engine allocates one pool and hands out per-layer views, [VP] §3.6).
+ *     row-major memory.  The library never allocates or frees device memory
+ *     and never waits for the device on the host; all work is enqueued on
+ *     `stream` (a hipStream_t; NULL = default stream) and is complete when
+ *     that stream is.  The caller owns the KV cache (the engine allocates
+ *     one pool and hands out per-layer views, [VP] §3.6).
+ *   - One exception, in pa_attention only: for a verify-like call (every
+ *     query_len * num_q_heads / num_kv_heads within 32, some above 16) the
+ *     two-tile decode launch runs on a side stream beside the one-tile launch.
+ *     That stream (non-blocking, default priority) and its two events are
+ *     created by the library on the first such call on a device and kept
+ *     until the process ends; the fork from and join back into `stream` are
+ *     event records and waits made under a process-wide lock, so the call
+ *     still completes with `stream`.
  *   - Host-checkable problems (null pointers, bad sizes, unsupported shapes,
  *     a too-small workspace, a failed launch) are returned synchronously as
  *     pa_status_t and nothing is enqueued.
@@ -51,7 +60,8 @@ typedef enum {
   PA_ERR_DTYPE = 3,        /* unknown dtype */
   PA_ERR_UNSUPPORTED = 4,  /* well formed but not implemented (e.g. head_dim > 256) */
   PA_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than pa_attention_workspace_size() */
-  PA_ERR_HIP = 6           /* a HIP runtime call or kernel launch failed */
+  PA_ERR_HIP = 6,          /* a HIP runtime call or kernel launch failed */
+  PA_ERR_VALUE = 7         /* a non-size argument is invalid (a non-finite softmax scale) */
 } pa_status_t;
 
 /* Device-side data-error bits (OR-ed into *d_err). */
@@ -62,7 +72,8 @@ enum {
                                   or the table is too narrow for seq_len */
   PA_DERR_SLOT_OOB = 8,        /* a slot_mapping entry >= num_blocks * block_size */
   PA_DERR_OVERFLOW = 16,       /* a prefix sum exceeds INT32_MAX */
-  PA_DERR_HINT = 32            /* pa_attention: a query_len exceeds the max_query_len hint */
+  PA_DERR_HINT = 32,           /* pa_attention: a query_len exceeds the max_query_len hint */
+  PA_DERR_DUP_SLOT = 64        /* pa_write_kv with validation on: two rows share a slot */
 };
 
 /* Human-readable name of a status code (static storage). */
@@ -85,6 +96,17 @@ int32_t pa_version(void);
  */
 enum { PA_POLICY_AUTO = 0, PA_POLICY_GENERIC = 1, PA_POLICY_FAST = 2 };
 int32_t pa_set_kernel_policy(int32_t policy);
+
+/*
+ * Input validation, process-wide (same thread-safety as the kernel policy):
+ * 1 = on, 0 = off (default).  With it on, pa_write_kv with a non-NULL d_err
+ * also checks that no two rows of the call share an in-range slot and flags
+ * PA_DERR_DUP_SLOT if they do ([VP] §2.1: copy-on-write keeps writers apart,
+ * so a repeated slot is invalid input).  The check is one extra launch of
+ * O(num_tokens^2) compares: a debugging aid.  Returns the previous setting,
+ * or -1 for a value other than 0 or 1 (unchanged).
+ */
+int32_t pa_set_validation(int32_t on);
 
 /*
  * pa_build_metadata — flat-batch metadata of one step.
@@ -138,7 +160,8 @@ pa_status_t pa_build_metadata(const int32_t* query_lens, const int32_t* seq_lens
  * A pure copy: stored bits are moved unchanged; the caches are never read.
  * Slots >= num_blocks * block_size are skipped and flag PA_DERR_SLOT_OOB.
  * Two rows with the same non-negative slot are invalid input (the copy-on-
- * write rule of [VP] §2.1 keeps writers apart); which row wins is unspecified.
+ * write rule of [VP] §2.1 keeps writers apart); which row wins is unspecified,
+ * and with validation on (pa_set_validation) the call flags PA_DERR_DUP_SLOT.
  */
 pa_status_t pa_write_kv(const void* k, const void* v, const int32_t* slot_mapping, int32_t num_tokens,
                         int32_t num_kv_heads, int32_t head_dim, void* k_cache, void* v_cache,
@@ -205,16 +228,20 @@ size_t pa_attention_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t
  *        that sequence's rows are unspecified (computed or zero).  A
  *        sequence longer than max_seq_len is computed correctly (its split
  *        parts just get longer).
- *   scale  softmax scale (1/sqrt(head_dim) in the usual model)
+ *   scale  softmax scale (1/sqrt(head_dim) in the usual model); any finite
+ *        value.  A non-finite scale returns PA_ERR_VALUE.  The MFMA paths
+ *        take scale > 0; a call with scale <= 0 runs on the generic kernel
+ *        (PA_POLICY_FAST: PA_ERR_UNSUPPORTED).
  *   out  [T, num_q_heads, head_dim], `dtype`
  *   workspace: device memory of at least pa_attention_workspace_size() bytes;
  *        contents on entry are irrelevant, on exit unspecified.
  * Arithmetic is fp32 (inputs widened, products and sums in fp32), output
  * rounded to `dtype` (nearest-even).  Supported: num_q_heads % num_kv_heads
- * == 0, 1 <= head_dim <= 256, block_size >= 1.  bf16/fp16 with head_dim 128,
- * block_size a multiple of 16, num_q_heads / num_kv_heads <= 16 and q, the
- * caches, out and workspace 16-byte aligned take the MFMA fast paths;
- * everything else takes a generic fp32 kernel.
+ * == 0, 1 <= head_dim <= 256, block_size >= 1.  bf16/fp16 with head_dim 64,
+ * 128 or 256, a block_size that is a multiple of 16 or divides 16,
+ * num_q_heads / num_kv_heads <= 16, scale > 0 and q, the caches, out and
+ * workspace 16-byte aligned take the MFMA fast paths; everything else takes
+ * a generic fp32 kernel.
  * The caches are never written.  Rows of sequences whose metadata is invalid
  * are written as zeros and flag PA_DERR_*.
  */

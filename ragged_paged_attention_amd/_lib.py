@@ -21,6 +21,7 @@ PA_F32, PA_BF16, PA_F16 = 0, 1, 2
 PA_POLICY_AUTO, PA_POLICY_GENERIC, PA_POLICY_FAST = 0, 1, 2
 PA_DERR_QLEN_GT_SEQLEN, PA_DERR_TOKEN_SUM, PA_DERR_BLOCK_OOB, PA_DERR_SLOT_OOB, PA_DERR_OVERFLOW = 1, 2, 4, 8, 16
 PA_DERR_HINT = 32
+PA_DERR_DUP_SLOT = 64
 
 
 class PAError(RuntimeError):
@@ -59,6 +60,8 @@ _lib.pa_version.restype = _i32
 _lib.pa_version.argtypes = []
 _lib.pa_set_kernel_policy.restype = _i32
 _lib.pa_set_kernel_policy.argtypes = [_i32]
+_lib.pa_set_validation.restype = _i32
+_lib.pa_set_validation.argtypes = [_i32]
 _lib.pa_build_metadata.restype = _i32
 _lib.pa_build_metadata.argtypes = [_p, _p, _i32, _i32, _p, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p]
 _lib.pa_write_kv.restype = _i32
@@ -107,6 +110,10 @@ def pa_version() -> int:
 
 def pa_set_kernel_policy(policy: int) -> int:
     return int(_lib.pa_set_kernel_policy(int(policy)))
+
+
+def pa_set_validation(on: int) -> int:
+    return int(_lib.pa_set_validation(int(on)))
 
 
 # --------------------------------------------------------------------------

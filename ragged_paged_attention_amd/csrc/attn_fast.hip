@@ -38,12 +38,6 @@
 #include "pa_common.h"
 #include "pa_internal.h"
 
-#ifndef PA_DECODE_LIST
-#define PA_DECODE_LIST 1  // decode kernels take the plan's work lists when the plan runs
-#endif
-#ifndef PA_DECODE_2T_SIDE_STREAM
-#define PA_DECODE_2T_SIDE_STREAM 1
-#endif
 
 namespace pa {
 namespace {
@@ -583,7 +577,9 @@ bool fast_path_supported(const AttnArgs& a) {
   const uintptr_t align = reinterpret_cast<uintptr_t>(a.q) | reinterpret_cast<uintptr_t>(a.k_cache) |
                           reinterpret_cast<uintptr_t>(a.v_cache) | reinterpret_cast<uintptr_t>(a.out) |
                           reinterpret_cast<uintptr_t>(a.workspace);
-  return (a.dtype == PA_BF16 || a.dtype == PA_F16) && (a.D == 64 || a.D == 128 || a.D == 256) &&
+  // scale > 0: the prefill kernel takes a tile's row maximum on the raw
+  // scores and scales it afterwards, which needs a positive scale
+  return (a.dtype == PA_BF16 || a.dtype == PA_F16) && (a.D == 64 || a.D == 128 || a.D == 256) && a.scale > 0.f &&
          (a.bs % kChunk == 0 || kChunk % a.bs == 0) && a.Hq / a.Hkv <= kTileRows && align % 16 == 0;
 }
 
@@ -691,7 +687,7 @@ SideStream* side_stream_locked() {
 }
 }  // namespace
 
-hipError_t launch_attn_fast(const AttnArgs& a, hipStream_t stream) {
+hipError_t launch_attn_fast(const AttnArgs& a, hipStream_t stream, bool side_stream_ok) {
   const FastPlan f = fast_plan(a.S, a.T, a.Hq, a.Hkv, a.D, a.max_qlen, a.max_seqlen);
   DecodeArgs d;
   d.q = static_cast<const uint16_t*>(a.q);
@@ -724,7 +720,7 @@ hipError_t launch_attn_fast(const AttnArgs& a, hipStream_t stream) {
   const int64_t items = s_pad * a.Hkv * d.P;
   // with the plan's lists: whole blocks of kXcdRun entries for every head
   const int64_t list_items = (static_cast<int64_t>(a.S) * d.P + kXcdRun - 1) / kXcdRun * kXcdRun * a.Hkv;
-  const int64_t grid_items = f.mfma_prefill && PA_DECODE_LIST ? std::max(items, list_items) : items;
+  const int64_t grid_items = f.mfma_prefill ? std::max(items, list_items) : items;
   const int64_t grid = (grid_items + 8 * kXcdRun - 1) / (8 * kXcdRun) * (8 * kXcdRun);
   if (grid > INT32_MAX) return hipErrorInvalidValue;
   d.n_items = static_cast<int32_t>(items);
@@ -741,17 +737,15 @@ hipError_t launch_attn_fast(const AttnArgs& a, hipStream_t stream) {
     const PlanLayout l = plan_layout(a.S, a.T, f.G, f.P, f.prefill_on, f.cascade_on);
     if (f.cascade_on) d.seq_prefix = reinterpret_cast<const int4*>(reinterpret_cast<const uint8_t*>(plan) + l.seqpre_off);
     const int2* dec = reinterpret_cast<const int2*>(reinterpret_cast<const uint8_t*>(plan) + l.dec_off);
-    if (PA_DECODE_LIST) {
-      d.dec_list[0] = dec;
-      d.dec_list[1] = dec + l.cap_dec;
-      d.dec_n = plan + 2;
-    }
+    d.dec_list[0] = dec;
+    d.dec_list[1] = dec + l.cap_dec;
+    d.dec_n = plan + 2;
   }
   const bool blk16 = a.bs % kChunk == 0;
   std::unique_lock<std::mutex> side_lock(g_side_mu, std::defer_lock);
   SideStream* side = nullptr;
   hipStream_t s2 = stream;  // the two-tile launch's stream
-  if (d.rows_cap > kTileRows && !f.prefill_on && PA_DECODE_2T_SIDE_STREAM) {
+  if (d.rows_cap > kTileRows && !f.prefill_on && side_stream_ok) {
     side_lock.lock();
     side = side_stream_locked();
     if (side && hipEventRecord(side->fork, stream) == hipSuccess &&

@@ -12,8 +12,9 @@
 // LDS, the wave agrees on the chunk max, and then all lanes accumulate
 // p_j * V[j] over the chunk with lane = head-dim element, so the V reads of one
 // key are coalesced across the wave.  This is the correctness path (fp32
-// inputs, odd shapes, tiny batches); the MFMA kernels handle bf16/f16 at
-// head_dim 128.
+// inputs, odd shapes, tiny batches, scale <= 0); the MFMA kernels handle
+// bf16/f16 at head_dim 64, 128 and 256 with block sizes that are multiples or
+// divisors of 16.
 #include "pa_common.h"
 #include "pa_internal.h"
 

@@ -43,19 +43,13 @@
 namespace pa {
 namespace {
 
-#ifndef PA_PREFILL_ROWS_PER_WG
-#define PA_PREFILL_ROWS_PER_WG 128
-#endif
-constexpr int kRowsPerWG = PA_PREFILL_ROWS_PER_WG;  // query rows per workgroup
+constexpr int kRowsPerWG = 128;                    // query rows per workgroup
 constexpr int kRowsPerWave = 32;                    // the 32 columns of a wave's MFMA tiles
 constexpr int kWaves = kRowsPerWG / kRowsPerWave;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 64;                          // KV tokens per tile
 constexpr float kRescaleSlack = 8.f;               // log2 units the running max may lag
-#ifndef PA_PREFILL_QT_RUN
-#define PA_PREFILL_QT_RUN 4
-#endif
-constexpr int kQtRun = PA_PREFILL_QT_RUN;           // query tiles of one (sequence, head) per XCD run
+constexpr int kQtRun = 4;                          // query tiles of one (sequence, head) per XCD run
 
 struct PrefillArgs {
   const uint16_t* q;
@@ -133,8 +127,9 @@ __device__ int32_t plan_block_scan(int32_t v, int32_t id, int32_t* wbuf) {
 
 // One workgroup plans the call.
 //
-// Cascade groups ("vLLM 原理" §2.1 and the prefix caching of
-// "LLM 推理引擎 Continuous Batching 与 PagedAttention" §5: sequences whose
+// Cascade groups ("vLLM 原理" §2.1 and the shared prefixes and automatic
+// prefix caching of "LLM 推理引擎 Continuous Batching 与 PagedAttention"
+// §4.1, §4.2: sequences whose
 // tables map the same physical block at the same logical position share that
 // block's contents): maximal runs of consecutive single-token decode
 // sequences whose tables agree on at least kCascadeMinTiles full 64-token
@@ -472,19 +467,17 @@ struct Geom {
 // Waves per SIMD the register budget is set for: head_dim 256 (O of 32 rows
 // x 256 columns, twice the Q fragments) runs one wave per SIMD, and one
 // workgroup per CU (its two LDS stages take 128 KB).
-#ifndef PA_PREFILL_WAVES_PER_EU
-#define PA_PREFILL_WAVES_PER_EU (kWaves / 2)  // two workgroups per CU
-#endif
+constexpr int kWavesPerEU = kWaves / 2;  // two workgroups per CU
 template <int D>
 constexpr int prefill_waves_per_eu() {
-  return D == 256 ? 1 : PA_PREFILL_WAVES_PER_EU;
+  return D == 256 ? 1 : kWavesPerEU;
 }
 
 // kBlk16: the block size is a multiple of 16 (a wave's 16-row group lies in
 // one block); otherwise it divides 16 and each row finds its own block.
 // D: head_dim (64, 128, 256).
 template <class F, bool kBlk16, int D>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(prefill_waves_per_eu<D>(), PA_PREFILL_WAVES_PER_EU))) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(prefill_waves_per_eu<D>(), kWavesPerEU))) void prefill_kernel(PrefillArgs a) {
   using M = Mma<F>;
   using Gm = Geom<D>;
   constexpr int kRowBytes = Gm::kRowBytes, kTileBytes = Gm::kTileBytes, kStageBytes = Gm::kStageBytes;

@@ -3,6 +3,7 @@
 
 #include "pa_bench.h"
 #include "pa_common.h"
+#include "pa_internal.h"
 
 namespace pa {
 namespace {
@@ -29,8 +30,6 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const uint4* __restric
   if ((threadIdx.x & 63) == 0 && acc == 0x9e3779b9u) atomicOr(sink, acc);  // data-dependent, never elided
 }
 
-constexpr int kPartChunks = 48;
-
 // One wave per (sequence, head, part of <= 48 chunks of 16 tokens); the same
 // lane -> (token, 16 bytes) mapping as the decode kernel's K and V loads.
 __global__ __launch_bounds__(64) void paged_read_kernel(const uint16_t* __restrict__ k_cache,
@@ -44,9 +43,9 @@ __global__ __launch_bounds__(64) void paged_read_kernel(const uint16_t* __restri
   const int32_t s = item % S, g = (item / S) % Hkv, part = item / S / Hkv;
   const int32_t L = seq_lens[s];
   const int32_t nchunks = ceil_div(L, 16);
-  const int32_t c0 = part * kPartChunks;
+  const int32_t c0 = part * pa::kPartChunks;
   if (c0 >= nchunks || part >= P) return;
-  const int32_t c1 = min(nchunks, c0 + kPartChunks);
+  const int32_t c1 = min(nchunks, c0 + pa::kPartChunks);
   const int64_t slot_stride = static_cast<int64_t>(Hkv) * 128;
   const int32_t* bt = block_tables + static_cast<int64_t>(s) * MB;
   const int32_t cpb = bs / 16;

@@ -5,6 +5,7 @@
 
 #include <atomic>
 #include <climits>
+#include <cmath>
 #include <cstdio>
 
 #include "pa.h"
@@ -13,6 +14,7 @@
 namespace {
 
 std::atomic<int32_t> g_policy{PA_POLICY_AUTO};
+std::atomic<int32_t> g_validate{0};
 thread_local char g_last_hip_error[256] = "";
 
 // Clears an error left behind by earlier, unrelated HIP calls in this thread,
@@ -31,6 +33,55 @@ int64_t elem_bytes(pa_dtype_t d) { return d == PA_F32 ? 4 : 2; }
 
 }  // namespace
 
+namespace pa {
+
+// Argument checks and path selection shared by pa_attention and
+// pa_attention_noalloc.  scratch: a workspace the library owns (its size is
+// a.workspace_bytes); the caller's workspace arguments are then not used, and
+// a call that would need more is refused with PA_ERR_WORKSPACE before any
+// other HIP call is made.
+pa_status_t attention_entry(AttnArgs a, const ScratchSource* scratch, hipStream_t stream) {
+  if (bad_dtype(a.dtype)) return PA_ERR_DTYPE;
+  if (a.S < 0 || a.T < 0 || a.Hq < 1 || a.Hkv < 1 || a.D < 1 || a.bs < 1 || a.NB < 1 || a.MB < 0)
+    return PA_ERR_SHAPE;
+  if (a.Hq % a.Hkv != 0) return PA_ERR_SHAPE;
+  if (static_cast<int64_t>(a.NB) * a.bs > INT32_MAX) return PA_ERR_SHAPE;
+  if (a.Hq > 65535) return PA_ERR_UNSUPPORTED;
+  if (a.D > 256) return PA_ERR_UNSUPPORTED;
+  if (a.T == 0) return PA_OK;
+  if (a.S == 0) return PA_ERR_SHAPE;
+  if (a.max_qlen < 1 || a.max_seqlen < 1) return PA_ERR_SHAPE;
+  if (!std::isfinite(a.scale)) return PA_ERR_VALUE;
+  if (!a.q || !a.k_cache || !a.v_cache || !a.block_tables || !a.qsl || !a.seq_lens || !a.out)
+    return PA_ERR_NULL;
+
+  const int32_t policy = g_policy.load();
+  const size_t need = fast_workspace_bytes(a.S, a.T, a.Hq, a.Hkv, a.D, a.max_qlen, a.max_seqlen);
+  if (scratch) {
+    // the workspace is the library's static scratch: check the size first,
+    // then look the device's copy up (alignment is checked on its address)
+    if (need > scratch->bytes) return PA_ERR_WORKSPACE;
+    void* p = nullptr;
+    const pa_status_t st = scratch->lookup(&p);
+    if (st != PA_OK) return st;
+    a.workspace = p;
+    a.workspace_bytes = scratch->bytes;
+  }
+  const bool fast_ok = fast_path_supported(a);
+  hipError_t e;
+  clear_stale_error();
+  if (policy == PA_POLICY_GENERIC || (policy == PA_POLICY_AUTO && !fast_ok)) {
+    e = launch_attn_generic(a, stream);
+  } else {
+    if (!fast_ok) return PA_ERR_UNSUPPORTED;
+    if (need > 0 && (!a.workspace || a.workspace_bytes < need)) return PA_ERR_WORKSPACE;
+    e = launch_attn_fast(a, stream, /*side_stream_ok=*/scratch == nullptr);
+  }
+  return hip_status(e, "pa_attention");
+}
+
+}  // namespace pa
+
 extern "C" {
 
 const char* pa_status_string(pa_status_t s) {
@@ -42,6 +93,7 @@ const char* pa_status_string(pa_status_t s) {
     case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: shape or dtype not implemented";
     case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing or too small";
     case PA_ERR_HIP: return "PA_ERR_HIP: HIP runtime or launch failure";
+    case PA_ERR_VALUE: return "PA_ERR_VALUE: invalid argument value";
   }
   return "PA_ERR_UNKNOWN";
 }
@@ -49,6 +101,11 @@ const char* pa_status_string(pa_status_t s) {
 int32_t pa_version(void) { return 100; }
 
 const char* pa_last_hip_error(void) { return g_last_hip_error; }
+
+int32_t pa_set_validation(int32_t on) {
+  if (on != 0 && on != 1) return -1;
+  return g_validate.exchange(on);
+}
 
 int32_t pa_set_kernel_policy(int32_t policy) {
   if (policy != PA_POLICY_AUTO && policy != PA_POLICY_GENERIC && policy != PA_POLICY_FAST) return -1;
@@ -94,7 +151,7 @@ pa_status_t pa_write_kv(const void* k, const void* v, const int32_t* slot_mappin
   clear_stale_error();
   hipError_t e = pa::launch_write_kv(k, v, slot_mapping, num_tokens, row_bytes, k_cache, v_cache,
                                      static_cast<int64_t>(num_blocks) * block_size, d_err,
-                                     static_cast<hipStream_t>(stream));
+                                     g_validate.load() != 0, static_cast<hipStream_t>(stream));
   return hip_status(e, "pa_write_kv");
 }
 
@@ -132,38 +189,11 @@ pa_status_t pa_attention(const void* q, const void* k_cache, const void* v_cache
                          int32_t max_query_len, int32_t max_seq_len, float scale, pa_dtype_t dtype,
                          void* out, void* workspace, size_t workspace_bytes, int32_t* d_err,
                          void* stream) {
-  if (bad_dtype(dtype)) return PA_ERR_DTYPE;
-  if (num_seqs < 0 || num_tokens < 0 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1 ||
-      block_size < 1 || num_blocks < 1 || max_blocks_per_seq < 0)
-    return PA_ERR_SHAPE;
-  if (num_q_heads % num_kv_heads != 0) return PA_ERR_SHAPE;
-  if (static_cast<int64_t>(num_blocks) * block_size > INT32_MAX) return PA_ERR_SHAPE;
-  if (num_q_heads > 65535) return PA_ERR_UNSUPPORTED;
-  if (head_dim > 256) return PA_ERR_UNSUPPORTED;
-  if (num_tokens == 0) return PA_OK;
-  if (num_seqs == 0) return PA_ERR_SHAPE;
-  if (max_query_len < 1 || max_seq_len < 1) return PA_ERR_SHAPE;
-  if (!q || !k_cache || !v_cache || !block_tables || !query_start_loc || !seq_lens || !out)
-    return PA_ERR_NULL;
-
   pa::AttnArgs a{q, k_cache, v_cache, block_tables, query_start_loc, seq_lens,
                  num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim, block_size,
                  num_blocks, max_blocks_per_seq, max_query_len, max_seq_len, scale, dtype,
                  out, workspace, workspace_bytes, d_err};
-  const int32_t policy = g_policy.load();
-  const bool fast_ok = pa::fast_path_supported(a);
-  hipError_t e;
-  clear_stale_error();
-  if (policy == PA_POLICY_GENERIC || (policy == PA_POLICY_AUTO && !fast_ok)) {
-    e = pa::launch_attn_generic(a, static_cast<hipStream_t>(stream));
-  } else {
-    if (!fast_ok) return PA_ERR_UNSUPPORTED;
-    const size_t need = pa::fast_workspace_bytes(num_seqs, num_tokens, num_q_heads, num_kv_heads,
-                                                 head_dim, max_query_len, max_seq_len);
-    if (need > 0 && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE;
-    e = pa::launch_attn_fast(a, static_cast<hipStream_t>(stream));
-  }
-  return hip_status(e, "pa_attention");
+  return pa::attention_entry(a, nullptr, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

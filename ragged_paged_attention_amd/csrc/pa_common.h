@@ -60,7 +60,7 @@ __device__ __forceinline__ void flag(int32_t* d_err, int32_t bits) {
 __host__ __device__ __forceinline__ int32_t ceil_div(int32_t a, int32_t b) { return (a + b - 1) / b; }
 
 // ---------------------------------------------------------------------------
-// wave64 reductions (DPP row ops within 16 lanes, then cross-row swaps)
+// wave64 reductions: butterfly over lane distances 32..1 with __shfl_xor
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float wave_max(float v) {
   for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));

@@ -24,7 +24,7 @@ hipError_t launch_metadata(const int32_t* query_lens, const int32_t* seq_lens, i
 // write_kv.hip
 hipError_t launch_write_kv(const void* k, const void* v, const int32_t* slot_mapping, int32_t T,
                            int64_t row_bytes, void* k_cache, void* v_cache, int64_t num_slots,
-                           int32_t* d_err, hipStream_t stream);
+                           int32_t* d_err, bool validate, hipStream_t stream);
 
 // copy_blocks.hip
 hipError_t launch_copy_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_v, int32_t src_nb,
@@ -53,11 +53,24 @@ hipError_t launch_attn_generic(const AttnArgs& a, hipStream_t stream);
 // Same kernel, skipping rows of sequences with query_len * (Hq/Hkv) <= skip_rows_le.
 hipError_t launch_attn_generic_rows(const AttnArgs& a, int32_t skip_rows_le, hipStream_t stream);
 
-// attn_fast.hip: bf16/f16, head_dim 128, block_size % 16 == 0.
+// attn_fast.hip: bf16/f16, head_dim 64/128/256, a block size that is a
+// multiple or a divisor of 16, G <= 16, scale > 0, 16-byte aligned buffers.
 bool fast_path_supported(const AttnArgs& a);
 size_t fast_workspace_bytes(int32_t S, int32_t T, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_q,
                             int32_t max_seqlen);
-hipError_t launch_attn_fast(const AttnArgs& a, hipStream_t stream);
+// side_stream_ok: the two-tile decode launch of a verify-like call may run on
+// the library's side stream (created on first use); false keeps every launch
+// on `stream`.
+hipError_t launch_attn_fast(const AttnArgs& a, hipStream_t stream, bool side_stream_ok);
+
+// A workspace owned by the library (pa_attention_noalloc): its size, and how
+// to find the current device's copy.
+struct ScratchSource {
+  size_t bytes;
+  pa_status_t (*lookup)(void** ptr);
+};
+// pa_api.cpp: checks, path selection and launches of one attention call.
+pa_status_t attention_entry(AttnArgs a, const ScratchSource* scratch, hipStream_t stream);
 
 // attn_prefill.hip: rows of sequences with query_len * (Hq/Hkv) > min_rows.
 // Work plan of one call on the MFMA paths, written to the workspace by the

@@ -63,12 +63,46 @@ __global__ __launch_bounds__(256) void write_kv_kernel(
   }
 }
 
+// Validation (pa_set_validation): flags PA_DERR_DUP_SLOT when two rows of
+// one write carry the same in-range slot ("vLLM 原理" §2.1: copy-on-write
+// keeps any two writers off one block, so a repeated slot is a caller bug).
+// Row t compares its slot with every row before it: rows are taken 256 at a
+// time into LDS and read back as broadcasts.  O(T^2 / 2) compares in all; a
+// debugging aid, off by default.
+constexpr int kDupRows = 256;
+__global__ __launch_bounds__(kDupRows) void dup_slot_kernel(const int32_t* __restrict__ slot_mapping, int32_t T,
+                                                          int64_t num_slots, int32_t* __restrict__ d_err) {
+  __shared__ int32_t tile[kDupRows];
+  const int32_t t = static_cast<int32_t>(blockIdx.x) * kDupRows + static_cast<int32_t>(threadIdx.x);
+  const int32_t mine = t < T ? slot_mapping[t] : -1;
+  const bool live = mine >= 0 && mine < num_slots;
+  bool dup = false;
+  // every row before this workgroup's last row; the trip count is uniform
+  const int32_t end = min(T, (static_cast<int32_t>(blockIdx.x) + 1) * kDupRows);
+  for (int32_t base = 0; base < end; base += kDupRows) {
+    __syncthreads();
+    tile[threadIdx.x] = base + static_cast<int32_t>(threadIdx.x) < T ? slot_mapping[base + threadIdx.x] : -1;
+    __syncthreads();
+    if (live) {
+      const int32_t n = min(kDupRows, t - base);  // rows u < t of this tile
+      for (int32_t j = 0; j < n; ++j) dup |= tile[j] == mine;
+    }
+  }
+  if (dup) flag(d_err, PA_DERR_DUP_SLOT);
+}
+
 }  // namespace
 
 hipError_t launch_write_kv(const void* k, const void* v, const int32_t* slot_mapping, int32_t T,
                            int64_t row_bytes, void* k_cache, void* v_cache, int64_t num_slots,
-                           int32_t* d_err, hipStream_t stream) {
+                           int32_t* d_err, bool validate, hipStream_t stream) {
   if (T == 0 || row_bytes == 0) return hipSuccess;
+  if (validate && d_err) {
+    launch_mark("dup_slot_kernel", stream);
+    dup_slot_kernel<<<static_cast<unsigned>((static_cast<int64_t>(T) + kDupRows - 1) / kDupRows), kDupRows, 0,
+                      stream>>>(slot_mapping, T, num_slots, d_err);
+    launch_done(stream);
+  }
   const uintptr_t align = reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v) |
                           reinterpret_cast<uintptr_t>(k_cache) | reinterpret_cast<uintptr_t>(v_cache) |
                           static_cast<uintptr_t>(row_bytes);

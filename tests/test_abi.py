@@ -24,8 +24,14 @@ def test_library_loads_and_exports_all_declared_symbols():
 
 def test_version_and_status_strings():
     assert rpa.pa_version() >= 100
-    for code in range(7):
+    for code in range(8):
         assert rpa.status_string(code).startswith("PA_")
+
+
+def test_validation_switch_roundtrip():
+    prev = rpa.pa_set_validation(1)
+    assert rpa.pa_set_validation(prev) == 1
+    assert rpa.pa_set_validation(2) == -1
 
 
 def test_kernel_policy_roundtrip():
@@ -53,6 +59,8 @@ def test_host_side_rejections_need_no_gpu():
     assert att(T=0) == 0                  # empty batch: nothing to do
     assert att() == 1                     # null pointers
     assert att(max_q=0) == 2              # size hints must be >= 1
+    assert att(scale=float("nan")) == 7   # non-finite softmax scale
+    assert att(scale=float("inf")) == 7
     assert lib.pa_attention_workspace_size(4, 100, 32, 32, 128, 1, 2001) >= 0
     cp = lambda nsrc=4, ndst=4, n=1, bb=8192, ptr=16: lib.pa_copy_blocks(ptr, ptr, ptr, ptr, nsrc, ndst, ptr, n, bb,
                                                                           NULL, NULL)
@@ -64,5 +72,5 @@ def test_host_side_rejections_need_no_gpu():
     assert cp(n=0, ptr=None) == 0         # nothing to copy
 
 
-def _attn_args(T=3, Hq=4, Hkv=2, D=16, max_q=2, S=2):
-    return [None] * 6 + [S, T, Hq, Hkv, D, 16, 8, 4, max_q, 8, ctypes.c_float(0.25), 1, None, None, 0, None, None]
+def _attn_args(T=3, Hq=4, Hkv=2, D=16, max_q=2, S=2, scale=0.25):
+    return [None] * 6 + [S, T, Hq, Hkv, D, 16, 8, 4, max_q, 8, ctypes.c_float(scale), 1, None, None, 0, None, None]

@@ -3,9 +3,12 @@ bench.py times, plus edge cases.
 
 Full sizes: metadata compared in full (bit-exact), the pool compared in full
 (bit-exact, NaN poison included) for the decode and shared-prefix batches,
-attention compared on sampled rows the oracle computes one by one (first and
-last rows, query-tile and KV-tile boundaries, the longest sequences, random
-rows) to the dtype's tolerance.
+attention compared to the dtype's tolerance on every row of the ragged
+prefill, decode and shared-prefix batches and on the longest chunks and
+decodes of the chunked mixed batch, with the fast kernels forced and checked
+to have run; the same batches again with one dominant key planted per
+(sequence, KV head), which a wrong-block read cannot hide under the
+tolerance.
 """
 import numpy as np
 import pytest
@@ -14,30 +17,46 @@ import torch
 import oracle
 import ragged_paged_attention_amd as rpa
 from tests.gpu_path import GpuRun, max_abs_err, tol_for
-from workloads import Batch, Workload, config, random_batch
+from workloads import Batch, Workload, config, plant_needles, random_batch
 from workloads.device import to_numpy_bits
 from workloads.generators import _pad_tables
 
 pytestmark = pytest.mark.gpu
 
 
-def _sample_rows(w, n_random=12, seed=0):
-    rng = np.random.default_rng(seed)
-    offs = w.new_row_offsets()
-    rows = {0, w.num_tokens - 1}
+_WORKLOADS = {}
+
+
+def _full(n):
+    """The full-size workload n, generated once per module (the decode batch's
+    3.3 GB of history takes a while to draw)."""
+    if n not in _WORKLOADS:
+        _WORKLOADS[n] = config(n)
+    return _WORKLOADS[n]
+
+
+def _rows_for(w, n):
+    """Rows compared against the oracle: every row of the ragged prefill, the
+    decode and the shared-prefix batches; for the chunked mixed batch every
+    row of its two longest chunks and of its 32 longest decodes, plus the
+    first and last rows."""
+    if n != 4:
+        return None
     ql, sl = w.step.query_lens, w.step.seq_lens
-    for s in np.argsort(-sl)[:4]:                        # longest contexts
-        rows.add(int(offs[s + 1]) - 1)
-    for s in range(w.num_seqs):                           # tile boundaries inside long chunks
-        q = int(ql[s])
-        for i in (31, 32, 127, 128, 255, 256, q - 2):
-            if 0 <= i < q:
-                rows.add(int(offs[s]) + i)
-    rows |= set(int(x) for x in rng.choice(w.num_tokens, size=min(n_random, w.num_tokens), replace=False))
-    rows = sorted(rows)
-    if len(rows) > 48:
-        rows = sorted(rng.choice(rows, size=48, replace=False).tolist())
-    return rows
+    offs = w.new_row_offsets()
+    chunks = [s for s in np.argsort(-sl, kind="stable") if ql[s] > 1][:2]
+    decodes = [s for s in np.argsort(-sl, kind="stable") if ql[s] == 1][:32]
+    rows = {0, w.num_tokens - 1}
+    for s in list(chunks) + list(decodes):
+        rows |= set(range(int(offs[s]), int(offs[s + 1])))
+    return sorted(rows)
+
+
+# kernels each full-size batch must run on the MFMA paths (and the generic
+# kernel must not run)
+_EXPECTED_KERNELS = {2: {"prefill_kernel"}, 3: {"decode_kernel", "merge_kernel"},
+                     4: {"decode_kernel", "prefill_kernel", "merge_kernel"},
+                     5: {"decode_kernel", "prefill_kernel", "merge_kernel"}}
 
 
 def _bits(a):
@@ -45,25 +64,67 @@ def _bits(a):
     return a.view(np.uint32) if a.dtype == np.float32 else a.view(np.uint16)
 
 
+def _run_fast(w):
+    """The step through the C ABI with the fast paths forced (a call they do
+    not support fails instead of falling back), timing which kernels ran."""
+    prev = rpa.pa_set_kernel_policy(rpa.PA_POLICY_FAST)
+    try:
+        g = GpuRun(w).fill_history()
+        torch.cuda.synchronize()
+        rpa.pa_bench_timing_begin()
+        g.step()
+        torch.cuda.synchronize()
+        kernels = set(rpa.pa_bench_timing_end())
+    finally:
+        rpa.pa_set_kernel_policy(prev)
+    return g, kernels
+
+
+def _compare(w, n, g, rows, label):
+    md, kc, vc, ref = oracle.run_step(w, rows=rows)
+    got = g.out if rows is None else g.out[torch.tensor(rows, device="cuda")]
+    err = max_abs_err(got, ref)
+    print(f"[full] config {n} {label}: {len(ref)} rows compared, max_abs_err={err:.3e}, "
+          f"max|ref|={float(np.max(np.abs(ref))):.3f}", flush=True)
+    assert err <= tol_for(w.dtype)
+    assert torch.isfinite(g.out).all()
+    return md, kc, vc
+
+
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("n", [2, 3, 4, 5])
 def test_full_size_config(n):
-    w = config(n)
+    w = _full(n)
     print(f"[full] config {n} {w.summary()}", flush=True)
-    rows = _sample_rows(w)
-    g = GpuRun(w).run()
-    torch.cuda.synchronize()
-    md, kc, vc, ref = oracle.run_step(w, rows=rows)
+    rows = _rows_for(w, n)
+    g, kernels = _run_fast(w)
+    print(f"[full] config {n}: kernels {sorted(kernels)}", flush=True)
+    assert _EXPECTED_KERNELS[n] <= kernels and "attn_generic_kernel" not in kernels
     assert g.err() == 0
+    md, kc, vc = _compare(w, n, g, rows, "N(0,1) data")
     for name in ("query_start_loc", "seq_start_loc", "positions", "token_to_seq", "slot_mapping", "stats"):
         assert np.array_equal(g.meta[name].cpu().numpy(), getattr(md, name)), name
     if n in (3, 5):
         assert np.array_equal(_bits(to_numpy_bits(g.k_cache)), _bits(kc)), "k_cache differs"
         assert np.array_equal(_bits(to_numpy_bits(g.v_cache)), _bits(vc)), "v_cache differs"
-    got = g.out[torch.tensor(rows, device="cuda")]
-    err = max_abs_err(got, ref)
-    print(f"[full] config {n}: {len(rows)} sampled rows, max_abs_err={err:.3e}", flush=True)
-    assert err <= tol_for(w.dtype)
-    assert torch.isfinite(g.out).all()
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("n", [3, 4, 5])
+def test_full_size_needles(n):
+    """Each sequence reads only its own blocks, which sit anywhere in the pool
+    ("vLLM Continuous Batching：从 Forward Shape 理解两个核心参数" §2.3补充).
+    With one dominant key per (sequence, KV head) every output row is that
+    key's V row, so a block read from the wrong place (a wrong id in the
+    decode kernel's block-id window, a misrouted shared prefix) moves a row by
+    O(1) instead of hiding under the tolerance."""
+    w = plant_needles(_full(n), seed=100 + n)
+    print(f"[needles] config {n} {w.summary()}", flush=True)
+    rows = _rows_for(w, n)
+    g, kernels = _run_fast(w)
+    assert _EXPECTED_KERNELS[n] <= kernels and "attn_generic_kernel" not in kernels
+    assert g.err() == 0
+    _compare(w, n, g, rows, "needles")
 
 
 def test_empty_batch_is_a_no_op():
@@ -122,19 +183,26 @@ def test_small_hints_flagged_and_still_correct_when_covered():
     assert max_abs_err(out, ref) <= tol_for(w.dtype)
 
 
-def test_very_long_decode_context_beyond_part_cap():
-    """A 60,001-token context needs more than 64 parts of 768 tokens: parts
-    get longer instead, and the result stays exact."""
-    L = 60001
+@pytest.mark.parametrize("needles", [False, True])
+def test_very_long_decode_context_beyond_part_cap(needles):
+    """A 70,001-token context needs more than 64 parts of 768 tokens: parts
+    get longer instead (69 blocks each, so the decode kernel's 64-entry
+    block-id window is refetched inside a part), and the result stays exact;
+    with a planted dominant key, a wrong id after the refetch would show."""
+    L = 70001
     bs = 16
     nb = -(-L // bs)
     rng = np.random.default_rng(9)
     tables = [[int(x) for x in rng.permutation(nb + 8)[:nb]]]
     w = _explicit("bf16", 4, 1, 128, bs, nb + 8, [1], [L], tables, 11)
+    if needles:
+        w = plant_needles(w, seed=12)
     g = GpuRun(w).run()
     _, _, _, ref = oracle.run_step(w)
     assert g.err() == 0
-    assert max_abs_err(g.out, ref) <= tol_for("bf16")
+    err = max_abs_err(g.out, ref)
+    print(f"[long] L={L} needles={needles} max_abs_err={err:.3e} max|ref|={float(np.abs(ref).max()):.3f}", flush=True)
+    assert err <= tol_for("bf16")
 
 
 @pytest.mark.parametrize("shape", [dict(Hq=64, Hkv=1, D=128, bs=16),   # G = 64 > 16: generic path

@@ -183,16 +183,86 @@ def test_error_flags_from_host_forced_data():
 
 
 def test_workspace_too_small_is_rejected():
-    w = config(3, scale_down=8)
+    """A mixed batch needs workspace (the work plan and split-K partials); one
+    byte less is refused with PA_ERR_WORKSPACE and nothing runs."""
+    w = config(4, scale_down=8)
     g = GpuRun(w).fill_history()
     need = rpa.pa_attention_workspace_size(w.num_seqs, w.num_tokens, w.num_q_heads, w.num_kv_heads,
                                            w.head_dim, w.max_query_len, w.max_seq_len)
-    if need == 0:
-        pytest.skip("this shape needs no workspace")
+    assert need > 0
     md = rpa.pa_build_metadata(g.db.query_lens, g.db.seq_lens, w.num_tokens, g.db.block_tables, w.block_size,
                                w.num_blocks)
     small = torch.empty(need - 1, dtype=torch.uint8, device="cuda")
+    out = torch.full_like(g.db.q, 3.0)
     with pytest.raises(rpa.PAError) as e:
         rpa.pa_attention(g.db.q, g.k_cache, g.v_cache, g.db.block_tables, md["query_start_loc"], g.db.seq_lens,
-                         w.max_query_len, w.max_seq_len, w.scale, workspace=small)
+                         w.max_query_len, w.max_seq_len, w.scale, out=out, workspace=small)
     assert e.value.status == 5
+    torch.cuda.synchronize()
+    assert bool((out == 3.0).all())
+
+
+class _Scaled:
+    """A workload seen with another softmax scale (same data)."""
+
+    def __init__(self, w, scale):
+        self._w, self.scale = w, scale
+
+    def __getattr__(self, name):
+        return getattr(self._w, name)
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.09, 0.7])
+@pytest.mark.parametrize("n", [4, 5])
+def test_any_finite_scale(n, scale):
+    """Attention is defined for any finite softmax scale.  A mixed batch (decode
+    rows and prefill chunks) and a shared-prefix batch, compared with the
+    oracle at scale 0 (every visible key weighs the same), a negative scale
+    and a large positive one; scale <= 0 runs on the generic kernel."""
+    w = _Scaled(config(n, scale_down=16), scale)
+    g = GpuRun(w).run()
+    _, _, _, ref = oracle.run_step(w)
+    err = max_abs_err(g.out, ref)
+    print(f"[scale {scale}] config {n} max_abs_err={err:.3e}", flush=True)
+    assert g.err() == 0
+    assert err <= tol_for(w.dtype)
+
+
+def test_duplicate_slots_flagged_with_validation():
+    """Two rows of one write with the same slot are invalid input (the
+    copy-on-write rule of "vLLM 原理" §2.1 keeps writers apart).  With
+    validation on, pa_write_kv flags PA_DERR_DUP_SLOT; a write with distinct
+    slots (a whole mixed step) is not flagged; with validation off nothing is
+    checked."""
+    w = config(4, scale_down=8)
+    g = GpuRun(w)
+    prev = rpa.pa_set_validation(1)
+    try:
+        g.fill_history()
+        g.step()
+        torch.cuda.synchronize()
+        assert g.err() == 0                       # history and step writes: every slot distinct
+        slots = g.meta["slot_mapping"].clone()
+        for a, b in ((5, 700), (w.num_tokens - 1, 0), (300, 301)):
+            bad = slots.clone()
+            bad[b] = bad[a]
+            d_err = torch.zeros(1, dtype=torch.int32, device="cuda")
+            rpa.pa_write_kv(g.db.k, g.db.v, bad, g.k_cache, g.v_cache, d_err=d_err)
+            torch.cuda.synchronize()
+            assert int(d_err.item()) == rpa.PA_DERR_DUP_SLOT, (a, b)
+        bad = slots.clone()
+        bad[7] = -1
+        bad[9] = -1                               # skipped rows are not duplicates
+        d_err = torch.zeros(1, dtype=torch.int32, device="cuda")
+        rpa.pa_write_kv(g.db.k, g.db.v, bad, g.k_cache, g.v_cache, d_err=d_err)
+        torch.cuda.synchronize()
+        assert int(d_err.item()) == 0
+        rpa.pa_set_validation(0)
+        bad = slots.clone()
+        bad[1] = bad[0]
+        d_err.zero_()
+        rpa.pa_write_kv(g.db.k, g.db.v, bad, g.k_cache, g.v_cache, d_err=d_err)
+        torch.cuda.synchronize()
+        assert int(d_err.item()) == 0
+    finally:
+        rpa.pa_set_validation(prev)

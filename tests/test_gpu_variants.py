@@ -15,6 +15,7 @@ import torch
 import oracle
 import ragged_paged_attention_amd as rpa
 from tests.gpu_path import GpuRun, max_abs_err, tol_for
+from workloads import plant_needles
 from workloads.generators import build_workload
 
 pytestmark = pytest.mark.gpu
@@ -41,7 +42,8 @@ SHAPES = {
 
 
 @pytest.mark.parametrize("shape", sorted(SHAPES))
-@pytest.mark.parametrize("D,bs", [(64, 16), (256, 16), (128, 8), (64, 8), (256, 8), (128, 4), (64, 32)])
+@pytest.mark.parametrize("D,bs", [(64, 16), (256, 16), (128, 8), (64, 8), (256, 8), (128, 4), (64, 32),
+                                  (128, 256)])
 @pytest.mark.parametrize("Hq,Hkv", [(16, 4), (8, 8)])
 def test_variant_matches_oracle(shape, D, bs, Hq, Hkv):
     c = SHAPES[shape]
@@ -90,3 +92,19 @@ def test_variant_shared_prefix_bs8():
     _, _, _, ref = oracle.run_step(w)
     assert g.err() == 0
     assert max_abs_err(g.out, ref) <= tol_for("bf16")
+
+
+@pytest.mark.parametrize("D,bs", [(128, 4), (128, 8), (64, 1), (128, 256)])
+def test_variant_needles(D, bs):
+    """One dominant key per (sequence, KV head) at block sizes below 16 (each
+    lane or DMA row looks its block up itself, and the decode kernel's id
+    window moves every 64 blocks) and at 256: a wrong block shows as an O(1)
+    error."""
+    c = SHAPES["mixed"]
+    w = plant_needles(_batch(16, 4, D, bs, c["ql"], c["sl"], seed=D + bs), seed=bs)
+    g = GpuRun(w).run()
+    _, _, _, ref = oracle.run_step(w)
+    assert g.err() == 0
+    err = max_abs_err(g.out, ref)
+    print(f"[variant needles] D={D} bs={bs} max_abs_err={err:.3e}", flush=True)
+    assert err <= tol_for(w.dtype)

@@ -486,3 +486,60 @@ def unshare(w: Workload, spare_ids: Sequence[int]) -> Workload:
     step = Batch(w.step.query_lens, w.step.seq_lens, bt, w.step.k, w.step.v)
     return Workload(w.name + "_unshared", w.dtype, w.num_q_heads, w.num_kv_heads, w.head_dim,
                     w.block_size, w.num_blocks, step, w.q, hist, segs, w.seed, w.poison, w.notes)
+
+
+def plant_needles(w: Workload, seed: int = 0, logit: float = 40.0) -> Workload:
+    """A copy of `w` in which every (sequence, KV head) hides one dominant key.
+
+    For sequence s and KV head g a position j is drawn at random among the
+    positions every new row of s can see (0 .. seq_len - query_len), every
+    query row of s at the G query heads of g is set to one fresh N(0, 1)
+    vector u, and the K row of position j, head g, to c * u with
+    c = logit / (scale * |u|^2): that key's score is about `logit` while the
+    others score about N(0, 1), so each output row is, to many digits, the V
+    row of the needle's position.  A read from a wrong block (or a block of
+    another sequence) moves such an output by O(1) instead of by the
+    O(1/sqrt(L)) of plain N(0, 1) data.  Positions are drawn so that no two
+    needles land on the same stored row and head (shared prefix blocks are
+    one stored row for the whole group).  V is unchanged."""
+    rng = np.random.default_rng(seed)
+    G = w.num_q_heads // w.num_kv_heads
+    q = w.q.copy()
+    hk = w.hist.k.copy()
+    sk = w.step.k.copy()
+    ho = w.hist_row_offsets()
+    no = w.new_row_offsets()
+    used = set()
+
+    def stored_row(s: int, j: int):
+        # the generator's own bookkeeping: which array and row holds position
+        # j of sequence s (history entries cover seq_len - query_len .. seq_len - 1
+        # of their own table, the step's rows come last)
+        for e in w.hist_segments[s]:
+            lo = int(w.hist.seq_lens[e] - w.hist.query_lens[e])
+            if lo <= j < int(w.hist.seq_lens[e]):
+                return "h", int(ho[e]) + j - lo
+        L, ql = int(w.step.seq_lens[s]), int(w.step.query_lens[s])
+        return "s", int(no[s]) + j - (L - ql)
+
+    for s in range(w.num_seqs):
+        L, ql = int(w.step.seq_lens[s]), int(w.step.query_lens[s])
+        if ql == 0 or L == 0:
+            continue
+        for g in range(w.num_kv_heads):
+            for _ in range(64):
+                j = int(rng.integers(0, L - ql + 1))
+                where = stored_row(s, j)
+                if (where, g) not in used:
+                    break
+            used.add((where, g))
+            u = rng.standard_normal(w.head_dim).astype(np.float32)
+            c = logit / (w.scale * float(np.dot(u.astype(np.float64), u.astype(np.float64))))
+            q[no[s]:no[s + 1], g * G:(g + 1) * G] = _store(u[None, None, :], w.dtype)
+            arr = hk if where[0] == "h" else sk
+            arr[where[1], g] = _store((c * u)[None, :], w.dtype)[0]
+    hist = Batch(w.hist.query_lens, w.hist.seq_lens, w.hist.block_tables, hk, w.hist.v)
+    step = Batch(w.step.query_lens, w.step.seq_lens, w.step.block_tables, sk, w.step.v)
+    return Workload(w.name + "_needles", w.dtype, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size,
+                    w.num_blocks, step, q, hist, [list(x) for x in w.hist_segments], w.seed, w.poison,
+                    w.notes)
