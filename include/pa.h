@@ -27,7 +27,7 @@
  *     created by the library on the first such call on a device and kept
  *     until the process ends; the fork from and join back into `stream` are
  *     event records and waits made under a process-wide lock, so the call
- *     still completes with `stream`.
+ *     still completes with `stream`.  pa_attention_noalloc never uses it.
  *   - Host-checkable problems (null pointers, bad sizes, unsupported shapes,
  *     a too-small workspace, a failed launch) are returned synchronously as
  *     pa_status_t and nothing is enqueued.
@@ -253,6 +253,34 @@ pa_status_t pa_attention(const void* q, const void* k_cache, const void* v_cache
                          int32_t max_query_len, int32_t max_seq_len, float scale, pa_dtype_t dtype,
                          void* out, void* workspace, size_t workspace_bytes, int32_t* d_err,
                          void* stream);
+
+/*
+ * pa_attention_noalloc — pa_attention for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).
+ *
+ * Same arguments, meaning and results as pa_attention, without the
+ * workspace: the library uses a static device array of
+ * PA_NOALLOC_SCRATCH_BYTES instead (one per device, held from the library's
+ * first use of that device until the process ends).  The call allocates and
+ * frees nothing; its first call on a device looks the array's address up.
+ *   - A call whose pa_attention_workspace_size() exceeds
+ *     PA_NOALLOC_SCRATCH_BYTES returns PA_ERR_WORKSPACE and enqueues nothing.
+ *   - Every call on one device shares that device's array, and nothing in it
+ *     needs to start at any value.  Calls that overlap on one device (on
+ *     different streams, or from several threads, without ordering between
+ *     them) race on it: the caller must order them.
+ *   - The two-tile decode launch of a verify-like call stays on `stream`
+ *     (pa_attention may put it on the library's side stream).
+ */
+#define PA_NOALLOC_SCRATCH_BYTES (64u << 20)
+pa_status_t pa_attention_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                 const int32_t* block_tables, const int32_t* query_start_loc,
+                                 const int32_t* seq_lens, int32_t num_seqs, int32_t num_tokens,
+                                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                                 int32_t max_query_len, int32_t max_seq_len, float scale,
+                                 pa_dtype_t dtype, void* out, int32_t* d_err, void* stream);
 
 #ifdef __cplusplus
 }

@@ -22,6 +22,7 @@ PA_POLICY_AUTO, PA_POLICY_GENERIC, PA_POLICY_FAST = 0, 1, 2
 PA_DERR_QLEN_GT_SEQLEN, PA_DERR_TOKEN_SUM, PA_DERR_BLOCK_OOB, PA_DERR_SLOT_OOB, PA_DERR_OVERFLOW = 1, 2, 4, 8, 16
 PA_DERR_HINT = 32
 PA_DERR_DUP_SLOT = 64
+PA_NOALLOC_SCRATCH_BYTES = 64 << 20   # include/pa.h
 
 
 class PAError(RuntimeError):
@@ -84,6 +85,8 @@ _lib.pa_bench_timing_end.restype = _i32
 _lib.pa_bench_timing_end.argtypes = [ctypes.POINTER(KernelTime), _i32, ctypes.POINTER(_i32)]
 _lib.pa_attention.restype = _i32
 _lib.pa_attention.argtypes = [_p, _p, _p, _p, _p, _p] + [_i32] * 10 + [_f32, _i32, _p, _p, _size, _p, _p]
+_lib.pa_attention_noalloc.restype = _i32
+_lib.pa_attention_noalloc.argtypes = [_p, _p, _p, _p, _p, _p] + [_i32] * 10 + [_f32, _i32, _p, _p, _p]
 
 
 def declared_symbols() -> list:
@@ -260,6 +263,29 @@ def pa_attention(q, k_cache, v_cache, block_tables, query_start_loc, seq_lens, m
                            int(max_query_len), int(max_seq_len), float(scale), _dtype_code(q.dtype),
                            _ptr(out), _ptr(workspace), wbytes, _ptr(d_err), _stream(q.device))
     _check(st, "pa_attention")
+    return out
+
+
+def pa_attention_noalloc(q, k_cache, v_cache, block_tables, query_start_loc, seq_lens, max_query_len: int,
+                         max_seq_len: int, scale: float, out=None, d_err=None):
+    """Calls pa_attention_noalloc (the library's static scratch instead of a
+    workspace).  Same shapes as pa_attention; returns out."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (out, "out")):
+        _need(t, n, q.dtype)
+    for t, n in ((block_tables, "block_tables"), (query_start_loc, "query_start_loc"), (seq_lens, "seq_lens")):
+        _need(t, n, torch.int32)
+    T, Hq, D = (int(x) for x in q.shape)
+    NB, BS, Hkv = int(k_cache.shape[0]), int(k_cache.shape[1]), int(k_cache.shape[2])
+    if int(k_cache.shape[3]) != D or v_cache.shape != k_cache.shape:
+        raise ValueError("cache shape mismatch")
+    if out is None:
+        out = torch.empty_like(q)
+    st = _lib.pa_attention_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                                   _ptr(query_start_loc), _ptr(seq_lens), int(seq_lens.shape[0]), T, Hq, Hkv, D,
+                                   BS, NB, int(block_tables.shape[1]), int(max_query_len), int(max_seq_len),
+                                   float(scale), _dtype_code(q.dtype), _ptr(out), _ptr(d_err), _stream(q.device))
+    _check(st, "pa_attention_noalloc")
     return out
 
 

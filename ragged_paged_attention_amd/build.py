@@ -22,7 +22,8 @@ LIB = os.path.join(PKG, "libpa.so")
 ARCH = "gfx950"
 
 SOURCES = ["pa_api.cpp", "metadata.hip", "write_kv.hip", "attn_generic.hip", "attn_fast.hip",
-           "attn_prefill.hip", "bench_probes.hip", "timing.cpp", "copy_blocks.hip"]
+           "attn_prefill.hip", "bench_probes.hip", "timing.cpp", "copy_blocks.hip",
+           "attn_noalloc.hip"]
 
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

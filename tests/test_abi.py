@@ -72,5 +72,20 @@ def test_host_side_rejections_need_no_gpu():
     assert cp(n=0, ptr=None) == 0         # nothing to copy
 
 
+def test_noalloc_refuses_calls_beyond_its_scratch_without_a_gpu():
+    """pa_attention_noalloc checks the call's workspace need against its
+    static scratch before any HIP call: too large a call is refused with
+    PA_ERR_WORKSPACE (the pointers below are never dereferenced)."""
+    lib = _lib.library()
+    fake = ctypes.c_void_p(1 << 20)
+    S, T, Hq, Hkv, D, max_q, max_l = 256, 8192, 32, 8, 128, 497, 8192
+    need = lib.pa_attention_workspace_size(S, T, Hq, Hkv, D, max_q, max_l)
+    assert need > rpa.PA_NOALLOC_SCRATCH_BYTES
+    args = [fake] * 6 + [S, T, Hq, Hkv, D, 16, 40000, 512, max_q, max_l, ctypes.c_float(0.088), 1, fake, None,
+                         None]
+    assert lib.pa_attention_noalloc(*args) == 5
+    assert lib.pa_attention_noalloc(*([None] * 6 + args[6:])) == 1   # null pointers come first
+
+
 def _attn_args(T=3, Hq=4, Hkv=2, D=16, max_q=2, S=2, scale=0.25):
     return [None] * 6 + [S, T, Hq, Hkv, D, 16, 8, 4, max_q, 8, ctypes.c_float(scale), 1, None, None, 0, None, None]
