@@ -67,12 +67,17 @@ def parse():
                     default=None,
                     help="run one leg only (for profiling)")
     ap.add_argument("--cpu-sample-rows", type=int, default=2048)
+    ap.add_argument("--cold-launches", type=int, default=50,
+                    help="single launches timed after a cache flush each (median reported)")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("ROCPROF_DIR", "OUT_MD"),
                     help="write a kernel-time summary (profiles/*.md) from a rocprofv3 --kernel-trace --stats "
                          "--output-format csv directory; no GPU needed")
     ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "KERNEL", "WORKLOAD"),
                     help="write profiles/KERNEL.WORKLOAD.pmc.md from two rocprofv3 --pmc runs (FETCH_SIZE, "
                          "WRITE_SIZE) of a bench leg, calibrated on the leg's copy of known size; no GPU needed")
+    ap.add_argument("--summarize-mfma", nargs=3, metavar=("PMC_DIR", "KERNEL", "WORKLOAD"),
+                    help="write profiles/KERNEL.WORKLOAD.mfma.pmc.md from one rocprofv3 --pmc --kernel-trace run "
+                         "with the MFMA counters; no GPU needed")
     ap.add_argument("--command", default="", help="the command that produced the rocprofv3 output (recorded)")
     return ap.parse_args()
 
@@ -102,6 +107,28 @@ class Timer:
         end.record()
         torch.cuda.synchronize()
         return start.elapsed_time(end) / iters  # ms
+
+    def time_cold(self, fn, iters=50, flush_bytes=1 << 30):
+        """Median (and 10th / 90th percentile) over `iters` single calls, each
+        preceded by a write of `flush_bytes` to a separate buffer (four times
+        the 256 MB Infinity Cache, so the call starts with cold caches), each
+        call bracketed by its own pair of events on the current stream."""
+        torch = self.torch
+        if getattr(self, "_flush", None) is None or self._flush.numel() != flush_bytes // 4:
+            self._flush = torch.empty(flush_bytes // 4, dtype=torch.int32, device="cuda")
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+        fn()
+        torch.cuda.synchronize()
+        for i in range(iters):
+            self._flush.fill_(i)
+            ev[i][0].record()
+            fn()
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        ts = sorted(a.elapsed_time(b) for a, b in ev)
+        pick = lambda q: ts[min(len(ts) - 1, int(q * (len(ts) - 1) + 0.5))]
+        return {"median_ms": pick(0.5), "p10_ms": pick(0.1), "p90_ms": pick(0.9), "launches": iters,
+                "flush_bytes": flush_bytes}
 
     def kernels(self, rpa, fn, iters):
         """Per-kernel launch durations (library-side HIP events on the launch
@@ -209,7 +236,8 @@ def roofline_for(kernel, avg_ms, w, workload_tag, one_decode_launch=False):
         a = pre_flops / (avg_ms / 1e3) / 1e12
         return {"bound": "mfma", "kernel": kernel, "achieved": a, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": a / BF16_PEAK_TFLOPS, "traffic": traffic_from_profiles(kernel, workload_tag),
-                "work_per_launch": pre_flops, "avg_launch_ms": avg_ms}
+                "work_per_launch": pre_flops, "avg_launch_ms": avg_ms,
+                "mfma_busy": mfma_from_profiles(kernel, workload_tag)}
     dec_bytes = work[kernel]
     a = dec_bytes / (avg_ms / 1e3) / 1e9
     return {"bound": "hbm", "kernel": kernel, "achieved": a, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -302,6 +330,94 @@ source_sha256_16: {source_hash(KERNEL_SOURCES[kernel])}
     print(f"wrote {out_md}")
 
 
+SIMDS = 256 * 4  # MI355X: 256 CUs x 4 SIMDs
+
+
+def _workload_flops(kernel, workload):
+    """Algorithmic FLOPs one launch of `kernel` performs on the named workload."""
+    from workloads import CONFIG_NAMES, config
+    n = {v: k for k, v in CONFIG_NAMES.items()}[workload]
+    w = config(n, poison=False)
+    return work_split(w)[kernel]
+
+
+def summarize_mfma(pmc_dir, kernel, workload, command):
+    """MFMA counters of one kernel, per dispatch, and what they say:
+      - MFMA busy fraction = SQ_VALU_MFMA_BUSY_CYCLES / (active cycles per XCD
+        x 1024 SIMDs): GRBM_GUI_ACTIVE adds up the 8 XCDs, so the active cycles
+        of one XCD (the kernel's duration in shader-clock cycles) are
+        GRBM_GUI_ACTIVE / 8;
+      - counted MFMA FLOPs = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 (the counter
+        is in units of 512 FLOPs) against the algorithmic FLOPs (causal pairs
+        only; the kernel also multiplies the masked half of diagonal tiles);
+      - the shader clock under the kernel = active cycles per XCD / duration."""
+    rows = _csv_rows(_find(pmc_dir, "counter_collection.csv"))
+    match = KERNEL_MATCH.get(kernel, kernel)
+    names = sorted({r["Counter_Name"] for r in rows})
+    per = {c: _counter_per_dispatch(rows, c, match) for c in names}
+    avg = {c: sum(v.values()) / max(1, len(v)) for c, v in per.items() if v}
+    n_disp = max((len(v) for v in per.values()), default=0)
+    durs = []
+    try:
+        for r in _csv_rows(_find(pmc_dir, "kernel_trace.csv")):
+            if match in r["Kernel_Name"]:
+                durs.append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    except FileNotFoundError:
+        pass
+    dur_us = sum(durs) / len(durs) if durs else None
+    active = avg.get("GRBM_GUI_ACTIVE", 0.0) / 8
+    busy = avg.get("SQ_VALU_MFMA_BUSY_CYCLES")
+    frac = busy / (active * SIMDS) if busy and active else None
+    counted = avg["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512 if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in avg else None
+    alg = _workload_flops(kernel, workload)
+    clock = active / (dur_us * 1e3) if dur_us and active else None
+    lines = [f"# MFMA counters: {kernel} on the {workload} workload", "",
+             "Command (run from the repository root on one MI355X):", f"- `{command}`", "",
+             f"Per dispatch, averaged over {n_disp} dispatches of `{match}`.  GRBM_GUI_ACTIVE adds up the",
+             "8 XCDs; one XCD's active cycles (GRBM_GUI_ACTIVE / 8) are the kernel's span in shader-clock",
+             "cycles.  MFMA busy fraction = SQ_VALU_MFMA_BUSY_CYCLES / (those cycles x 1024 SIMDs).",
+             "SQ_INSTS_VALU_MFMA_MOPS_BF16 counts bf16 MFMA work in units of 512 FLOPs.", "",
+             "| counter | per dispatch |", "|---|---|"]
+    lines += [f"| {c} | {v:.4e} |" for c, v in sorted(avg.items())]
+    lines += ["", "| derived | value |", "|---|---|"]
+    if dur_us:
+        lines.append(f"| kernel duration under counters (kernel trace) | {dur_us:.2f} us |")
+    if clock:
+        lines.append(f"| shader clock over the kernel | {clock:.3f} GHz |")
+    if frac is not None:
+        lines.append(f"| MFMA busy fraction | {frac:.4f} |")
+    if counted:
+        lines.append(f"| counted MFMA FLOPs | {counted:.4e} |")
+    lines.append(f"| algorithmic FLOPs (causal) | {alg:.4e} |")
+    if counted:
+        lines.append(f"| counted / algorithmic | {counted / alg:.4f} |")
+    if counted and busy:
+        lines.append(f"| busy cycles per 1024 counted FLOPs | {busy * 1024 / counted:.4f} |")
+    lines += ["", f"mfma_busy_frac: {frac if frac is not None else 'null'}",
+              f"shader_clock_ghz: {clock if clock else 'null'}",
+              f"source_sha256_16: {source_hash(KERNEL_SOURCES[kernel])}", ""]
+    out_md = os.path.join(PROFILES, f"{kernel}.{workload}.mfma.pmc.md")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines))
+    print(f"wrote {out_md}")
+
+
+def mfma_from_profiles(kernel: str, workload: str):
+    """MFMA busy fraction and shader clock from the committed counter summary,
+    or None if there is none or the kernel's source changed since."""
+    path = os.path.join(PROFILES, f"{kernel}.{workload}.mfma.pmc.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"source_sha256_16:\s*([0-9a-f]{16})", text)
+    b = re.search(r"mfma_busy_frac:\s*([0-9.e+-]+)", text)
+    c = re.search(r"shader_clock_ghz:\s*([0-9.e+-]+)", text)
+    if not m or not b or m.group(1) != source_hash(KERNEL_SOURCES[kernel]):
+        return None
+    return {"mfma_busy_frac": float(b.group(1)), "shader_clock_ghz": float(c.group(1)) if c else None,
+            "source": os.path.relpath(path, ROOT)}
+
+
 def main():
     args = parse()
     if args.summarize_trace:
@@ -309,6 +425,9 @@ def main():
         return
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc, args.command)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(*args.summarize_mfma, args.command)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (--gpus {args.gpus} was asked for): the library has no multi-GPU "
@@ -347,6 +466,7 @@ def main():
                          w.scale, w.max_query_len, w.max_seq_len, out=out, workspace=ws)
 
         ms = timer.time(step, args.steps, args.warmup)
+        cold = timer.time_cold(step, args.cold_launches)
         kern = timer.kernels(rpa, step, args.steps)
         ql = w.step.query_lens
         one = "decode_kernel_2t" not in kern
@@ -360,6 +480,7 @@ def main():
                        "heads_q_kv": [w.num_q_heads, w.num_kv_heads], "head_dim": w.head_dim,
                        "block_size": w.block_size, "pool_blocks": w.num_blocks, "seed": w.seed},
             "kernels_ms_per_step": {k: round(n * avg / args.steps, 5) for k, (n, avg) in kern.items()},
+            "cold_cache": {**cold, "tokens_per_s": w.num_tokens / (cold["median_ms"] / 1e3)},
             "step_work": {"decode_bytes": dec_bytes, "prefill_flops": split["prefill_kernel"]},
         })
         # the whole step against the two rooflines: the time the decode bytes
@@ -394,6 +515,7 @@ def main():
         attn3 = lambda: rpa.pa_attention(db.q, g3.k_cache, g3.v_cache, db.block_tables, qsl3, db.seq_lens,
                                          w3.max_query_len, w3.max_seq_len, w3.scale, out=out3, workspace=ws3)
         ms3 = timer.time(attn3, max(args.steps, 20), args.warmup)
+        cold3 = timer.time_cold(attn3, args.cold_launches)
         kern3 = timer.kernels(rpa, attn3, 10)
         kv3 = accounting.kv_read_bytes(w3.step.seq_lens, w3.num_kv_heads, w3.head_dim, w3.dtype)
         gbs = kv3 / (ms3 / 1e3) / 1e9
@@ -406,6 +528,7 @@ def main():
         result["decode_kv_read"] = {
             "workload": "decode batch: 100 seqs x 2001 tokens, 32/32 heads, D 128, bs 16, bf16",
             "GBps": gbs, "frac_hbm_peak": gbs / HBM_PEAK_GBS, "kv_bytes": kv3, "ms_per_call": ms3,
+            "cold_cache": {**cold3, "GBps": kv3 / (cold3["median_ms"] / 1e3) / 1e9},
             "kernels_ms": {k: round(avg, 5) for k, (n, avg) in kern3.items()},
             "decode_kernel_GBps": kv3 / (kern3["decode_kernel"][1] / 1e3) / 1e9,
             "ceiling_stream_read_GBps": stream_gbs,
@@ -474,13 +597,18 @@ def main():
         attn5 = lambda: rpa.pa_attention(db.q, g5.k_cache, g5.v_cache, db.block_tables, qsl5, db.seq_lens,
                                          w5.max_query_len, w5.max_seq_len, w5.scale, out=out5, workspace=ws5)
         ms5 = timer.time(attn5, max(args.steps, 20), args.warmup)
+        cold5 = timer.time_cold(attn5, args.cold_launches)
+        kern5 = timer.kernels(rpa, attn5, 10)
         kv5 = accounting.kv_read_bytes(w5.step.seq_lens, w5.num_kv_heads, w5.head_dim, w5.dtype)
         uq5 = accounting.unique_kv_bytes_fast(w5.step.block_tables, w5.step.seq_lens, w5.block_size,
                                               w5.num_kv_heads, w5.head_dim, w5.dtype)
         result["shared_prefix_decode"] = {
             "workload": "64 seqs in 4 groups sharing 16384-token prefixes + 512 private, 64/8 heads, bf16",
             "ms_per_call": ms5, "logical_GBps": kv5 / (ms5 / 1e3) / 1e9, "unique_GBps": uq5 / (ms5 / 1e3) / 1e9,
-            "logical_bytes": kv5, "unique_bytes": uq5}
+            "logical_bytes": kv5, "unique_bytes": uq5,
+            "kernels_ms": {k: round(avg, 5) for k, (n, avg) in kern5.items()},
+            "cold_cache": {**cold5, "logical_GBps": kv5 / (cold5["median_ms"] / 1e3) / 1e9,
+                           "unique_GBps": uq5 / (cold5["median_ms"] / 1e3) / 1e9}}
         del g5, ws5, out5
         torch.cuda.empty_cache()
 
@@ -498,6 +626,7 @@ def main():
         attn6 = lambda: rpa.pa_attention(db.q, g6.k_cache, g6.v_cache, db.block_tables, qsl6, db.seq_lens,
                                          w6.max_query_len, w6.max_seq_len, w6.scale, out=out6, workspace=ws6)
         ms6 = timer.time(attn6, max(args.steps, 20), args.warmup)
+        cold6 = timer.time_cold(attn6, args.cold_launches)
         kern6 = timer.kernels(rpa, attn6, 10)
         kv6 = accounting.kv_read_bytes(w6.step.seq_lens, w6.num_kv_heads, w6.head_dim, w6.dtype)
         result["verify_kv_read"] = {
@@ -506,6 +635,7 @@ def main():
             "tokens": w6.num_tokens, "ms_per_call": ms6, "GBps": kv6 / (ms6 / 1e3) / 1e9,
             "frac_hbm_peak": kv6 / (ms6 / 1e3) / 1e9 / HBM_PEAK_GBS, "kv_bytes": kv6,
             "tokens_per_s": w6.num_tokens / (ms6 / 1e3),
+            "cold_cache": {**cold6, "GBps": kv6 / (cold6["median_ms"] / 1e3) / 1e9},
             "kernels_ms": {k: round(avg, 5) for k, (n, avg) in kern6.items()}}
         one6 = "decode_kernel_2t" not in kern6
         split6 = work_split(w6, one6)
@@ -529,14 +659,17 @@ def main():
         attn2 = lambda: rpa.pa_attention(db.q, g2.k_cache, g2.v_cache, db.block_tables, qsl2, db.seq_lens,
                                          w2.max_query_len, w2.max_seq_len, w2.scale, out=out2, workspace=ws2)
         ms2 = timer.time(attn2, max(args.steps, 20), args.warmup)
+        cold2 = timer.time_cold(attn2, args.cold_launches)
         kern2 = timer.kernels(rpa, attn2, 10)
         fl2 = accounting.attention_flops(w2.step.query_lens, w2.step.seq_lens, w2.num_q_heads, w2.head_dim)
         tf = fl2 / (ms2 / 1e3) / 1e12
         result["prefill_mfma"] = {
             "workload": "ragged prefill: prompts 16/128/1024/2048 (T=3216), 32/32 heads, D 128, bs 16, bf16",
             "TFLOPs": tf, "frac_bf16_peak": tf / BF16_PEAK_TFLOPS, "flops": fl2, "ms_per_call": ms2,
+            "cold_cache": {**cold2, "TFLOPs": fl2 / (cold2["median_ms"] / 1e3) / 1e12},
             "kernels_ms": {k: round(avg, 5) for k, (n, avg) in kern2.items()},
-            "prefill_kernel_TFLOPs": fl2 / (kern2["prefill_kernel"][1] / 1e3) / 1e12}
+            "prefill_kernel_TFLOPs": fl2 / (kern2["prefill_kernel"][1] / 1e3) / 1e12,
+            "mfma_busy": mfma_from_profiles("prefill_kernel", w2.name)}
         if args.only == "prefill":
             result["roofline"] = roofline_for("prefill_kernel", kern2["prefill_kernel"][1], w2, w2.name)
 
