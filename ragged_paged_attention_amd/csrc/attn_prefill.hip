@@ -64,6 +64,7 @@ struct PrefillArgs {
   int32_t* d_err;
   const int32_t* plan;  // work list (layout in pa_internal.h)
   const int4* groups;   // cascade groups
+  const int32_t* members;  // cascade members (a group's x is its first position)
   float* ws_pre;        // cascade prefix partials: (slot, KV head, group row)
 };
 
@@ -81,6 +82,7 @@ struct PlanArgs {
   int32_t* plan;
   int4* groups;
   int4* seq_prefix;
+  int32_t* members;  // cascade members, each leader's stretch in rank order
   int2* dec;         // decode lists: one-tile at dec, two-tile at dec + cap_dec
   int32_t* d_err;
 };
@@ -129,13 +131,20 @@ __device__ int32_t plan_block_scan(int32_t v, int32_t id, int32_t* wbuf) {
 //
 // Cascade groups ("vLLM 原理" §2.1 and the shared prefixes and automatic
 // prefix caching of "LLM 推理引擎 Continuous Batching 与 PagedAttention"
-// §4.1, §4.2: sequences whose
-// tables map the same physical block at the same logical position share that
-// block's contents): maximal runs of consecutive single-token decode
-// sequences whose tables agree on at least kCascadeMinTiles full 64-token
-// tiles from the start, at most kRowsPerWG / G members.  The group's shared
-// prefix (the common full blocks, rounded down to whole tiles) is read once
-// for all members, in up to kCascadeMaxParts parts.
+// §4.1, §4.2: sequences whose tables map the same physical block at the same
+// logical position share that block's contents).  Candidates are
+// single-token decode sequences with at least kCascadeMinTiles full 64-token
+// tiles; those whose first block ids are equal are gathered through an LDS
+// hash table keyed by that id, whose entry keeps the smallest such sequence
+// (the leader), so the grouping depends only on which tables share blocks,
+// not on where the sequences sit in the batch.  Every other candidate
+// compares its table with its leader's from the start and joins if they
+// agree on at least kCascadeMinTiles tiles; the group's shared prefix is the
+// fewest blocks any joined member shares with the leader, rounded down to
+// whole tiles (members agree pairwise there), read once for all members in up
+// to kCascadeMaxParts parts.  A leader's members are listed in the plan
+// (rank order) and cut into groups of at most kCascadeRows / G; groups take
+// their indices in leader order, and the first kCascadeEntries are cascaded.
 //
 // Work list: every prefill-class (sequence, query tile) and every cascade
 // prefix part, counting-sorted by the K/V tiles it reads, heaviest first.
@@ -147,8 +156,14 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(PlanArgs a) {
   __shared__ int32_t hist[kPlanBuckets];
   __shared__ int32_t cursor[kPlanBuckets];
   __shared__ int32_t wave_tot[kPlanThreads / 64];
-  __shared__ int32_t common_blocks[kCascadeMaxSeqs];  // full blocks shared with sequence s - 1
-  __shared__ int32_t chunk_of[kCascadeMaxSeqs];       // first sequence of s's chunk
+  __shared__ int32_t common_blocks[kCascadeMaxSeqs];  // full blocks; for a follower then the blocks it shares with its leader
+  __shared__ int32_t slot_of[kCascadeMaxSeqs];        // hash slot of the sequence's first block id, -1 if no candidate
+  __shared__ int32_t gbase_of[kCascadeMaxSeqs];       // leader with members: its first group index, else -1
+  __shared__ int32_t mbase_of[kCascadeMaxSeqs];       // leader with members: its first member-list position
+  __shared__ int32_t hkey[kCascadeHash];              // first block id of the slot, -1 while empty
+  __shared__ int32_t hmin[kCascadeHash];              // smallest candidate with that id: the leader
+  __shared__ int32_t hcnt[kCascadeHash];              // joined followers, later the rank counter
+  __shared__ int32_t hpre[kCascadeHash];              // fewest blocks a joined follower shares with the leader
   __shared__ int32_t n_groups;
   __shared__ int32_t dhist[2][kDecBuckets];
   __shared__ int32_t dcur[2][kDecBuckets];
@@ -167,34 +182,55 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(PlanArgs a) {
   bool prefix_zero_late = false;
   if (a.cascade_on) {
     const int32_t thr_blocks = ceil_div(kCascadeMinTiles * kTile, a.bs);
-    bool candidate = false;
+    const int32_t max_members = max(2, kCascadeRows / a.G);
+    for (int i = tid; i < kCascadeHash; i += kPlanThreads) {
+      hkey[i] = -1;
+      hmin[i] = INT32_MAX;
+      hcnt[i] = 0;
+      hpre[i] = INT32_MAX;
+    }
+    __syncthreads();
+    // candidates into the hash table (at most kCascadeMaxSeqs keys in twice as
+    // many slots, so linear probing always finds a free or matching slot)
     for (int32_t s = tid; s < a.S; s += kPlanThreads) {
-      int32_t c = 0;
-      if (s > 0) {
-        const int32_t ql0 = a.qsl[s] - a.qsl[s - 1], ql1 = a.qsl[s + 1] - a.qsl[s];
-        const int32_t L0 = a.seq_lens[s - 1], L1 = a.seq_lens[s];
-        if (ql0 == 1 && ql1 == 1 && L0 >= 1 && L1 >= 1 && ceil_div(L0, a.bs) <= a.MB &&
-            ceil_div(L1, a.bs) <= a.MB) {
-          c = min(L0, L1) / a.bs;  // blocks full in both contexts
-          if (c > 0 && a.block_tables[static_cast<int64_t>(s - 1) * a.MB] !=
-                           a.block_tables[static_cast<int64_t>(s) * a.MB])
-            c = 0;
+      int32_t slot = -1, full = 0;
+      const int32_t ql = a.qsl[s + 1] - a.qsl[s], L = a.seq_lens[s];
+      if (ql == 1 && L >= 1 && ceil_div(L, a.bs) <= a.MB) {
+        full = L / a.bs;
+        const int32_t key = a.block_tables[static_cast<int64_t>(s) * a.MB];
+        if (full >= thr_blocks && key >= 0) {
+          int32_t h = static_cast<int32_t>((static_cast<uint32_t>(key) * 2654435761u) >> (32 - kCascadeHashBits));
+          for (;;) {
+            const int32_t old = atomicCAS(&hkey[h], -1, key);
+            if (old == -1 || old == key) break;
+            h = (h + 1) & (kCascadeHash - 1);
+          }
+          atomicMin(&hmin[h], s);
+          slot = h;
         }
       }
-      common_blocks[s] = c;
-      candidate |= c >= thr_blocks;
+      slot_of[s] = slot;
+      common_blocks[s] = full;
+      gbase_of[s] = -1;
     }
-    if (!__syncthreads_or(candidate)) {  // no two neighbours can share enough: no group
+    __syncthreads();
+    bool follower = false;  // a candidate that is not its slot's leader
+    for (int32_t s = tid; s < a.S; s += kPlanThreads) follower |= slot_of[s] >= 0 && hmin[slot_of[s]] != s;
+    if (!__syncthreads_or(follower)) {  // no two candidates start with the same block: no group
       prefix_zero_late = true;
       if (tid == 0) a.plan[1] = 0;
     } else {
       for (int32_t s = tid; s < a.S; s += kPlanThreads) a.seq_prefix[s] = make_int4(0, 0, 0, 0);
-      // first block that differs, one wave per candidate, kCmpStep blocks per
-      // step with all their loads in flight
-      for (int32_t s = 1 + wave; s < a.S; s += kPlanThreads / 64) {
-        const int32_t n = common_blocks[s];
-        if (n <= 1) continue;
-        const int32_t* b0 = a.block_tables + static_cast<int64_t>(s - 1) * a.MB;
+      // each follower's first block differing from its leader's, one wave per
+      // follower, kCmpStep blocks per step with all their loads in flight
+      // (leaders' entries of common_blocks are only read here)
+      for (int32_t s = wave; s < a.S; s += kPlanThreads / 64) {
+        const int32_t slot = slot_of[s];
+        if (slot < 0) continue;
+        const int32_t ld = hmin[slot];
+        if (ld == s) continue;
+        const int32_t n = min(common_blocks[s], common_blocks[ld]);
+        const int32_t* b0 = a.block_tables + static_cast<int64_t>(ld) * a.MB;
         const int32_t* b1 = a.block_tables + static_cast<int64_t>(s) * a.MB;
         int32_t first = n;
         for (int32_t j0 = 0; j0 < n && first == n; j0 += kCmpStep) {
@@ -220,54 +256,40 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(PlanArgs a) {
         if (lane == 0) common_blocks[s] = first;
       }
       __syncthreads();
-      // Groups, in parallel: a run starts at s unless s shares at least
-      // kCascadeMinTiles tiles with s - 1; runs are cut into chunks of at most
-      // kCascadeRows / G members; a chunk of two or more is a group (the first
-      // kCascadeEntries of them), its prefix the fewest blocks any two
-      // neighbours in it share, rounded down to whole tiles.
-      constexpr int kPerS = kCascadeMaxSeqs / kPlanThreads;
-      const int32_t max_members = max(2, kCascadeRows / a.G);
-      int32_t run_start[kPerS], m = -1;
-#pragma unroll
-      for (int j = 0; j < kPerS; ++j) {
-        const int32_t s = kPerS * tid + j;
-        if (s < a.S && (s == 0 || common_blocks[s] < thr_blocks)) m = s;
-        run_start[j] = m;  // latest start within this thread's slice
-      }
-      const int32_t before = plan_block_scan<true>(m, -1, wave_tot);
-#pragma unroll
-      for (int j = 0; j < kPerS; ++j) {
-        const int32_t s = kPerS * tid + j;
-        const int32_t rs = max(run_start[j], before);
-        if (s < a.S) chunk_of[s] = rs + (s - rs) / max_members * max_members;
-      }
-      __syncthreads();
-      int32_t is_group[kPerS], members[kPerS], common[kPerS], n_mine = 0;
-#pragma unroll
-      for (int j = 0; j < kPerS; ++j) {
-        const int32_t s = kPerS * tid + j;
-        is_group[j] = 0;
-        if (s < a.S && chunk_of[s] == s) {
-          int32_t e = s + 1, c = INT32_MAX;
-          while (e < a.S && chunk_of[e] == s) {
-            c = min(c, common_blocks[e]);
-            ++e;
-          }
-          members[j] = e - s;
-          common[j] = c;
-          is_group[j] = e - s >= 2;
-          n_mine += is_group[j];
+      // followers sharing at least thr_blocks with their leader join it
+      for (int32_t s = tid; s < a.S; s += kPlanThreads) {
+        const int32_t slot = slot_of[s];
+        if (slot >= 0 && hmin[slot] != s && common_blocks[s] >= thr_blocks) {
+          atomicAdd(&hcnt[slot], 1);
+          atomicMin(&hpre[slot], common_blocks[s]);
         }
       }
-      int32_t gidx = plan_block_scan<false>(n_mine, 0, wave_tot);
-#pragma unroll
-      for (int j = 0; j < kPerS; ++j) {
-        if (!is_group[j]) continue;
-        if (gidx < a.cap_groups)
-          a.groups[gidx] = make_int4(kPerS * tid + j, members[j], common[j] * a.bs / kTile * kTile, 0);
-        ++gidx;
+      __syncthreads();
+      // groups in leader order: a leader with members heads ceil(members /
+      // max_members) groups over its stretch of the member list
+      static_assert(kCascadeMaxSeqs == kPlanThreads, "one sequence per thread in the group scan");
+      {
+        const int32_t s = tid;
+        int32_t ngs = 0, nms = 0, slot = -1;
+        if (s < a.S) {
+          slot = slot_of[s];
+          if (slot >= 0 && hmin[slot] == s && hcnt[slot] > 0) {
+            nms = hcnt[slot] + 1;  // the followers and the leader
+            ngs = ceil_div(nms, max_members);
+          }
+        }
+        const int32_t gb = plan_block_scan<false>(ngs, 0, wave_tot);
+        const int32_t mb = plan_block_scan<false>(nms, 0, wave_tot);
+        if (ngs > 0) {
+          gbase_of[s] = gb;
+          mbase_of[s] = mb;
+          hcnt[slot] = 0;  // from here on the slot's rank counter
+          const int32_t pre_tokens = hpre[slot] * a.bs / kTile * kTile;
+          for (int32_t c = 0; c < ngs && gb + c < a.cap_groups; ++c)
+            a.groups[gb + c] = make_int4(mb + c * max_members, min(max_members, nms - c * max_members), pre_tokens, 0);
+        }
+        if (tid == kPlanThreads - 1) n_groups = min(gb + ngs, a.cap_groups);
       }
-      if (tid == kPlanThreads - 1) n_groups = min(gidx, a.cap_groups);
       __syncthreads();
       // parts (up to kCascadeMaxParts of at least kCascadeMinTiles tiles,
       // kCascadeEntries over all groups) and each group's first prefix slot
@@ -291,10 +313,22 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(PlanArgs a) {
         }
       }
       __syncthreads();
-      for (int32_t gi = wave; gi < ngr; gi += kPlanThreads / 64) {
-        const int4 gr = a.groups[gi];
-        for (int32_t k = lane; k < gr.y; k += 64)
-          a.seq_prefix[gr.x + k] = make_int4(gr.z, gr.w & 255, gr.w >> 8, k * a.G);
+      // members: the leader and each joined follower take a rank in the
+      // leader's stretch of the member list (any order: a member's rows give
+      // the same values wherever they sit in the group), and a member of a
+      // cascaded group gets its prefix record
+      for (int32_t s = tid; s < a.S; s += kPlanThreads) {
+        const int32_t slot = slot_of[s];
+        if (slot < 0) continue;
+        const int32_t ld = hmin[slot];
+        if (gbase_of[ld] < 0 || (ld != s && common_blocks[s] < thr_blocks)) continue;
+        const int32_t r = atomicAdd(&hcnt[slot], 1);
+        a.members[mbase_of[ld] + r] = s;
+        const int32_t gi = gbase_of[ld] + r / max_members;
+        if (gi < ngr) {
+          const int4 gr = a.groups[gi];
+          a.seq_prefix[s] = make_int4(gr.z, gr.w & 255, gr.w >> 8, (r % max_members) * a.G);
+        }
       }
       if (tid == 0) a.plan[1] = ngr;
     }
@@ -520,7 +554,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(prefil
   // through the first member's table (the same blocks as every member's), and
   // the result is a split-K partial per row for the decode merge.
   const bool cascade = ent.x < 0;
-  int32_t s, qt_first, q0, qlen, rows_total, L, pp = 0, slot = 0, kt_begin = 0, kt_end = 0;
+  int32_t s, qt_first, q0, qlen, rows_total, L, pp = 0, slot = 0, kt_begin = 0, kt_end = 0, mbeg = 0;
   if (!cascade) {
     s = ent.x;
     qt_first = ent.y;
@@ -530,7 +564,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(prefil
     L = a.seq_lens[s];
   } else {
     const int4 gr = a.groups[-ent.x - 1];
-    s = gr.x;
+    s = a.members[gr.x];  // any member's table holds the shared prefix
+    mbeg = gr.x;
     qt_first = 0;
     q0 = 0;
     qlen = 1;
@@ -666,7 +701,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(prefil
     if (!cascade) kt_end = (L - qlen + last_row / a.G) / kTile + 1;
     // flat token index of row rho (its query head is rho mod G)
     auto row_token = [&](int32_t rho) -> int32_t {
-      return cascade ? a.qsl[s + rho / a.G] : q0 + rho / a.G;
+      return cascade ? a.qsl[a.members[mbeg + rho / a.G]] : q0 + rho / a.G;
     };
     issue_tile(kt_begin, lds0, load_bid(kt_begin));
     int32_t bid_next = load_bid(kt_begin + 1);
@@ -870,7 +905,8 @@ PlanLayout plan_layout(int32_t S, int32_t T, int32_t G, int32_t P, bool prefill_
   l.cap_entries = static_cast<int32_t>(cap > INT32_MAX ? INT32_MAX : cap);
   l.groups_off = (static_cast<size_t>(kPlanHeader) * 4 + static_cast<size_t>(cap) * 8 + 15) & ~static_cast<size_t>(15);
   l.seqpre_off = l.groups_off + static_cast<size_t>(l.cap_groups) * 16;
-  l.dec_off = (l.seqpre_off + (cascade_on ? static_cast<size_t>(S) * 16 : 0) + 15) & ~static_cast<size_t>(15);
+  l.members_off = l.seqpre_off + (cascade_on ? static_cast<size_t>(S) * 16 : 0);
+  l.dec_off = (l.members_off + (cascade_on ? static_cast<size_t>(S) * 4 : 0) + 15) & ~static_cast<size_t>(15);
   l.cap_dec = static_cast<int64_t>(S) * P;
   l.bytes = l.dec_off + static_cast<size_t>(2 * l.cap_dec) * 8;
   return l;
@@ -901,6 +937,7 @@ hipError_t launch_attn_plan(const AttnArgs& a, int32_t rows_cap, int32_t P, bool
   p.plan = plan;
   p.groups = reinterpret_cast<int4*>(reinterpret_cast<uint8_t*>(plan) + l.groups_off);
   p.seq_prefix = reinterpret_cast<int4*>(reinterpret_cast<uint8_t*>(plan) + l.seqpre_off);
+  p.members = reinterpret_cast<int32_t*>(reinterpret_cast<uint8_t*>(plan) + l.members_off);
   p.P = P;
   p.max_q = a.max_qlen;
   p.cap_dec = l.cap_dec;
@@ -935,6 +972,7 @@ hipError_t launch_attn_prefill(const AttnArgs& a, int32_t rows_cap, int32_t P, b
   const PlanLayout l = plan_layout(a.S, a.T, p.G, P, prefill_on, cascade_on);
   p.plan = plan;
   p.groups = reinterpret_cast<const int4*>(reinterpret_cast<const uint8_t*>(plan) + l.groups_off);
+  p.members = reinterpret_cast<const int32_t*>(reinterpret_cast<const uint8_t*>(plan) + l.members_off);
   p.ws_pre = ws_pre;
   const int64_t n_eb = (static_cast<int64_t>(l.cap_entries) + kQtRun - 1) / kQtRun;
   const int64_t items_raw = n_eb * kQtRun * a.Hkv;

@@ -81,11 +81,12 @@ pa_status_t attention_entry(AttnArgs a, const ScratchSource* scratch, hipStream_
 //   int2  entries[cap_entries]  (s >= 0, q-tile): a prefill query tile;
 //                               (-(group + 1), part): a part of a cascade
 //                               group's shared prefix
-//   int4  groups[cap_groups]    (first sequence, members, prefix tokens,
-//                               parts | first prefix slot << 8)
+//   int4  groups[cap_groups]    (first member-list position, members,
+//                               prefix tokens, parts | first prefix slot << 8)
 //   int4  seq_prefix[S]         (prefix tokens, parts, first prefix slot, first
 //                               row in the group) of the sequence's cascade
 //                               group; all 0 if it has none
+//   int32 members[S]            cascade members, each group a stretch
 //   int2  dec[2][S * P]         decode work lists, one-tile then two-tile:
 //                               (sequence, part), heaviest part first
 // Prefix partials live in their own workspace region: kCascadeEntries slots
@@ -114,11 +115,13 @@ constexpr int kCascadeMaxParts = 16;   // prefix parts of one group
 constexpr int kCascadeEntries = 64;    // prefix parts of one call, over all groups
 constexpr int kCascadeRows = 128;      // rows of one group: members x query heads
 constexpr int kCascadeMinTiles = 16;   // shortest shared prefix taken, in 64-token tiles
-constexpr int kCascadeMaxSeqs = 4096;  // sequences the detection handles (LDS)
+constexpr int kCascadeMaxSeqs = 1024;  // sequences the detection handles (one per plan thread)
+constexpr int kCascadeHashBits = 11;   // LDS hash table of first block ids: 2x the sequences
+constexpr int kCascadeHash = 1 << kCascadeHashBits;
 struct PlanLayout {
   int32_t cap_entries, cap_groups;
   int64_t cap_dec;                                 // entries of each decode list
-  size_t groups_off, seqpre_off, dec_off, bytes;  // byte offsets from the plan base; total
+  size_t groups_off, seqpre_off, members_off, dec_off, bytes;  // byte offsets from the plan base; total
 };
 PlanLayout plan_layout(int32_t S, int32_t T, int32_t G, int32_t P, bool prefill_on, bool cascade_on);
 // Shared-prefix (cascade) decode may run in this call: long enough contexts,

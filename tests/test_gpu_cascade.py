@@ -1,11 +1,12 @@
 """GPU parity of shared-prefix (cascade) decode, and a guard on workspace use.
 
 Sequences whose block tables map the same physical blocks at the same logical
-positions share those blocks' contents ("vLLM 原理" §2.1; the prefix caching
-of "LLM 推理引擎 Continuous Batching 与 PagedAttention" §5).  pa_attention
-finds runs of consecutive single-token decode sequences sharing at least 1024
-tokens from the start, reads each such prefix once for the whole run, and
-merges it with every member's own suffix.  The results must be those of
+positions share those blocks' contents ("vLLM 原理" §2.1; the shared prefixes
+and prefix caching of "LLM 推理引擎 Continuous Batching 与 PagedAttention"
+§4.1, §4.2).  pa_attention groups single-token decode sequences whose tables
+start with the same block and agree on at least 1024 tokens, wherever they
+sit in the batch, reads each such prefix once for the whole group, and merges
+it with every member's own suffix.  The results must be those of
 plain per-sequence attention (the oracle), whatever the grouping.
 """
 import numpy as np
@@ -15,7 +16,7 @@ import torch
 import oracle
 import ragged_paged_attention_amd as rpa
 from tests.gpu_path import GpuRun, max_abs_err, tol_for
-from workloads import config, verify_batch
+from workloads import config, permute_sequences, unshare, verify_batch
 from workloads.generators import build_workload
 
 pytestmark = pytest.mark.gpu
@@ -135,3 +136,29 @@ def test_workspace_writes_stay_inside_reported_size(make):
     assert bool((buf[need:] == 0xA5).all())
     _, _, _, ref = oracle.run_step(w, rows=[0, w.num_tokens - 1])
     assert max_abs_err(out[[0, w.num_tokens - 1]], ref) <= tol_for(w.dtype)
+
+
+@pytest.mark.parametrize("scale_down", [1, 4])
+def test_grouping_does_not_depend_on_batch_order(scale_down):
+    """The shared-prefix batch, its sequences shuffled: every sequence's output
+    is bit-identical to the unshuffled run's (the same groups, prefixes and
+    parts are found however the sharers are spread over the batch), the
+    grouping is really used (a copy with private blocks gives other bits),
+    and both match the oracle."""
+    w = config(5, scale_down=scale_down)
+    perm = np.random.default_rng(17).permutation(w.num_seqs)
+    wp = permute_sequences(w, perm)
+    print(f"[cascade order] {w.summary()}", flush=True)
+    a = GpuRun(w).run().out
+    b = GpuRun(wp).run().out
+    inv = np.argsort(perm)          # sequences are single-token: row i is sequence i
+    b_back = b[torch.from_numpy(inv).to("cuda")]
+    assert torch.equal(a.view(torch.int16), b_back.view(torch.int16))
+    w.num_blocks += int((w.step.block_tables >= 0).sum())
+    used = set(int(x) for x in w.step.block_tables.ravel() if x >= 0)
+    u = unshare(w, [x for x in range(w.num_blocks) if x not in used])
+    c = GpuRun(u).run().out
+    assert not torch.equal(a.view(torch.int16), c.view(torch.int16))
+    rows = list(range(0, w.num_tokens, max(1, w.num_tokens // 16)))
+    _, _, _, ref = oracle.run_step(wp, rows=rows)
+    assert max_abs_err(b[torch.tensor(rows, device="cuda")], ref) <= tol_for(w.dtype)

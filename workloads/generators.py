@@ -543,3 +543,19 @@ def plant_needles(w: Workload, seed: int = 0, logit: float = 40.0) -> Workload:
     return Workload(w.name + "_needles", w.dtype, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size,
                     w.num_blocks, step, q, hist, [list(x) for x in w.hist_segments], w.seed, w.poison,
                     w.notes)
+
+
+def permute_sequences(w: Workload, perm: Sequence[int]) -> Workload:
+    """The same batch with its sequences in another order: new sequence i is
+    old sequence perm[i] (its lengths, block-table row, new K/V/Q rows and
+    history entries move with it).  Block placement and values are unchanged,
+    so every sequence's attention is the same."""
+    perm = [int(x) for x in perm]
+    no = w.new_row_offsets()
+    rows = np.concatenate([np.arange(no[s], no[s + 1], dtype=np.int64) for s in perm]) if perm else \
+        np.zeros(0, dtype=np.int64)
+    step = Batch(w.step.query_lens[perm], w.step.seq_lens[perm], w.step.block_tables[perm], w.step.k[rows],
+                 w.step.v[rows])
+    return Workload(w.name + "_permuted", w.dtype, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size,
+                    w.num_blocks, step, w.q[rows], w.hist, [list(w.hist_segments[s]) for s in perm], w.seed,
+                    w.poison, w.notes)
