@@ -16,7 +16,8 @@
  * Conventions for every entry point:
  *   - All array arguments are DEVICE pointers to caller-owned, contiguous,
  *     row-major memory.  The library never allocates or frees device memory
- *     and never waits for the device on the host; all work is enqueued on
+ *     and never waits for the device on the host (unless the plan trace of
+ *     pa_set_trace is on); all work is enqueued on
  *     `stream` (a hipStream_t; NULL = default stream) and is complete when
  *     that stream is.  The caller owns the KV cache (the engine allocates
  *     one pool and hands out per-layer views, [VP] §3.6).
@@ -99,7 +100,9 @@ int32_t pa_set_kernel_policy(int32_t policy);
 
 /*
  * Input validation, process-wide (same thread-safety as the kernel policy):
- * 1 = on, 0 = off (default).  With it on, pa_write_kv with a non-NULL d_err
+ * 1 = on, 0 = off (the default, or on when the environment variable
+ * PA_VALIDATE is set to anything but "" or "0" when the library is loaded).
+ * With it on, pa_write_kv with a non-NULL d_err
  * also checks that no two rows of the call share an in-range slot and flags
  * PA_DERR_DUP_SLOT if they do ([VP] §2.1: copy-on-write keeps writers apart,
  * so a repeated slot is invalid input).  The check is one extra launch of
@@ -107,6 +110,24 @@ int32_t pa_set_kernel_policy(int32_t policy);
  * or -1 for a value other than 0 or 1 (unchanged).
  */
 int32_t pa_set_validation(int32_t on);
+
+/*
+ * Plan trace, process-wide (same thread-safety as the kernel policy): 1 = on,
+ * 0 = off (the default, or on when the environment variable PA_TRACE is set
+ * to anything but "" or "0" when the library is loaded).  With it on, every
+ * pa_attention call that launched its kernels then waits for its stream,
+ * copies its work plan from the workspace to the host and prints it to
+ * stderr, each line starting with "[pa_trace]": the path taken, the work
+ * split (query heads per KV head, decode parts, rows per decode item,
+ * whether prefill rows and shared prefixes are planned, workspace bytes),
+ * the prefill list (prefill query tiles and shared-prefix parts), every
+ * shared-prefix group (its members, prefix tokens and parts), the first
+ * entries of each decode list, and d_err.  The wait makes it a debugging aid:
+ * not for timing or graph capture.  pa_attention_noalloc never traces.
+ * Returns the previous setting, or -1 for a value other than 0 or 1
+ * (unchanged).
+ */
+int32_t pa_set_trace(int32_t on);
 
 /*
  * pa_build_metadata — flat-batch metadata of one step.

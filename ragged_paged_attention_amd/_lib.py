@@ -63,6 +63,8 @@ _lib.pa_set_kernel_policy.restype = _i32
 _lib.pa_set_kernel_policy.argtypes = [_i32]
 _lib.pa_set_validation.restype = _i32
 _lib.pa_set_validation.argtypes = [_i32]
+_lib.pa_set_trace.restype = _i32
+_lib.pa_set_trace.argtypes = [_i32]
 _lib.pa_build_metadata.restype = _i32
 _lib.pa_build_metadata.argtypes = [_p, _p, _i32, _i32, _p, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p]
 _lib.pa_write_kv.restype = _i32
@@ -117,6 +119,10 @@ def pa_set_kernel_policy(policy: int) -> int:
 
 def pa_set_validation(on: int) -> int:
     return int(_lib.pa_set_validation(int(on)))
+
+
+def pa_set_trace(on: int) -> int:
+    return int(_lib.pa_set_trace(int(on)))
 
 
 # --------------------------------------------------------------------------

@@ -32,7 +32,9 @@
 // parts with the rescaling algebra.  A sequence with one part writes out
 // directly.
 #include <algorithm>
+#include <cstdio>
 #include <mutex>
+#include <vector>
 
 #include "mfma_common.h"
 #include "pa_common.h"
@@ -778,6 +780,77 @@ hipError_t launch_attn_fast(const AttnArgs& a, hipStream_t stream, bool side_str
     launch_done(stream);
   }
   return hipGetLastError();
+}
+
+static void trace_header(const AttnArgs& a, const char* path) {
+  std::fprintf(stderr,
+               "[pa_trace] pa_attention S=%d T=%d Hq=%d Hkv=%d D=%d block_size=%d max_query_len=%d "
+               "max_seq_len=%d scale=%g path=%s\n",
+               a.S, a.T, a.Hq, a.Hkv, a.D, a.bs, a.max_qlen, a.max_seqlen, static_cast<double>(a.scale), path);
+}
+
+void trace_attn_generic(const AttnArgs& a) { trace_header(a, "generic"); }
+
+static hipError_t trace_d_err(const AttnArgs& a, hipStream_t stream) {
+  if (!a.d_err) return hipSuccess;
+  int32_t e = 0;
+  const hipError_t r = hipMemcpyAsync(&e, a.d_err, sizeof(e), hipMemcpyDeviceToHost, stream);
+  if (r == hipSuccess && hipStreamSynchronize(stream) == hipSuccess)
+    std::fprintf(stderr, "[pa_trace]   d_err=0x%x\n", static_cast<unsigned>(e));
+  return r;
+}
+
+// Waits for the call, copies its plan to the host and prints it.
+hipError_t trace_attn_fast(const AttnArgs& a, hipStream_t stream) {
+  const FastPlan f = fast_plan(a.S, a.T, a.Hq, a.Hkv, a.D, a.max_qlen, a.max_seqlen);
+  trace_header(a, "fast");
+  std::fprintf(stderr,
+               "[pa_trace]   split: G=%d decode_parts<=%d rows_per_decode_item<=%d "
+               "prefill_rows=%d shared_prefix=%d workspace_bytes=%zu\n",
+               f.G, f.P, f.rows_cap, f.prefill_on ? 1 : 0, f.cascade_on ? 1 : 0, f.bytes);
+  hipError_t e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return e;
+  if (!f.mfma_prefill) {
+    std::fprintf(stderr, "[pa_trace]   plan: none (decode items mapped directly: %d sequences x %d heads x %d parts)\n",
+                 a.S, a.Hkv, f.P);
+    return trace_d_err(a, stream);
+  }
+  const PlanLayout l = plan_layout(a.S, a.T, f.G, f.P, f.prefill_on, f.cascade_on);
+  std::vector<uint8_t> h(l.bytes);
+  e = hipMemcpy(h.data(), static_cast<const uint8_t*>(a.workspace) + f.plan_off, l.bytes, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return e;
+  const int32_t* hdr = reinterpret_cast<const int32_t*>(h.data());
+  const int2* entries = reinterpret_cast<const int2*>(hdr + kPlanHeader);
+  const int32_t n_entries = std::min(hdr[0], l.cap_entries), n_groups = std::min(hdr[1], l.cap_groups);
+  const int64_t n_dec[2] = {std::min<int64_t>(hdr[2], l.cap_dec), std::min<int64_t>(hdr[3], l.cap_dec)};
+  int32_t n_tiles = 0, n_parts = 0;
+  for (int32_t i = 0; i < n_entries; ++i) (entries[i].x >= 0 ? n_tiles : n_parts)++;
+  std::fprintf(stderr,
+               "[pa_trace]   plan: %d prefill-kernel entries (%d query tiles, %d shared-prefix parts), %d "
+               "shared-prefix groups, decode items %lld one-tile, %lld two-tile\n",
+               n_entries, n_tiles, n_parts, n_groups, static_cast<long long>(n_dec[0]),
+               static_cast<long long>(n_dec[1]));
+  const int4* groups = reinterpret_cast<const int4*>(h.data() + l.groups_off);
+  const int32_t* members = reinterpret_cast<const int32_t*>(h.data() + l.members_off);
+  for (int32_t g = 0; g < n_groups; ++g) {
+    const int4 gr = groups[g];
+    std::fprintf(stderr, "[pa_trace]   group %d: prefix_tokens=%d parts=%d first_prefix_slot=%d members=%d [", g,
+                 gr.z, gr.w & 255, gr.w >> 8, gr.y);
+    for (int32_t k = 0; k < gr.y && gr.x + k < a.S; ++k) std::fprintf(stderr, "%s%d", k ? " " : "", members[gr.x + k]);
+    std::fprintf(stderr, "]\n");
+  }
+  constexpr int32_t kShow = 32;
+  std::fprintf(stderr, "[pa_trace]   prefill list (sequence, query tile) or (-(group + 1), part), heaviest first:");
+  for (int32_t i = 0; i < std::min(n_entries, kShow); ++i) std::fprintf(stderr, " (%d,%d)", entries[i].x, entries[i].y);
+  std::fprintf(stderr, "%s\n", n_entries > kShow ? " ..." : "");
+  const int2* dec = reinterpret_cast<const int2*>(h.data() + l.dec_off);
+  for (int c = 0; c < 2; ++c) {
+    std::fprintf(stderr, "[pa_trace]   %s decode list (sequence, part), heaviest first:", c ? "two-tile" : "one-tile");
+    for (int64_t i = 0; i < std::min<int64_t>(n_dec[c], kShow); ++i)
+      std::fprintf(stderr, " (%d,%d)", dec[c * l.cap_dec + i].x, dec[c * l.cap_dec + i].y);
+    std::fprintf(stderr, "%s\n", n_dec[c] > kShow ? " ..." : "");
+  }
+  return trace_d_err(a, stream);
 }
 
 }  // namespace pa

@@ -69,8 +69,9 @@ struct PrefillArgs {
 };
 
 constexpr int kPlanThreads = 1024;
-constexpr int kCmpStep = 2048;  // block ids a wave compares per step (64 registers of loads in flight)
 constexpr int kPlanBuckets = 2048;  // K/V tile counts; larger ones share the top bucket
+constexpr int kMatchThreads = 256;  // matching kernel: one workgroup per sequence
+constexpr int kMatchU = 8;          // block ids per thread and compare step (2048 per step)
 
 struct PlanArgs {
   const int32_t* qsl;
@@ -83,8 +84,17 @@ struct PlanArgs {
   int4* groups;
   int4* seq_prefix;
   int32_t* members;  // cascade members, each leader's stretch in rank order
+  const int2* match; // per sequence: (leader, blocks shared with it), from cascade_match_kernel
   int2* dec;         // decode lists: one-tile at dec, two-tile at dec + cap_dec
   int32_t* d_err;
+};
+
+struct MatchArgs {
+  const int32_t* qsl;
+  const int32_t* seq_lens;
+  const int32_t* block_tables;
+  int32_t S, MB, bs, thr_blocks;
+  int2* match;
 };
 
 constexpr int kDecBuckets = 1024;  // decode list weights: chunks of a part, larger ones share the top bucket
@@ -99,11 +109,6 @@ __device__ __forceinline__ int32_t plan_weight(int32_t L, int32_t qlen, int32_t 
   if (L < qlen) return 1;  // invalid: the kernel only writes zeros
   const int32_t last_row = min(qt * kRowsPerWG + kRowsPerWG - 1, rows - 1);
   return min((L - qlen + last_row / G) / kTile + 1, kPlanBuckets - 1);
-}
-
-__device__ __forceinline__ int32_t wave_min_i32(int32_t v) {
-  for (int off = 32; off >= 1; off >>= 1) v = min(v, __shfl_xor(v, off, 64));
-  return v;
 }
 
 // Exclusive scan over the kPlanThreads threads of the plan workgroup (sum or
@@ -127,24 +132,115 @@ __device__ int32_t plan_block_scan(int32_t v, int32_t id, int32_t* wbuf) {
   return kMax ? max(before, excl) : before + excl;
 }
 
+// A cascade candidate: a single-token decode sequence with at least
+// thr_blocks full blocks and a valid first block id (its key).  The four
+// loads are unconditional (s < S, and the caller checks MB >= 1), so a
+// thread's loads for two sequences are all in flight together.
+struct Candidate {
+  int32_t key, full;
+  bool ok;
+};
+__device__ __forceinline__ Candidate cascade_candidate(const MatchArgs& a, int32_t s) {
+  const int32_t q0 = a.qsl[s], q1 = a.qsl[s + 1], L = a.seq_lens[s];
+  const int32_t key = a.block_tables[static_cast<int64_t>(s) * a.MB];
+  Candidate c;
+  c.key = key;
+  c.full = L / a.bs;
+  c.ok = q1 - q0 == 1 && L >= 1 && ceil_div(L, a.bs) <= a.MB && c.full >= a.thr_blocks && key >= 0;
+  return c;
+}
+
+// Smallest value any thread of the workgroup offers (INT32_MAX if none);
+// every thread must call it.
+__device__ __forceinline__ int32_t match_block_min(int32_t v, int32_t* cell) {
+  if (threadIdx.x == 0) *cell = INT32_MAX;
+  __syncthreads();
+  if (v != INT32_MAX) atomicMin(cell, v);
+  __syncthreads();
+  const int32_t m = *cell;
+  __syncthreads();  // the cell is reused by the next call
+  return m;
+}
+
+// Cascade matching, one workgroup per sequence s ("vLLM 原理" §2.1, and the
+// shared prefixes of "LLM 推理引擎 Continuous Batching 与 PagedAttention"
+// §4.1, §4.2: sequences whose tables map the same physical block at the same
+// logical position share that block's contents).  A candidate's leader is
+// the smallest candidate with the same first block id (itself if there is
+// none before it), so the grouping depends only on which tables share
+// blocks, not on where the sequences sit in the batch.  A follower compares
+// its table with its leader's from the start; match[s] = (leader, full
+// blocks the two agree on from the start), (s, full blocks) for a leader and
+// (-1, 0) for a sequence that is no candidate.
+__global__ __launch_bounds__(kMatchThreads) void cascade_match_kernel(MatchArgs a) {
+  __shared__ int32_t cell, leader_full;
+  const int32_t s = blockIdx.x;
+  const int tid = threadIdx.x;
+  if (a.MB < 1) {  // no table entries: no candidates (and no row to read)
+    if (tid == 0) a.match[s] = make_int2(-1, 0);
+    return;
+  }
+  // this sequence and the first kMatchThreads sequences, loads in flight together
+  const Candidate me = cascade_candidate(a, s);
+  Candidate other = cascade_candidate(a, min(tid, s));
+  if (!me.ok) {
+    if (tid == 0) a.match[s] = make_int2(-1, 0);
+    return;
+  }
+  int32_t ld = s;
+  for (int32_t t0 = 0; t0 < s; t0 += kMatchThreads) {
+    const int32_t t = t0 + tid;
+    if (t0 > 0) other = cascade_candidate(a, min(t, s));
+    const bool hit = t < s && other.ok && other.key == me.key;
+    const int32_t m = match_block_min(hit ? t : INT32_MAX, &cell);
+    if (m != INT32_MAX) {
+      if (t == m) leader_full = other.full;
+      __syncthreads();
+      ld = m;
+      break;
+    }
+  }
+  int32_t first = me.full;
+  if (ld != s) {
+    const int32_t n = min(me.full, leader_full);
+    const int32_t* b0 = a.block_tables + static_cast<int64_t>(ld) * a.MB;
+    const int32_t* b1 = a.block_tables + static_cast<int64_t>(s) * a.MB;
+    first = n;
+    for (int32_t j0 = 0; j0 < n; j0 += kMatchThreads * kMatchU) {
+      // all loads first (indices clamped into the row), then the compares
+      int32_t x0[kMatchU], x1[kMatchU];
+#pragma unroll
+      for (int u = 0; u < kMatchU; ++u) {
+        const int32_t j = min(j0 + kMatchThreads * u + tid, n - 1);
+        x0[u] = b0[j];
+        x1[u] = b1[j];
+      }
+      int32_t mn = INT32_MAX;
+#pragma unroll
+      for (int u = 0; u < kMatchU; ++u) {
+        const int32_t j = j0 + kMatchThreads * u + tid;
+        if (j < n && x0[u] != x1[u]) mn = min(mn, j);
+      }
+      const int32_t m = match_block_min(mn, &cell);
+      if (m != INT32_MAX) {
+        first = m;
+        break;
+      }
+    }
+  }
+  if (tid == 0) a.match[s] = make_int2(ld, first);
+}
+
 // One workgroup plans the call.
 //
-// Cascade groups ("vLLM 原理" §2.1 and the shared prefixes and automatic
-// prefix caching of "LLM 推理引擎 Continuous Batching 与 PagedAttention"
-// §4.1, §4.2: sequences whose tables map the same physical block at the same
-// logical position share that block's contents).  Candidates are
-// single-token decode sequences with at least kCascadeMinTiles full 64-token
-// tiles; those whose first block ids are equal are gathered through an LDS
-// hash table keyed by that id, whose entry keeps the smallest such sequence
-// (the leader), so the grouping depends only on which tables share blocks,
-// not on where the sequences sit in the batch.  Every other candidate
-// compares its table with its leader's from the start and joins if they
-// agree on at least kCascadeMinTiles tiles; the group's shared prefix is the
-// fewest blocks any joined member shares with the leader, rounded down to
-// whole tiles (members agree pairwise there), read once for all members in up
-// to kCascadeMaxParts parts.  A leader's members are listed in the plan
-// (rank order) and cut into groups of at most kCascadeRows / G; groups take
-// their indices in leader order, and the first kCascadeEntries are cascaded.
+// Cascade groups, from cascade_match_kernel's (leader, shared blocks) of each
+// candidate: a follower that agrees with its leader on at least
+// kCascadeMinTiles tiles joins it; the group's shared prefix is the fewest
+// blocks any joined member shares with the leader, rounded down to whole
+// tiles (members agree pairwise there), read once for all members in up to
+// kCascadeMaxParts parts.  A leader's members are listed in the plan (rank
+// order) and cut into groups of at most kCascadeRows / G; groups take their
+// indices in leader order, and the first kCascadeEntries are cascaded.
 //
 // Work list: every prefill-class (sequence, query tile) and every cascade
 // prefix part, counting-sorted by the K/V tiles it reads, heaviest first.
@@ -156,14 +252,10 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(PlanArgs a) {
   __shared__ int32_t hist[kPlanBuckets];
   __shared__ int32_t cursor[kPlanBuckets];
   __shared__ int32_t wave_tot[kPlanThreads / 64];
-  __shared__ int32_t common_blocks[kCascadeMaxSeqs];  // full blocks; for a follower then the blocks it shares with its leader
-  __shared__ int32_t slot_of[kCascadeMaxSeqs];        // hash slot of the sequence's first block id, -1 if no candidate
-  __shared__ int32_t gbase_of[kCascadeMaxSeqs];       // leader with members: its first group index, else -1
-  __shared__ int32_t mbase_of[kCascadeMaxSeqs];       // leader with members: its first member-list position
-  __shared__ int32_t hkey[kCascadeHash];              // first block id of the slot, -1 while empty
-  __shared__ int32_t hmin[kCascadeHash];              // smallest candidate with that id: the leader
-  __shared__ int32_t hcnt[kCascadeHash];              // joined followers, later the rank counter
-  __shared__ int32_t hpre[kCascadeHash];              // fewest blocks a joined follower shares with the leader
+  __shared__ int32_t gbase_of[kCascadeMaxSeqs];  // leader with members: its first group index, else -1
+  __shared__ int32_t mbase_of[kCascadeMaxSeqs];  // leader with members: its first member-list position
+  __shared__ int32_t hcnt[kCascadeMaxSeqs];      // leader: joined followers, later the rank counter
+  __shared__ int32_t hpre[kCascadeMaxSeqs];      // leader: fewest blocks a joined follower shares with it
   __shared__ int32_t n_groups;
   __shared__ int32_t dhist[2][kDecBuckets];
   __shared__ int32_t dcur[2][kDecBuckets];
@@ -181,110 +273,42 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(PlanArgs a) {
   // possible at all, else once at the very end.
   bool prefix_zero_late = false;
   if (a.cascade_on) {
+    static_assert(kCascadeMaxSeqs == kPlanThreads, "one sequence per thread in the cascade phases");
     const int32_t thr_blocks = ceil_div(kCascadeMinTiles * kTile, a.bs);
     const int32_t max_members = max(2, kCascadeRows / a.G);
-    for (int i = tid; i < kCascadeHash; i += kPlanThreads) {
-      hkey[i] = -1;
-      hmin[i] = INT32_MAX;
-      hcnt[i] = 0;
-      hpre[i] = INT32_MAX;
-    }
+    const int32_t s = tid;
+    int2 m = make_int2(-1, 0);
+    if (s < a.S) m = a.match[s];
+    gbase_of[s] = -1;
+    hcnt[s] = 0;
+    hpre[s] = INT32_MAX;
     __syncthreads();
-    // candidates into the hash table (at most kCascadeMaxSeqs keys in twice as
-    // many slots, so linear probing always finds a free or matching slot)
-    for (int32_t s = tid; s < a.S; s += kPlanThreads) {
-      int32_t slot = -1, full = 0;
-      const int32_t ql = a.qsl[s + 1] - a.qsl[s], L = a.seq_lens[s];
-      if (ql == 1 && L >= 1 && ceil_div(L, a.bs) <= a.MB) {
-        full = L / a.bs;
-        const int32_t key = a.block_tables[static_cast<int64_t>(s) * a.MB];
-        if (full >= thr_blocks && key >= 0) {
-          int32_t h = static_cast<int32_t>((static_cast<uint32_t>(key) * 2654435761u) >> (32 - kCascadeHashBits));
-          for (;;) {
-            const int32_t old = atomicCAS(&hkey[h], -1, key);
-            if (old == -1 || old == key) break;
-            h = (h + 1) & (kCascadeHash - 1);
-          }
-          atomicMin(&hmin[h], s);
-          slot = h;
-        }
-      }
-      slot_of[s] = slot;
-      common_blocks[s] = full;
-      gbase_of[s] = -1;
+    // followers sharing at least thr_blocks with their leader join it
+    const bool joins = m.x >= 0 && m.x != s && m.y >= thr_blocks;
+    if (joins) {
+      atomicAdd(&hcnt[m.x], 1);
+      atomicMin(&hpre[m.x], m.y);
     }
-    __syncthreads();
-    bool follower = false;  // a candidate that is not its slot's leader
-    for (int32_t s = tid; s < a.S; s += kPlanThreads) follower |= slot_of[s] >= 0 && hmin[slot_of[s]] != s;
-    if (!__syncthreads_or(follower)) {  // no two candidates start with the same block: no group
+    if (!__syncthreads_or(joins)) {  // no follower joined: no group
       prefix_zero_late = true;
       if (tid == 0) a.plan[1] = 0;
     } else {
-      for (int32_t s = tid; s < a.S; s += kPlanThreads) a.seq_prefix[s] = make_int4(0, 0, 0, 0);
-      // each follower's first block differing from its leader's, one wave per
-      // follower, kCmpStep blocks per step with all their loads in flight
-      // (leaders' entries of common_blocks are only read here)
-      for (int32_t s = wave; s < a.S; s += kPlanThreads / 64) {
-        const int32_t slot = slot_of[s];
-        if (slot < 0) continue;
-        const int32_t ld = hmin[slot];
-        if (ld == s) continue;
-        const int32_t n = min(common_blocks[s], common_blocks[ld]);
-        const int32_t* b0 = a.block_tables + static_cast<int64_t>(ld) * a.MB;
-        const int32_t* b1 = a.block_tables + static_cast<int64_t>(s) * a.MB;
-        int32_t first = n;
-        for (int32_t j0 = 0; j0 < n && first == n; j0 += kCmpStep) {
-          // unconditional loads (index clamped into the row) first, then the
-          // compares: with the loads under the j < n test the compiler issued
-          // them one pair at a time, waiting for each
-          constexpr int kU = kCmpStep / 64;
-          int32_t x0[kU], x1[kU];
-#pragma unroll
-          for (int u = 0; u < kU; ++u) {
-            const int32_t j = min(j0 + 64 * u + lane, n - 1);
-            x0[u] = b0[j];
-            x1[u] = b1[j];
-          }
-          int32_t mn = n;
-#pragma unroll
-          for (int u = 0; u < kU; ++u) {
-            const int32_t j = j0 + 64 * u + lane;
-            if (j < n && x0[u] != x1[u]) mn = min(mn, j);
-          }
-          first = wave_min_i32(mn);
-        }
-        if (lane == 0) common_blocks[s] = first;
-      }
-      __syncthreads();
-      // followers sharing at least thr_blocks with their leader join it
-      for (int32_t s = tid; s < a.S; s += kPlanThreads) {
-        const int32_t slot = slot_of[s];
-        if (slot >= 0 && hmin[slot] != s && common_blocks[s] >= thr_blocks) {
-          atomicAdd(&hcnt[slot], 1);
-          atomicMin(&hpre[slot], common_blocks[s]);
-        }
-      }
-      __syncthreads();
+      if (s < a.S) a.seq_prefix[s] = make_int4(0, 0, 0, 0);
       // groups in leader order: a leader with members heads ceil(members /
       // max_members) groups over its stretch of the member list
-      static_assert(kCascadeMaxSeqs == kPlanThreads, "one sequence per thread in the group scan");
       {
-        const int32_t s = tid;
-        int32_t ngs = 0, nms = 0, slot = -1;
-        if (s < a.S) {
-          slot = slot_of[s];
-          if (slot >= 0 && hmin[slot] == s && hcnt[slot] > 0) {
-            nms = hcnt[slot] + 1;  // the followers and the leader
-            ngs = ceil_div(nms, max_members);
-          }
+        int32_t ngs = 0, nms = 0;
+        if (m.x == s && hcnt[s] > 0) {
+          nms = hcnt[s] + 1;  // the followers and the leader
+          ngs = ceil_div(nms, max_members);
         }
         const int32_t gb = plan_block_scan<false>(ngs, 0, wave_tot);
         const int32_t mb = plan_block_scan<false>(nms, 0, wave_tot);
         if (ngs > 0) {
           gbase_of[s] = gb;
           mbase_of[s] = mb;
-          hcnt[slot] = 0;  // from here on the slot's rank counter
-          const int32_t pre_tokens = hpre[slot] * a.bs / kTile * kTile;
+          hcnt[s] = 0;  // from here on the leader's rank counter
+          const int32_t pre_tokens = hpre[s] * a.bs / kTile * kTile;
           for (int32_t c = 0; c < ngs && gb + c < a.cap_groups; ++c)
             a.groups[gb + c] = make_int4(mb + c * max_members, min(max_members, nms - c * max_members), pre_tokens, 0);
         }
@@ -317,12 +341,9 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(PlanArgs a) {
       // leader's stretch of the member list (any order: a member's rows give
       // the same values wherever they sit in the group), and a member of a
       // cascaded group gets its prefix record
-      for (int32_t s = tid; s < a.S; s += kPlanThreads) {
-        const int32_t slot = slot_of[s];
-        if (slot < 0) continue;
-        const int32_t ld = hmin[slot];
-        if (gbase_of[ld] < 0 || (ld != s && common_blocks[s] < thr_blocks)) continue;
-        const int32_t r = atomicAdd(&hcnt[slot], 1);
+      const int32_t ld = m.x;
+      if (ld >= 0 && gbase_of[ld] >= 0 && (ld == s || joins)) {
+        const int32_t r = atomicAdd(&hcnt[ld], 1);
         a.members[mbase_of[ld] + r] = s;
         const int32_t gi = gbase_of[ld] + r / max_members;
         if (gi < ngr) {
@@ -335,6 +356,26 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(PlanArgs a) {
   }
   __syncthreads();
   const int32_t ng = n_groups;
+
+  // A decode-class sequence's item: list c (one-tile 0, two-tile 1) and the
+  // chunks its parts cover (nch, the cascade prefix removed); special: the
+  // decode kernels only zero-fill it (one weight-0 part).  False: no decode item.
+  auto dec_item = [&](int32_t s, int32_t& c, int32_t& nch, bool& special) -> bool {
+    const int32_t qlen = a.qsl[s + 1] - a.qsl[s];
+    if (qlen <= 0 || qlen > a.T) return false;
+    const int32_t rows = qlen * a.G;
+    c = 0;
+    nch = 0;
+    special = true;
+    if (rows > a.rows_cap) return !a.prefill_on;
+    c = rows > 16 ? 1 : 0;
+    const int32_t L = a.seq_lens[s];
+    if (L < qlen || ceil_div(L, a.bs) > a.MB) return true;
+    const int32_t pre = a.cascade_on && !prefix_zero_late ? a.seq_prefix[s].x : 0;
+    nch = ceil_div(L, 16) - pre / 16;
+    special = false;
+    return true;
+  };
 
   // Histogram by the weight of each sequence's heaviest query tile (its
   // last) and of each group's prefix parts.  A sequence's query tiles stay
@@ -407,25 +448,10 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(PlanArgs a) {
   // last.  The max_query_len hint is checked here for every sequence.
   // (dhist was cleared at the start; no barrier here, so the list entries'
   // stores above need not complete before the decode histogram is built)
-  // list c, parts np of cpp chunks over nch chunks; special: one weight-0 part
-  auto dec_item = [&](int32_t s, int32_t& c, int32_t& np, int32_t& cpp, int32_t& nch, bool& special) -> bool {
-    const int32_t qlen = a.qsl[s + 1] - a.qsl[s];
-    if (qlen <= 0 || qlen > a.T) return false;
-    const int32_t rows = qlen * a.G;
-    c = 0;
+  auto item_parts = [&](int32_t nch, bool special, int32_t& np, int32_t& cpp) {
     np = 1;
     cpp = 0;
-    nch = 0;
-    special = true;
-    if (rows > a.rows_cap) return !a.prefill_on;
-    c = rows > 16 ? 1 : 0;
-    const int32_t L = a.seq_lens[s];
-    if (L < qlen || ceil_div(L, a.bs) > a.MB) return true;
-    const int32_t pre = a.cascade_on && !prefix_zero_late ? a.seq_prefix[s].x : 0;
-    nch = ceil_div(L, 16) - pre / 16;
-    plan_parts(nch, a.P, &np, &cpp);
-    special = false;
-    return true;
+    if (!special) plan_parts(nch, a.P, &np, &cpp);
   };
   auto part_weight = [&](int32_t p, int32_t cpp, int32_t nch, bool special) {
     return special ? 0 : min(min(cpp, nch - p * cpp), kDecBuckets - 1);
@@ -435,7 +461,8 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(PlanArgs a) {
     if (qlen > a.max_q) flag(a.d_err, PA_DERR_HINT);
     int32_t c, np, cpp, nch;
     bool special;
-    if (!dec_item(s, c, np, cpp, nch, special)) continue;
+    if (!dec_item(s, c, nch, special)) continue;
+    item_parts(nch, special, np, cpp);
     for (int32_t p = 0; p < np; ++p) atomicAdd(&dhist[c][part_weight(p, cpp, nch, special)], 1);
   }
   __syncthreads();
@@ -454,7 +481,8 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(PlanArgs a) {
   for (int32_t s = tid; s < a.S; s += kPlanThreads) {
     int32_t c, np, cpp, nch;
     bool special;
-    if (!dec_item(s, c, np, cpp, nch, special)) continue;
+    if (!dec_item(s, c, nch, special)) continue;
+    item_parts(nch, special, np, cpp);
     int2* list = a.dec + c * a.cap_dec;
     for (int32_t p = 0; p < np; ++p) {
       const int32_t pos = atomicAdd(&dcur[c][part_weight(p, cpp, nch, special)], 1);
@@ -906,7 +934,8 @@ PlanLayout plan_layout(int32_t S, int32_t T, int32_t G, int32_t P, bool prefill_
   l.groups_off = (static_cast<size_t>(kPlanHeader) * 4 + static_cast<size_t>(cap) * 8 + 15) & ~static_cast<size_t>(15);
   l.seqpre_off = l.groups_off + static_cast<size_t>(l.cap_groups) * 16;
   l.members_off = l.seqpre_off + (cascade_on ? static_cast<size_t>(S) * 16 : 0);
-  l.dec_off = (l.members_off + (cascade_on ? static_cast<size_t>(S) * 4 : 0) + 15) & ~static_cast<size_t>(15);
+  l.match_off = (l.members_off + (cascade_on ? static_cast<size_t>(S) * 4 : 0) + 7) & ~static_cast<size_t>(7);
+  l.dec_off = (l.match_off + (cascade_on ? static_cast<size_t>(S) * 8 : 0) + 15) & ~static_cast<size_t>(15);
   l.cap_dec = static_cast<int64_t>(S) * P;
   l.bytes = l.dec_off + static_cast<size_t>(2 * l.cap_dec) * 8;
   return l;
@@ -938,11 +967,27 @@ hipError_t launch_attn_plan(const AttnArgs& a, int32_t rows_cap, int32_t P, bool
   p.groups = reinterpret_cast<int4*>(reinterpret_cast<uint8_t*>(plan) + l.groups_off);
   p.seq_prefix = reinterpret_cast<int4*>(reinterpret_cast<uint8_t*>(plan) + l.seqpre_off);
   p.members = reinterpret_cast<int32_t*>(reinterpret_cast<uint8_t*>(plan) + l.members_off);
+  int2* match = reinterpret_cast<int2*>(reinterpret_cast<uint8_t*>(plan) + l.match_off);
+  p.match = match;
   p.P = P;
   p.max_q = a.max_qlen;
   p.cap_dec = l.cap_dec;
   p.dec = reinterpret_cast<int2*>(reinterpret_cast<uint8_t*>(plan) + l.dec_off);
   p.d_err = a.d_err;
+  if (cascade_on) {
+    MatchArgs m;
+    m.qsl = a.qsl;
+    m.seq_lens = a.seq_lens;
+    m.block_tables = a.block_tables;
+    m.S = a.S;
+    m.MB = a.MB;
+    m.bs = a.bs;
+    m.thr_blocks = ceil_div(kCascadeMinTiles * kTile, a.bs);
+    m.match = match;
+    launch_mark("cascade_match_kernel", stream);
+    cascade_match_kernel<<<static_cast<uint32_t>(a.S), kMatchThreads, 0, stream>>>(m);
+    launch_done(stream);
+  }
   launch_mark("attn_plan_kernel", stream);
   attn_plan_kernel<<<1, kPlanThreads, 0, stream>>>(p);
   launch_done(stream);

@@ -7,14 +7,23 @@
 #include <climits>
 #include <cmath>
 #include <cstdio>
+#include <cstdlib>
+#include <cstring>
 
 #include "pa.h"
 #include "pa_internal.h"
 
 namespace {
 
+// A debugging switch from the environment: set and not "" or "0".
+int32_t env_flag(const char* name) {
+  const char* v = std::getenv(name);
+  return v && v[0] && std::strcmp(v, "0") != 0 ? 1 : 0;
+}
+
 std::atomic<int32_t> g_policy{PA_POLICY_AUTO};
-std::atomic<int32_t> g_validate{0};
+std::atomic<int32_t> g_validate{env_flag("PA_VALIDATE")};
+std::atomic<int32_t> g_trace{env_flag("PA_TRACE")};
 thread_local char g_last_hip_error[256] = "";
 
 // Clears an error left behind by earlier, unrelated HIP calls in this thread,
@@ -76,7 +85,10 @@ pa_status_t attention_entry(AttnArgs a, const ScratchSource* scratch, hipStream_
     if (!fast_ok) return PA_ERR_UNSUPPORTED;
     if (need > 0 && (!a.workspace || a.workspace_bytes < need)) return PA_ERR_WORKSPACE;
     e = launch_attn_fast(a, stream, /*side_stream_ok=*/scratch == nullptr);
+    if (e == hipSuccess && !scratch && g_trace.load()) e = trace_attn_fast(a, stream);
+    return hip_status(e, "pa_attention");
   }
+  if (e == hipSuccess && !scratch && g_trace.load()) trace_attn_generic(a);
   return hip_status(e, "pa_attention");
 }
 
@@ -105,6 +117,11 @@ const char* pa_last_hip_error(void) { return g_last_hip_error; }
 int32_t pa_set_validation(int32_t on) {
   if (on != 0 && on != 1) return -1;
   return g_validate.exchange(on);
+}
+
+int32_t pa_set_trace(int32_t on) {
+  if (on != 0 && on != 1) return -1;
+  return g_trace.exchange(on);
 }
 
 int32_t pa_set_kernel_policy(int32_t policy) {

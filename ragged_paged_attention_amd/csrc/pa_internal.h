@@ -62,6 +62,10 @@ size_t fast_workspace_bytes(int32_t S, int32_t T, int32_t Hq, int32_t Hkv, int32
 // the library's side stream (created on first use); false keeps every launch
 // on `stream`.
 hipError_t launch_attn_fast(const AttnArgs& a, hipStream_t stream, bool side_stream_ok);
+// Plan trace (pa_set_trace): waits for `stream`, then prints the call's work
+// split and plan to stderr; the generic path prints its header line only.
+hipError_t trace_attn_fast(const AttnArgs& a, hipStream_t stream);
+void trace_attn_generic(const AttnArgs& a);
 
 // A workspace owned by the library (pa_attention_noalloc): its size, and how
 // to find the current device's copy.
@@ -87,6 +91,9 @@ pa_status_t attention_entry(AttnArgs a, const ScratchSource* scratch, hipStream_
 //                               row in the group) of the sequence's cascade
 //                               group; all 0 if it has none
 //   int32 members[S]            cascade members, each group a stretch
+//   int2  match[S]              (leader, full blocks shared with it) of a
+//                               cascade candidate, written by the matching
+//                               kernel before the plan; (-1, 0) otherwise
 //   int2  dec[2][S * P]         decode work lists, one-tile then two-tile:
 //                               (sequence, part), heaviest part first
 // Prefix partials live in their own workspace region: kCascadeEntries slots
@@ -116,12 +123,10 @@ constexpr int kCascadeEntries = 64;    // prefix parts of one call, over all gro
 constexpr int kCascadeRows = 128;      // rows of one group: members x query heads
 constexpr int kCascadeMinTiles = 16;   // shortest shared prefix taken, in 64-token tiles
 constexpr int kCascadeMaxSeqs = 1024;  // sequences the detection handles (one per plan thread)
-constexpr int kCascadeHashBits = 11;   // LDS hash table of first block ids: 2x the sequences
-constexpr int kCascadeHash = 1 << kCascadeHashBits;
 struct PlanLayout {
   int32_t cap_entries, cap_groups;
   int64_t cap_dec;                                 // entries of each decode list
-  size_t groups_off, seqpre_off, members_off, dec_off, bytes;  // byte offsets from the plan base; total
+  size_t groups_off, seqpre_off, members_off, match_off, dec_off, bytes;  // byte offsets from the plan base; total
 };
 PlanLayout plan_layout(int32_t S, int32_t T, int32_t G, int32_t P, bool prefill_on, bool cascade_on);
 // Shared-prefix (cascade) decode may run in this call: long enough contexts,

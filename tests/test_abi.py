@@ -2,7 +2,9 @@
 declares; host-side argument checks return their status codes without
 touching a GPU (null pointers and bad sizes are rejected before any launch)."""
 import ctypes
+import os
 import subprocess
+import sys
 
 import pytest
 
@@ -32,6 +34,26 @@ def test_validation_switch_roundtrip():
     prev = rpa.pa_set_validation(1)
     assert rpa.pa_set_validation(prev) == 1
     assert rpa.pa_set_validation(2) == -1
+
+
+def test_trace_switch_roundtrip():
+    prev = rpa.pa_set_trace(1)
+    assert rpa.pa_set_trace(prev) == 1
+    assert rpa.pa_set_trace(-1) == -1
+
+
+@pytest.mark.parametrize("value,expected", [("1", ["1", "1"]), ("yes", ["1", "1"]), ("0", ["0", "0"]),
+                                            ("", ["0", "0"])])
+def test_environment_sets_trace_and_validation_at_load(value, expected):
+    """PA_TRACE and PA_VALIDATE in the environment at load time give the
+    switches' initial values (a fresh process: the library reads them once)."""
+    code = "import ragged_paged_attention_amd as r; print(r.pa_set_trace(0), r.pa_set_validation(0))"
+    env = {**os.environ, "PA_TRACE": value, "PA_VALIDATE": value}
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    out = subprocess.run([sys.executable, "-c", code], env=env, cwd=root, capture_output=True, text=True,
+                         timeout=120)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.split() == expected
 
 
 def test_kernel_policy_roundtrip():

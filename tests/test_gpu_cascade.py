@@ -9,6 +9,10 @@ sit in the batch, reads each such prefix once for the whole group, and merges
 it with every member's own suffix.  The results must be those of
 plain per-sequence attention (the oracle), whatever the grouping.
 """
+import os
+import re
+import tempfile
+
 import numpy as np
 import pytest
 import torch
@@ -162,3 +166,45 @@ def test_grouping_does_not_depend_on_batch_order(scale_down):
     rows = list(range(0, w.num_tokens, max(1, w.num_tokens // 16)))
     _, _, _, ref = oracle.run_step(wp, rows=rows)
     assert max_abs_err(b[torch.tensor(rows, device="cuda")], ref) <= tol_for(w.dtype)
+
+
+def _capture_fd2(fn):
+    """Runs fn() with file descriptor 2 sent to a temporary file; returns
+    fn's result and what was written there."""
+    with tempfile.TemporaryFile(mode="w+b") as tmp:
+        saved = os.dup(2)
+        try:
+            os.dup2(tmp.fileno(), 2)
+            res = fn()
+            torch.cuda.synchronize()
+        finally:
+            os.dup2(saved, 2)
+            os.close(saved)
+        tmp.seek(0)
+        return res, tmp.read().decode()
+
+
+def test_trace_lists_the_groups():
+    """With the plan trace on, the call prints its plan: the three groups of
+    the three_groups batch with their members and prefix tokens (2048; 1040
+    and 1520 rounded down to whole 64-token tiles), and the output still
+    matches the oracle."""
+    c = CASES["three_groups"]
+    w = grouped_batch(len("three_groups"), c["segs"], c["Hq"], c["Hkv"])
+    prev = rpa.pa_set_trace(1)
+    try:
+        g, text = _capture_fd2(lambda: GpuRun(w).run())
+    finally:
+        rpa.pa_set_trace(prev)
+    print(text, flush=True)
+    assert "path=fast" in text and "shared_prefix=1" in text
+    groups = {}
+    for m in re.finditer(r"group \d+: prefix_tokens=(\d+) parts=(\d+) first_prefix_slot=\d+ members=(\d+) "
+                         r"\[([0-9 ]*)\]", text):
+        members = tuple(sorted(int(x) for x in m.group(4).split()))
+        assert len(members) == int(m.group(3)) and int(m.group(2)) >= 1
+        groups[members] = int(m.group(1))
+    assert groups == {tuple(range(0, 5)): 2048, (6, 7): 1024, tuple(range(9, 18)): 1472}
+    assert "d_err=0x0" in text
+    _, _, _, ref = oracle.run_step(w)
+    assert max_abs_err(g.out, ref) <= tol_for(w.dtype)
