@@ -33,7 +33,6 @@
 // directly.
 #include <algorithm>
 #include <cstdio>
-#include <mutex>
 #include <vector>
 
 #include "mfma_common.h"
@@ -656,40 +655,7 @@ static void launch_merge(const DecodeArgs& d, int32_t D, dim3 grid, hipStream_t 
   else merge_kernel<F, 128><<<grid, 256, 0, stream>>>(d);
 }
 
-// A side stream per device for the two-tile decode launch.  The one-tile and
-// two-tile instances take disjoint items and are both HBM-bound; a batch
-// whose items split between them (a verify step of a few draft tokens) fills
-// the machine only partly with either alone (verify batch 0.525 -> 0.504 ms).
-// Used when no prefill rows can come (max_query_len x G <= 32): with them,
-// two-tile items are rare and the fork and join only cost time.  Created on
-// first use, default priority, never destroyed; the fork and join events are
-// recorded and waited on under one lock, so concurrent calls cannot
-// interleave them.
-namespace {
-struct SideStream {
-  hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-  bool ok = false, tried = false;
-};
-constexpr int kMaxDevices = 64;
-SideStream g_side[kMaxDevices];
-std::mutex g_side_mu;
-
-SideStream* side_stream_locked() {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
-  SideStream& ss = g_side[dev];
-  if (!ss.tried) {
-    ss.tried = true;
-    ss.ok = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) == hipSuccess &&
-            hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) == hipSuccess &&
-            hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) == hipSuccess;
-  }
-  return ss.ok ? &ss : nullptr;
-}
-}  // namespace
-
-hipError_t launch_attn_fast(const AttnArgs& a, hipStream_t stream, bool side_stream_ok) {
+hipError_t launch_attn_fast(const AttnArgs& a, hipStream_t stream) {
   const FastPlan f = fast_plan(a.S, a.T, a.Hq, a.Hkv, a.D, a.max_qlen, a.max_seqlen);
   DecodeArgs d;
   d.q = static_cast<const uint16_t*>(a.q);
@@ -743,34 +709,21 @@ hipError_t launch_attn_fast(const AttnArgs& a, hipStream_t stream, bool side_str
     d.dec_list[1] = dec + l.cap_dec;
     d.dec_n = plan + 2;
   }
+  // Both decode instances on `stream`, one after the other.  Running the
+  // two-tile launch on a second stream beside the one-tile launch (both
+  // HBM-bound, each filling the machine only partly) measured slower once the
+  // plan's sorted work lists were in place: verify batch 0.459 ms side by
+  // side, 0.437 ms one after the other (either order).
   const bool blk16 = a.bs % kChunk == 0;
-  std::unique_lock<std::mutex> side_lock(g_side_mu, std::defer_lock);
-  SideStream* side = nullptr;
-  hipStream_t s2 = stream;  // the two-tile launch's stream
-  if (d.rows_cap > kTileRows && !f.prefill_on && side_stream_ok) {
-    side_lock.lock();
-    side = side_stream_locked();
-    if (side && hipEventRecord(side->fork, stream) == hipSuccess &&
-        hipStreamWaitEvent(side->s, side->fork, 0) == hipSuccess)
-      s2 = side->s;
-    else
-      side = nullptr;
-  }
-  if (d.rows_cap > kTileRows) {
-    launch_mark("decode_kernel_2t", s2);
-    if (a.dtype == PA_BF16) launch_decode<BF16, 2>(d, a.D, blk16, static_cast<uint32_t>(grid), s2);
-    else launch_decode<F16, 2>(d, a.D, blk16, static_cast<uint32_t>(grid), s2);
-    launch_done(s2);
-  }
   launch_mark("decode_kernel", stream);
   if (a.dtype == PA_BF16) launch_decode<BF16, 1>(d, a.D, blk16, static_cast<uint32_t>(grid), stream);
   else launch_decode<F16, 1>(d, a.D, blk16, static_cast<uint32_t>(grid), stream);
   launch_done(stream);
-  if (side) {  // join: the merge and everything after it wait for the two-tile launch
-    hipError_t e = hipEventRecord(side->join, side->s);
-    if (e == hipSuccess) e = hipStreamWaitEvent(stream, side->join, 0);
-    side_lock.unlock();
-    if (e != hipSuccess) return e;
+  if (d.rows_cap > kTileRows) {
+    launch_mark("decode_kernel_2t", stream);
+    if (a.dtype == PA_BF16) launch_decode<BF16, 2>(d, a.D, blk16, static_cast<uint32_t>(grid), stream);
+    else launch_decode<F16, 2>(d, a.D, blk16, static_cast<uint32_t>(grid), stream);
+    launch_done(stream);
   }
   if (d.P > 1 || f.cascade_on) {
     launch_mark("merge_kernel", stream);

@@ -58,10 +58,7 @@ hipError_t launch_attn_generic_rows(const AttnArgs& a, int32_t skip_rows_le, hip
 bool fast_path_supported(const AttnArgs& a);
 size_t fast_workspace_bytes(int32_t S, int32_t T, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_q,
                             int32_t max_seqlen);
-// side_stream_ok: the two-tile decode launch of a verify-like call may run on
-// the library's side stream (created on first use); false keeps every launch
-// on `stream`.
-hipError_t launch_attn_fast(const AttnArgs& a, hipStream_t stream, bool side_stream_ok);
+hipError_t launch_attn_fast(const AttnArgs& a, hipStream_t stream);
 // Plan trace (pa_set_trace): waits for `stream`, then prints the call's work
 // split and plan to stderr; the generic path prints its header line only.
 hipError_t trace_attn_fast(const AttnArgs& a, hipStream_t stream);
