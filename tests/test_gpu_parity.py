@@ -131,6 +131,36 @@ def test_sharing_invariance_bitexact():
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
+@pytest.mark.parametrize("n", [4, 5])
+def test_isolation_from_other_sequences_blocks_bitexact(n):
+    """Overwriting every cache block that the even-numbered sequences' tables
+    do not map (the odd sequences' blocks and the unused pool) leaves the
+    even sequences' outputs bit-identical ("vLLM Continuous Batching：从
+    Forward Shape 理解两个核心参数" §2.3补充: a sequence reads only through its
+    own block table), while the odd sequences' outputs change."""
+    w = config(n, scale_down=8)
+    print(f"[case] isolation cfg{n} {w.summary()}", flush=True)
+    g = GpuRun(w).run()
+    before = g.out.clone()
+    bt = w.step.block_tables
+    keep = sorted(set(int(b) for s in range(0, w.num_seqs, 2) for b in bt[s] if b >= 0))
+    mask = torch.ones(w.num_blocks, dtype=torch.bool)
+    mask[keep] = False
+    other = mask.nonzero().flatten().to("cuda")
+    gen = torch.Generator(device="cuda").manual_seed(n)
+    for cache in (g.k_cache, g.v_cache):
+        noise = torch.randn((len(other),) + tuple(cache.shape[1:]), generator=gen, device="cuda") * 3
+        cache[other] = noise.to(cache.dtype)
+    g.step()  # metadata, this step's K/V write, attention
+    torch.cuda.synchronize()
+    assert g.err() == 0
+    qsl = w.new_row_offsets()
+    even = torch.cat([torch.arange(int(qsl[s]), int(qsl[s + 1])) for s in range(0, w.num_seqs, 2)]).to("cuda")
+    odd = torch.cat([torch.arange(int(qsl[s]), int(qsl[s + 1])) for s in range(1, w.num_seqs, 2)]).to("cuda")
+    assert torch.equal(before[even].view(torch.int16), g.out[even].view(torch.int16))
+    assert not torch.equal(before[odd].view(torch.int16), g.out[odd].view(torch.int16))
+
+
 def test_deterministic():
     w = config(4, scale_down=8)
     g = GpuRun(w).run()
