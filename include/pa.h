@@ -212,8 +212,7 @@ pa_status_t pa_copy_blocks(const void* src_k, const void* src_v, void* dst_k, vo
  * Bytes of device workspace pa_attention needs for these sizes and hints
  * (split-K partial results, shared-prefix partial results and the call's
  * work plan).  Depends only on its arguments; pass the same max_query_len and
- * max_seq_len as to pa_attention.  0 when the call needs none (or the shape
- * takes the generic kernel).
+ * max_seq_len as to pa_attention.  0 when such a call needs none.
  */
 size_t pa_attention_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
                                    int32_t num_kv_heads, int32_t head_dim, int32_t max_query_len,
