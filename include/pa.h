@@ -21,8 +21,16 @@
  *     `stream` (a hipStream_t; NULL = default stream) and is complete when
  *     that stream is.  The caller owns the KV cache (the engine allocates
  *     one pool and hands out per-layer views, [VP] §3.6).
- *     The library creates no streams or events of its own and takes no locks
- *     around launches.
+ *   - One exception, in pa_attention only: on a large mixed batch (prefill
+ *     rows, head_dim 128, a block size that is a multiple of 16, at least 64
+ *     sequences and at most 64 new tokens per sequence on average) the
+ *     decode launches run on a side stream beside the prefill kernel, which
+ *     stays on `stream`.  That stream (non-blocking, default priority) and
+ *     its two events are created by the library on the first such call on a
+ *     device and kept until the process ends; the fork from and join back
+ *     into `stream` are event records and waits made under a process-wide
+ *     lock, so the call still completes with `stream`.
+ *     pa_attention_noalloc never uses it.
  *   - Host-checkable problems (null pointers, bad sizes, unsupported shapes,
  *     a too-small workspace, a failed launch) are returned synchronously as
  *     pa_status_t and nothing is enqueued.
@@ -286,6 +294,8 @@ pa_status_t pa_attention(const void* q, const void* k_cache, const void* v_cache
  *     needs to start at any value.  Calls that overlap on one device (on
  *     different streams, or from several threads, without ordering between
  *     them) race on it: the caller must order them.
+ *   - Every launch stays on `stream` (pa_attention may put a large mixed
+ *     batch's decode launches on the library's side stream).
  */
 #define PA_NOALLOC_SCRATCH_BYTES (64u << 20)
 pa_status_t pa_attention_noalloc(const void* q, const void* k_cache, const void* v_cache,

@@ -33,6 +33,7 @@
 // directly.
 #include <algorithm>
 #include <cstdio>
+#include <mutex>
 #include <vector>
 
 #include "mfma_common.h"
@@ -82,14 +83,21 @@ struct DecodeArgs {
 // Waves per SIMD the register budget is set for: the pair-buffered K/V
 // fragments and the O accumulators of head_dim 256 need about twice the
 // registers (and head_dim 256 items take one row tile only).
-template <int NT, int D>
+template <int NT, int D, bool kBeside>
 constexpr int decode_min_waves() {
-  return D == 256 ? 1 : (NT == 1 ? 3 : 2);
+  return kBeside || D == 256 ? 1 : (NT == 1 ? 3 : 2);
 }
 
-template <class F, int NT, int D, bool kBlk16>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(decode_min_waves<NT, D>(), 8))) void decode_kernel(
+// kBeside: the instance that runs beside the prefill kernel on a mixed batch
+// (launch_attn_fast): each of its waves holds more than half of a SIMD's
+// registers (168 VGPRs and AGPRs up to a100, 272 in all), so at most one of
+// them sits on a SIMD, next to one prefill wave (208 registers); the two
+// kernels then share every CU at a fixed split (one prefill workgroup and
+// four decode waves) instead of taking each other's slots as they free up.
+template <class F, int NT, int D, bool kBlk16, bool kBeside = false>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(decode_min_waves<NT, D, kBeside>(), 8))) void decode_kernel(
     DecodeArgs a) {
+  if constexpr (kBeside) __asm__ volatile("" ::: "a100");  // register footprint only; no instruction
   using M = Mma<F>;
   constexpr int kKK = D / 32;       // 16x16x32 K steps of QK; also V loads per 16-row chunk
   constexpr int kDT = D / 16;       // 16-wide output tiles of PV
@@ -632,9 +640,17 @@ size_t fast_workspace_bytes(int32_t S, int32_t T, int32_t Hq, int32_t Hkv, int32
   return fast_plan(S, T, Hq, Hkv, D, max_q, max_seqlen).bytes;
 }
 
-// One decode launch for the call's head_dim and block-size class.
+// One decode launch for the call's head_dim and block-size class.  beside:
+// the one-tile head_dim-128 instance that runs next to the prefill kernel.
 template <class F, int NT>
-static void launch_decode(const DecodeArgs& d, int32_t D, bool blk16, uint32_t grid, hipStream_t stream) {
+static void launch_decode(const DecodeArgs& d, int32_t D, bool blk16, uint32_t grid, hipStream_t stream,
+                          bool beside = false) {
+  if constexpr (NT == 1) {
+    if (beside) {
+      decode_kernel<F, 1, 128, true, true><<<grid, 64, 0, stream>>>(d);
+      return;
+    }
+  }
 #define PA_DECODE_D(DD)                                                          \
   if (blk16) decode_kernel<F, NT, DD, true><<<grid, 64, 0, stream>>>(d);        \
   else decode_kernel<F, NT, DD, false><<<grid, 64, 0, stream>>>(d);
@@ -655,7 +671,42 @@ static void launch_merge(const DecodeArgs& d, int32_t D, dim3 grid, hipStream_t 
   else merge_kernel<F, 128><<<grid, 256, 0, stream>>>(d);
 }
 
-hipError_t launch_attn_fast(const AttnArgs& a, hipStream_t stream) {
+// A side stream per device for the decode launches of a large mixed batch,
+// which run beside the prefill kernel (launch_attn_fast).  Created on first
+// use, default priority, never destroyed; the fork and join events are
+// recorded and waited on under one lock, so concurrent calls cannot
+// interleave them.
+namespace {
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  bool ok = false, tried = false;
+};
+constexpr int kMaxDevices = 64;
+SideStream g_side[kMaxDevices];
+std::mutex g_side_mu;
+
+SideStream* side_stream_locked() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  SideStream& ss = g_side[dev];
+  if (!ss.tried) {
+    ss.tried = true;
+    ss.ok = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) == hipSuccess &&
+            hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) == hipSuccess &&
+            hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) == hipSuccess;
+  }
+  return ss.ok ? &ss : nullptr;
+}
+}  // namespace
+
+bool decode_beside_prefill(const AttnArgs& a) {
+  const FastPlan f = fast_plan(a.S, a.T, a.Hq, a.Hkv, a.D, a.max_qlen, a.max_seqlen);
+  return f.prefill_on && a.D == kD && a.bs % kChunk == 0 && a.S >= kBesideMinSeqs &&
+         static_cast<int64_t>(a.T) <= static_cast<int64_t>(kBesideMaxMeanQuery) * a.S;
+}
+
+hipError_t launch_attn_fast(const AttnArgs& a, hipStream_t stream, bool side_stream_ok) {
   const FastPlan f = fast_plan(a.S, a.T, a.Hq, a.Hkv, a.D, a.max_qlen, a.max_seqlen);
   DecodeArgs d;
   d.q = static_cast<const uint16_t*>(a.q);
@@ -693,15 +744,42 @@ hipError_t launch_attn_fast(const AttnArgs& a, hipStream_t stream) {
   if (grid > INT32_MAX) return hipErrorInvalidValue;
   d.n_items = static_cast<int32_t>(items);
 
-  // plan (work list, cascade groups), then prefill query tiles and cascade
-  // prefix parts on the MFMA prefill kernel
+  // A large mixed batch (many decode sequences next to a few prefill
+  // chunks) runs its decode launches on a side stream beside the prefill
+  // kernel: the prefill kernel takes one workgroup per CU (its launch asks
+  // for kBesideLdsPad more bytes of LDS) and the decode kernel one wave per
+  // SIMD (its kBeside instance), so the HBM-bound decode and the MFMA-bound
+  // prefill share every CU (mixed batch: 0.715 -> 0.68 ms per step; the same
+  // two launches side by side without the split: 0.721 ms, the decode waves
+  // taking every slot a prefill workgroup frees).  Other calls run their
+  // launches one after the other on `stream`.
+  const bool beside = side_stream_ok && decode_beside_prefill(a);
+  std::unique_lock<std::mutex> side_lock(g_side_mu, std::defer_lock);
+  SideStream* side = nullptr;
+  hipStream_t ds = stream;  // the decode launches' stream
   if (f.mfma_prefill) {
     int32_t* plan = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(a.workspace) + f.plan_off);
     hipError_t e = launch_attn_plan(a, f.rows_cap, f.P, f.prefill_on, f.cascade_on, plan, stream);
     if (e != hipSuccess) return e;
+    if (beside) {  // the decode launches wait for the plan only
+      side_lock.lock();
+      side = side_stream_locked();
+      if (side && hipEventRecord(side->fork, stream) == hipSuccess &&
+          hipStreamWaitEvent(side->s, side->fork, 0) == hipSuccess)
+        ds = side->s;
+      else
+        side = nullptr;
+    }
     e = launch_attn_prefill(a, f.rows_cap, f.P, f.prefill_on, f.cascade_on, plan,
-                            reinterpret_cast<float*>(static_cast<uint8_t*>(a.workspace) + f.pre_off), stream);
-    if (e != hipSuccess) return e;
+                            reinterpret_cast<float*>(static_cast<uint8_t*>(a.workspace) + f.pre_off),
+                            side ? kBesideLdsPad : 0, stream);
+    if (e != hipSuccess) {
+      if (side) {  // rejoin, so `stream` still orders after the side stream
+        (void)hipEventRecord(side->join, side->s);
+        (void)hipStreamWaitEvent(stream, side->join, 0);
+      }
+      return e;
+    }
     const PlanLayout l = plan_layout(a.S, a.T, f.G, f.P, f.prefill_on, f.cascade_on);
     if (f.cascade_on) d.seq_prefix = reinterpret_cast<const int4*>(reinterpret_cast<const uint8_t*>(plan) + l.seqpre_off);
     const int2* dec = reinterpret_cast<const int2*>(reinterpret_cast<const uint8_t*>(plan) + l.dec_off);
@@ -709,21 +787,27 @@ hipError_t launch_attn_fast(const AttnArgs& a, hipStream_t stream) {
     d.dec_list[1] = dec + l.cap_dec;
     d.dec_n = plan + 2;
   }
-  // Both decode instances on `stream`, one after the other.  Running the
+  // The one-tile and two-tile instances one after the other.  Running the
   // two-tile launch on a second stream beside the one-tile launch (both
   // HBM-bound, each filling the machine only partly) measured slower once the
   // plan's sorted work lists were in place: verify batch 0.459 ms side by
   // side, 0.437 ms one after the other (either order).
   const bool blk16 = a.bs % kChunk == 0;
-  launch_mark("decode_kernel", stream);
-  if (a.dtype == PA_BF16) launch_decode<BF16, 1>(d, a.D, blk16, static_cast<uint32_t>(grid), stream);
-  else launch_decode<F16, 1>(d, a.D, blk16, static_cast<uint32_t>(grid), stream);
-  launch_done(stream);
+  launch_mark("decode_kernel", ds);
+  if (a.dtype == PA_BF16) launch_decode<BF16, 1>(d, a.D, blk16, static_cast<uint32_t>(grid), ds, side != nullptr);
+  else launch_decode<F16, 1>(d, a.D, blk16, static_cast<uint32_t>(grid), ds, side != nullptr);
+  launch_done(ds);
   if (d.rows_cap > kTileRows) {
-    launch_mark("decode_kernel_2t", stream);
-    if (a.dtype == PA_BF16) launch_decode<BF16, 2>(d, a.D, blk16, static_cast<uint32_t>(grid), stream);
-    else launch_decode<F16, 2>(d, a.D, blk16, static_cast<uint32_t>(grid), stream);
-    launch_done(stream);
+    launch_mark("decode_kernel_2t", ds);
+    if (a.dtype == PA_BF16) launch_decode<BF16, 2>(d, a.D, blk16, static_cast<uint32_t>(grid), ds);
+    else launch_decode<F16, 2>(d, a.D, blk16, static_cast<uint32_t>(grid), ds);
+    launch_done(ds);
+  }
+  if (side) {  // join: the merge and everything after it wait for the decode launches
+    hipError_t e = hipEventRecord(side->join, side->s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(stream, side->join, 0);
+    side_lock.unlock();
+    if (e != hipSuccess) return e;
   }
   if (d.P > 1 || f.cascade_on) {
     launch_mark("merge_kernel", stream);
@@ -759,8 +843,9 @@ hipError_t trace_attn_fast(const AttnArgs& a, hipStream_t stream) {
   trace_header(a, "fast");
   std::fprintf(stderr,
                "[pa_trace]   split: G=%d decode_parts<=%d rows_per_decode_item<=%d "
-               "prefill_rows=%d shared_prefix=%d workspace_bytes=%zu\n",
-               f.G, f.P, f.rows_cap, f.prefill_on ? 1 : 0, f.cascade_on ? 1 : 0, f.bytes);
+               "prefill_rows=%d shared_prefix=%d decode_beside_prefill=%d workspace_bytes=%zu\n",
+               f.G, f.P, f.rows_cap, f.prefill_on ? 1 : 0, f.cascade_on ? 1 : 0, decode_beside_prefill(a) ? 1 : 0,
+               f.bytes);
   hipError_t e = hipStreamSynchronize(stream);
   if (e != hipSuccess) return e;
   if (!f.mfma_prefill) {

@@ -995,7 +995,7 @@ hipError_t launch_attn_plan(const AttnArgs& a, int32_t rows_cap, int32_t P, bool
 }
 
 hipError_t launch_attn_prefill(const AttnArgs& a, int32_t rows_cap, int32_t P, bool prefill_on, bool cascade_on,
-                               const int32_t* plan, float* ws_pre, hipStream_t stream) {
+                               const int32_t* plan, float* ws_pre, size_t lds_pad, hipStream_t stream) {
   PrefillArgs p;
   p.q = static_cast<const uint16_t*>(a.q);
   p.k_cache = static_cast<const uint16_t*>(a.k_cache);
@@ -1030,11 +1030,11 @@ hipError_t launch_attn_prefill(const AttnArgs& a, int32_t rows_cap, int32_t P, b
   const bool blk16 = a.bs % 16 == 0;
 #define PA_PREFILL_D(DD)                                                                             \
   if (blk16) {                                                                                       \
-    if (a.dtype == PA_BF16) prefill_kernel<BF16, true, DD><<<grid, kThreads, 0, stream>>>(p);        \
-    else prefill_kernel<F16, true, DD><<<grid, kThreads, 0, stream>>>(p);                            \
+    if (a.dtype == PA_BF16) prefill_kernel<BF16, true, DD><<<grid, kThreads, lds_pad, stream>>>(p);        \
+    else prefill_kernel<F16, true, DD><<<grid, kThreads, lds_pad, stream>>>(p);                            \
   } else {                                                                                           \
-    if (a.dtype == PA_BF16) prefill_kernel<BF16, false, DD><<<grid, kThreads, 0, stream>>>(p);       \
-    else prefill_kernel<F16, false, DD><<<grid, kThreads, 0, stream>>>(p);                           \
+    if (a.dtype == PA_BF16) prefill_kernel<BF16, false, DD><<<grid, kThreads, lds_pad, stream>>>(p);       \
+    else prefill_kernel<F16, false, DD><<<grid, kThreads, lds_pad, stream>>>(p);                           \
   }
   if (a.D == 64) {
     PA_PREFILL_D(64)

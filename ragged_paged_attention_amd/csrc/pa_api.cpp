@@ -84,7 +84,7 @@ pa_status_t attention_entry(AttnArgs a, const ScratchSource* scratch, hipStream_
   } else {
     if (!fast_ok) return PA_ERR_UNSUPPORTED;
     if (need > 0 && (!a.workspace || a.workspace_bytes < need)) return PA_ERR_WORKSPACE;
-    e = launch_attn_fast(a, stream);
+    e = launch_attn_fast(a, stream, /*side_stream_ok=*/scratch == nullptr);
     if (e == hipSuccess && !scratch && g_trace.load()) e = trace_attn_fast(a, stream);
     return hip_status(e, "pa_attention");
   }

@@ -58,7 +58,18 @@ hipError_t launch_attn_generic_rows(const AttnArgs& a, int32_t skip_rows_le, hip
 bool fast_path_supported(const AttnArgs& a);
 size_t fast_workspace_bytes(int32_t S, int32_t T, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_q,
                             int32_t max_seqlen);
-hipError_t launch_attn_fast(const AttnArgs& a, hipStream_t stream);
+// side_stream_ok: a large mixed batch may run its decode launches on the
+// library's side stream beside the prefill kernel (decode_beside_prefill);
+// false keeps every launch on `stream`.
+hipError_t launch_attn_fast(const AttnArgs& a, hipStream_t stream, bool side_stream_ok);
+// A call whose decode launches run beside the prefill kernel (given a side
+// stream): prefill rows, head_dim 128, a block size that is a multiple of 16,
+// at least kBesideMinSeqs sequences and at most kBesideMaxMeanQuery new
+// tokens per sequence on average (many decodes next to a few chunks).
+bool decode_beside_prefill(const AttnArgs& a);
+constexpr int kBesideMinSeqs = 64;
+constexpr int kBesideMaxMeanQuery = 64;
+constexpr size_t kBesideLdsPad = 20 << 10;  // prefill launch's extra LDS: 84 KB per workgroup, one per CU
 // Plan trace (pa_set_trace): waits for `stream`, then prints the call's work
 // split and plan to stderr; the generic path prints its header line only.
 hipError_t trace_attn_fast(const AttnArgs& a, hipStream_t stream);
@@ -132,7 +143,9 @@ bool cascade_possible(int32_t S, int32_t max_seqlen);
 hipError_t launch_attn_plan(const AttnArgs& a, int32_t rows_cap, int32_t P, bool prefill_on, bool cascade_on,
                             int32_t* plan, hipStream_t stream);
 // Prefill query tiles and cascade prefix parts (their partials go to ws_pre).
+// lds_pad: extra dynamic LDS per workgroup (unused by the kernel; it caps
+// the workgroups per CU).
 hipError_t launch_attn_prefill(const AttnArgs& a, int32_t rows_cap, int32_t P, bool prefill_on, bool cascade_on,
-                               const int32_t* plan, float* ws_pre, hipStream_t stream);
+                               const int32_t* plan, float* ws_pre, size_t lds_pad, hipStream_t stream);
 
 }  // namespace pa

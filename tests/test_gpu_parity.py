@@ -5,6 +5,9 @@ max-abs-error 1e-5 for fp32 inputs and 2e-2 for bf16/f16 inputs (fp32
 accumulation), on the same seeded inputs.  Unwritten pool slots hold NaN, so
 any read outside a sequence's visible rows shows up as NaN.
 """
+import os
+import tempfile
+
 import numpy as np
 import pytest
 import torch
@@ -159,6 +162,43 @@ def test_isolation_from_other_sequences_blocks_bitexact(n):
     odd = torch.cat([torch.arange(int(qsl[s]), int(qsl[s + 1])) for s in range(1, w.num_seqs, 2)]).to("cuda")
     assert torch.equal(before[even].view(torch.int16), g.out[even].view(torch.int16))
     assert not torch.equal(before[odd].view(torch.int16), g.out[odd].view(torch.int16))
+
+
+def test_mixed_batch_decode_beside_prefill():
+    """A large mixed batch (128 sequences, 4096 tokens) runs its decode
+    launches beside the prefill kernel on the library's side stream; every
+    decode row and the last rows of every chunk match the oracle, and two
+    calls give the same bits."""
+    w = config(4, scale_down=2)
+    print(f"[case] beside {w.summary()}", flush=True)
+    prev = rpa.pa_set_trace(1)
+    try:
+        with tempfile.TemporaryFile(mode="w+b") as tmp:
+            saved = os.dup(2)
+            try:
+                os.dup2(tmp.fileno(), 2)
+                g = GpuRun(w).run()
+            finally:
+                os.dup2(saved, 2)
+                os.close(saved)
+            tmp.seek(0)
+            text = tmp.read().decode()
+    finally:
+        rpa.pa_set_trace(prev)
+    assert "decode_beside_prefill=1" in text
+    assert g.err() == 0
+    ql = w.step.query_lens
+    offs = w.new_row_offsets()
+    rows = [int(offs[s]) for s in range(w.num_seqs) if ql[s] == 1]
+    rows += [int(offs[s + 1]) - 1 for s in range(w.num_seqs) if ql[s] > 1]
+    _, _, _, ref = oracle.run_step(w, rows=rows)
+    err = max_abs_err(g.out[torch.tensor(rows, device="cuda")], ref)
+    print(f"[beside] rows {len(rows)} max_abs_err={err:.3e}", flush=True)
+    assert err <= tol_for(w.dtype)
+    first = g.out.clone()
+    g.step()
+    torch.cuda.synchronize()
+    assert torch.equal(first.view(torch.int16), g.out.view(torch.int16))
 
 
 def test_deterministic():
