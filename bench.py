@@ -79,6 +79,7 @@ def parse():
                     help="write profiles/KERNEL.WORKLOAD.mfma.pmc.md from one rocprofv3 --pmc --kernel-trace run "
                          "with the MFMA counters; no GPU needed")
     ap.add_argument("--command", default="", help="the command that produced the rocprofv3 output (recorded)")
+    ap.add_argument("--note", default="", help="a paragraph added to a counter summary (how to read it)")
     return ap.parse_args()
 
 
@@ -110,17 +111,21 @@ class Timer:
 
     def time_cold(self, fn, iters=50, flush_bytes=1 << 30):
         """Median (and 10th / 90th percentile) over `iters` single calls, each
-        preceded by a write of `flush_bytes` to a separate buffer (four times
+        preceded by a read of `flush_bytes` of a separate buffer (four times
         the 256 MB Infinity Cache, so the call starts with cold caches), each
-        call bracketed by its own pair of events on the current stream."""
+        call bracketed by its own pair of events on the current stream.  The
+        flush reads rather than writes: after a write, the caches hold dirty
+        lines of the flush buffer whose write-back would land in the timed
+        call."""
         torch = self.torch
         if getattr(self, "_flush", None) is None or self._flush.numel() != flush_bytes // 4:
-            self._flush = torch.empty(flush_bytes // 4, dtype=torch.int32, device="cuda")
+            self._flush = torch.ones(flush_bytes // 4, dtype=torch.int32, device="cuda")
+            self._flush_sum = torch.empty((), dtype=torch.int64, device="cuda")
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
         fn()
         torch.cuda.synchronize()
         for i in range(iters):
-            self._flush.fill_(i)
+            torch.sum(self._flush, dim=0, dtype=torch.int64, out=self._flush_sum)
             ev[i][0].record()
             fn()
             ev[i][1].record()
@@ -341,7 +346,7 @@ def _workload_flops(kernel, workload):
     return work_split(w)[kernel]
 
 
-def summarize_mfma(pmc_dir, kernel, workload, command):
+def summarize_mfma(pmc_dir, kernel, workload, command, note=""):
     """MFMA counters of one kernel, per dispatch, and what they say:
       - MFMA busy fraction = SQ_VALU_MFMA_BUSY_CYCLES / (active cycles per XCD
         x 1024 SIMDs): GRBM_GUI_ACTIVE adds up the 8 XCDs, so the active cycles
@@ -376,8 +381,10 @@ def summarize_mfma(pmc_dir, kernel, workload, command):
              f"Per dispatch, averaged over {n_disp} dispatches of `{match}`.  GRBM_GUI_ACTIVE adds up the",
              "8 XCDs; one XCD's active cycles (GRBM_GUI_ACTIVE / 8) are the kernel's span in shader-clock",
              "cycles.  MFMA busy fraction = SQ_VALU_MFMA_BUSY_CYCLES / (those cycles x 1024 SIMDs).",
-             "SQ_INSTS_VALU_MFMA_MOPS_BF16 counts bf16 MFMA work in units of 512 FLOPs.", "",
-             "| counter | per dispatch |", "|---|---|"]
+             "SQ_INSTS_VALU_MFMA_MOPS_BF16 counts bf16 MFMA work in units of 512 FLOPs.", ""]
+    if note:
+        lines += [note, ""]
+    lines += ["| counter | per dispatch |", "|---|---|"]
     lines += [f"| {c} | {v:.4e} |" for c, v in sorted(avg.items())]
     lines += ["", "| derived | value |", "|---|---|"]
     if dur_us:
@@ -427,7 +434,7 @@ def main():
         summarize_pmc(*args.summarize_pmc, args.command)
         return
     if args.summarize_mfma:
-        summarize_mfma(*args.summarize_mfma, args.command)
+        summarize_mfma(*args.summarize_mfma, args.command, args.note)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (--gpus {args.gpus} was asked for): the library has no multi-GPU "
@@ -513,6 +520,10 @@ def main():
         if concurrent:
             result["roofline"]["concurrent_with"] = other
             result["roofline_other_kernel"]["concurrent_with"] = dominant
+            for r in (result["roofline"], result["roofline_other_kernel"]):
+                if r.get("mfma_busy"):
+                    # counter collection runs dispatches one at a time
+                    r["mfma_busy"]["measured_alone"] = True
         if not args.no_cpu_baseline:
             result["cpu_baseline"] = cpu_baseline(config(4, poison=False), args.cpu_sample_rows)
         del g, ws, out
