@@ -6,6 +6,9 @@ attention.  Nothing here computes any part of the method.
 """
 from __future__ import annotations
 
+import os
+import tempfile
+
 import numpy as np
 import torch
 
@@ -69,3 +72,35 @@ def tol_for(dtype: str) -> float:
 def max_abs_err(gpu_out, ref: np.ndarray) -> float:
     g = gpu_out.detach().to(torch.float64).cpu().numpy()
     return float(np.max(np.abs(g - ref))) if ref.size else 0.0
+
+
+def capture_stderr(fn):
+    """Runs fn() (then waits for the GPU) with file descriptor 2 sent to a
+    temporary file; returns fn's result and what was written there (the
+    library's trace goes to stderr)."""
+    with tempfile.TemporaryFile(mode="w+b") as tmp:
+        saved = os.dup(2)
+        try:
+            os.dup2(tmp.fileno(), 2)
+            res = fn()
+            torch.cuda.synchronize()
+        finally:
+            os.dup2(saved, 2)
+            os.close(saved)
+        tmp.seek(0)
+        return res, tmp.read().decode()
+
+
+def one_stream_output(g, workspace_bytes):
+    """The same call as g's last step through pa_attention_noalloc, which
+    keeps every launch on the caller's stream (no side stream); returns its
+    output."""
+    w, db = g.w, g.db
+    assert 0 < workspace_bytes <= rpa.PA_NOALLOC_SCRATCH_BYTES
+    out = torch.full_like(db.q, float("nan"))
+    d_err = torch.zeros(1, dtype=torch.int32, device=db.q.device)
+    rpa.pa_attention_noalloc(db.q, g.k_cache, g.v_cache, db.block_tables, g.meta["query_start_loc"], db.seq_lens,
+                             max(1, w.max_query_len), max(1, w.max_seq_len), w.scale, out=out, d_err=d_err)
+    torch.cuda.synchronize()
+    assert int(d_err.item()) == 0
+    return out

@@ -9,9 +9,7 @@ sit in the batch, reads each such prefix once for the whole group, and merges
 it with every member's own suffix.  The results must be those of
 plain per-sequence attention (the oracle), whatever the grouping.
 """
-import os
 import re
-import tempfile
 
 import numpy as np
 import pytest
@@ -19,7 +17,7 @@ import torch
 
 import oracle
 import ragged_paged_attention_amd as rpa
-from tests.gpu_path import GpuRun, max_abs_err, tol_for
+from tests.gpu_path import GpuRun, capture_stderr, max_abs_err, one_stream_output, tol_for
 from workloads import config, permute_sequences, unshare, verify_batch
 from workloads.generators import build_workload
 
@@ -168,22 +166,6 @@ def test_grouping_does_not_depend_on_batch_order(scale_down):
     assert max_abs_err(b[torch.tensor(rows, device="cuda")], ref) <= tol_for(w.dtype)
 
 
-def _capture_fd2(fn):
-    """Runs fn() with file descriptor 2 sent to a temporary file; returns
-    fn's result and what was written there."""
-    with tempfile.TemporaryFile(mode="w+b") as tmp:
-        saved = os.dup(2)
-        try:
-            os.dup2(tmp.fileno(), 2)
-            res = fn()
-            torch.cuda.synchronize()
-        finally:
-            os.dup2(saved, 2)
-            os.close(saved)
-        tmp.seek(0)
-        return res, tmp.read().decode()
-
-
 def test_trace_lists_the_groups():
     """With the plan trace on, the call prints its plan: the three groups of
     the three_groups batch with their members and prefix tokens (2048; 1040
@@ -193,7 +175,7 @@ def test_trace_lists_the_groups():
     w = grouped_batch(len("three_groups"), c["segs"], c["Hq"], c["Hkv"])
     prev = rpa.pa_set_trace(1)
     try:
-        g, text = _capture_fd2(lambda: GpuRun(w).run())
+        g, text = capture_stderr(lambda: GpuRun(w).run())
     finally:
         rpa.pa_set_trace(prev)
     print(text, flush=True)
@@ -208,3 +190,32 @@ def test_trace_lists_the_groups():
     assert "d_err=0x0" in text
     _, _, _, ref = oracle.run_step(w)
     assert max_abs_err(g.out, ref) <= tol_for(w.dtype)
+
+
+def test_groups_beside_prefill_chunks():
+    """Shared prefixes in a large mixed batch: 66 decodes in three groups
+    next to four prefill chunks run with the decode launches beside the
+    prefill kernel (which also takes the groups' prefix parts).  The groups
+    form as on their own, the output equals the one-stream path bit for bit
+    and matches the oracle on every row."""
+    segs = [("group", 22, 2048, 1, 200), ("single", 96, 1500), ("group", 22, 1024, 1, 300),
+            ("single", 160, 2200), ("group", 22, 1536, 1, 300), ("single", 128, 900), ("single", 112, 2000)]
+    w = grouped_batch(31, segs, 32, 8)
+    print(f"[case] groups beside chunks: {w.summary()}", flush=True)
+    need = rpa.pa_attention_workspace_size(w.num_seqs, w.num_tokens, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                                           w.max_query_len, w.max_seq_len)
+    prev = rpa.pa_set_trace(1)
+    try:
+        g, text = capture_stderr(lambda: GpuRun(w).run())
+    finally:
+        rpa.pa_set_trace(prev)
+    assert "decode_beside_prefill=1" in text and "shared_prefix=1" in text
+    sizes = sorted(int(m.group(1)) for m in re.finditer(r"group \d+: prefix_tokens=(\d+)", text))
+    assert sizes == [1024, 1536, 2048]
+    assert g.err() == 0
+    serial = one_stream_output(g, need)
+    assert torch.equal(g.out.view(torch.int16), serial.view(torch.int16))
+    _, _, _, ref = oracle.run_step(w)
+    err = max_abs_err(g.out, ref)
+    print(f"[groups beside chunks] max_abs_err={err:.3e}", flush=True)
+    assert err <= tol_for(w.dtype)

@@ -5,8 +5,6 @@ max-abs-error 1e-5 for fp32 inputs and 2e-2 for bf16/f16 inputs (fp32
 accumulation), on the same seeded inputs.  Unwritten pool slots hold NaN, so
 any read outside a sequence's visible rows shows up as NaN.
 """
-import os
-import tempfile
 
 import numpy as np
 import pytest
@@ -17,7 +15,7 @@ import ragged_paged_attention_amd as rpa
 from workloads import config, random_batch, relabel_blocks, unshare
 from workloads.device import to_numpy_bits
 
-from tests.gpu_path import GpuRun, max_abs_err, tol_for
+from tests.gpu_path import GpuRun, capture_stderr, max_abs_err, one_stream_output, tol_for
 
 pytestmark = pytest.mark.gpu
 
@@ -173,16 +171,7 @@ def test_mixed_batch_decode_beside_prefill():
     print(f"[case] beside {w.summary()}", flush=True)
     prev = rpa.pa_set_trace(1)
     try:
-        with tempfile.TemporaryFile(mode="w+b") as tmp:
-            saved = os.dup(2)
-            try:
-                os.dup2(tmp.fileno(), 2)
-                g = GpuRun(w).run()
-            finally:
-                os.dup2(saved, 2)
-                os.close(saved)
-            tmp.seek(0)
-            text = tmp.read().decode()
+        g, text = capture_stderr(lambda: GpuRun(w).run())
     finally:
         rpa.pa_set_trace(prev)
     assert "decode_beside_prefill=1" in text
@@ -199,6 +188,33 @@ def test_mixed_batch_decode_beside_prefill():
     g.step()
     torch.cuda.synchronize()
     assert torch.equal(first.view(torch.int16), g.out.view(torch.int16))
+
+
+@pytest.mark.parametrize("dtype,bs", [("bf16", 16), ("f16", 16), ("bf16", 32)])
+def test_mixed_batch_beside_equals_one_stream(dtype, bs):
+    """The CU split changes where the kernels run, not what they compute: a
+    mixed batch of 64 sequences (60 decodes beside 4 chunks) through
+    pa_attention (decode launches on the side stream, prefill at one
+    workgroup per CU) gives the same bits as through pa_attention_noalloc
+    (every launch on the caller's stream, prefill at two workgroups per CU),
+    on every row; all rows match the oracle."""
+    w = config(4, scale_down=4, dtype=dtype, block_size=bs)
+    print(f"[case] beside vs one stream {dtype} bs {bs}: {w.summary()}", flush=True)
+    need = rpa.pa_attention_workspace_size(w.num_seqs, w.num_tokens, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                                           w.max_query_len, w.max_seq_len)
+    prev = rpa.pa_set_trace(1)
+    try:
+        g, text = capture_stderr(lambda: GpuRun(w).run())
+    finally:
+        rpa.pa_set_trace(prev)
+    assert "decode_beside_prefill=1" in text
+    assert g.err() == 0
+    serial = one_stream_output(g, need)
+    assert torch.equal(g.out.view(torch.int16), serial.view(torch.int16))
+    _, _, _, ref = oracle.run_step(w)
+    err = max_abs_err(g.out, ref)
+    print(f"[beside] {dtype} bs {bs}: max_abs_err={err:.3e}", flush=True)
+    assert err <= tol_for(w.dtype)
 
 
 def test_deterministic():

@@ -286,11 +286,12 @@ CONFIG_NAMES = {
 
 
 def config(n: int, seed: Optional[int] = None, dtype: Optional[str] = None, poison: bool = True,
-           scale_down: int = 1) -> Workload:
+           scale_down: int = 1, block_size: Optional[int] = None) -> Workload:
     """The five workloads (1-based).  `seed` defaults to the config number.
 
     `scale_down` > 1 shrinks lengths and counts of configs 2-5 (same structure,
     same head shapes) so the oracle finishes in seconds; 1 is the full size.
+    `block_size` replaces config 4's 16 (the pool keeps its token capacity).
     """
     seed = n if seed is None else seed
     rng = np.random.default_rng(seed)
@@ -323,7 +324,8 @@ def config(n: int, seed: Optional[int] = None, dtype: Optional[str] = None, pois
         return build_workload("decode", dtype or "bf16", 32, 32, 128, bs, NB, [1] * S, sl, tables,
                               seed, rng, poison=poison)
     if n == 4:
-        bs, NB = 16, 40000
+        bs = block_size or 16
+        NB = 40000 * 16 // bs
         n_dec, n_chunk, budget = 240, 16, 8192
         lo, hi, ctx_hi = 128, 8192, 4096
         if f > 1:
