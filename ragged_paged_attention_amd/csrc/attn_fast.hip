@@ -49,6 +49,7 @@ constexpr int kMaxRows = 32;        // query rows of one decode item (two tiles)
 // Compile-time tuning of the decode work order (measured on MI355X); the
 // part split (kPartChunks, plan_parts) is in pa_internal.h.
 constexpr int kXcdRun = 16;         // consecutive decode items kept on one XCD
+constexpr int kSimds = 1024;        // 256 CUs x 4 SIMDs
 constexpr int kGroupHeadsBelow = 16;  // item order: head-grouped when Hkv < this
 
 struct DecodeArgs {
@@ -65,7 +66,8 @@ struct DecodeArgs {
   int32_t prefill_on;  // the prefill kernel runs in this call
   int32_t max_q;       // the caller's max_query_len hint
   // Decode work lists of the plan (one-tile, two-tile items; null without a
-  // plan): entries (sequence, part), heaviest first; counts in dec_n[0..1].
+  // plan): entries (sequence, part), heaviest first; counts in dec_n[0..1],
+  // chunks per part of each list in dec_n[2..3].
   const int2* dec_list[2];
   const int32_t* dec_n;
   float scale_log2e;
@@ -224,7 +226,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(decode_min_w
   const int32_t nchunks = ceil_div(L, kChunk);
   const int32_t cbeg = pre / kChunk;
   int32_t np, cpp;
-  plan_parts(nchunks - cbeg, a.P, &np, &cpp);
+  plan_parts(nchunks - cbeg, a.P, &np, &cpp, a.dec_list[0] ? a.dec_n[2 + NT - 1] : kPartChunks);
   if (part >= np) return;
   const int32_t c0 = cbeg + part * cpp;
   const int32_t c1 = min(nchunks, c0 + cpp);
@@ -490,7 +492,8 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
     prow = sp.w;
   }
   int32_t np, cpp;
-  plan_parts(ceil_div(L, kChunk) - pre / kChunk, a.P, &np, &cpp);
+  plan_parts(ceil_div(L, kChunk) - pre / kChunk, a.P, &np, &cpp,
+             a.dec_list[0] ? a.dec_n[2 + (rows > kTileRows ? 1 : 0)] : kPartChunks);
   if (np == 1 && npp == 0) return;  // written directly by the decode kernel
   const int32_t ntot = np + npp;
   const int32_t stride = a.rows_cap * kPF;  // one decode part's partials
@@ -759,7 +762,10 @@ hipError_t launch_attn_fast(const AttnArgs& a, hipStream_t stream, bool side_str
   hipStream_t ds = stream;  // the decode launches' stream
   if (f.mfma_prefill) {
     int32_t* plan = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(a.workspace) + f.plan_off);
-    hipError_t e = launch_attn_plan(a, f.rows_cap, f.P, f.prefill_on, f.cascade_on, plan, stream);
+    // list entries one wave of each decode launch holds: waves per SIMD x
+    // 1024 SIMDs, one wave per KV head of an entry
+    const int32_t dec_slots[2] = {kSimds * (beside || a.D == 256 ? 1 : 3) / a.Hkv, kSimds * 2 / a.Hkv};
+    hipError_t e = launch_attn_plan(a, f.rows_cap, f.P, f.prefill_on, f.cascade_on, dec_slots, plan, stream);
     if (e != hipSuccess) return e;
     if (beside) {  // the decode launches wait for the plan only
       side_lock.lock();
@@ -865,9 +871,10 @@ hipError_t trace_attn_fast(const AttnArgs& a, hipStream_t stream) {
   for (int32_t i = 0; i < n_entries; ++i) (entries[i].x >= 0 ? n_tiles : n_parts)++;
   std::fprintf(stderr,
                "[pa_trace]   plan: %d prefill-kernel entries (%d query tiles, %d shared-prefix parts), %d "
-               "shared-prefix groups, decode items %lld one-tile, %lld two-tile\n",
+               "shared-prefix groups, decode items %lld one-tile, %lld two-tile (parts of at most %d, %d "
+               "tokens)\n",
                n_entries, n_tiles, n_parts, n_groups, static_cast<long long>(n_dec[0]),
-               static_cast<long long>(n_dec[1]));
+               static_cast<long long>(n_dec[1]), hdr[4] * kChunk, hdr[5] * kChunk);
   const int4* groups = reinterpret_cast<const int4*>(h.data() + l.groups_off);
   const int32_t* members = reinterpret_cast<const int32_t*>(h.data() + l.members_off);
   for (int32_t g = 0; g < n_groups; ++g) {

@@ -89,7 +89,9 @@ pa_status_t attention_entry(AttnArgs a, const ScratchSource* scratch, hipStream_
 // planning kernel (attn_prefill.hip) and read by the prefill, decode and merge
 // kernels:
 //   int32 header[kPlanHeader]   [0] list entries, [1] cascade groups,
-//                               [2], [3] one-tile / two-tile decode entries
+//                               [2], [3] one-tile / two-tile decode entries,
+//                               [4], [5] chunks per decode part of the
+//                               one-tile / two-tile list (plan_parts)
 //   int2  entries[cap_entries]  (s >= 0, q-tile): a prefill query tile;
 //                               (-(group + 1), part): a part of a cascade
 //                               group's shared prefix
@@ -107,15 +109,17 @@ pa_status_t attention_entry(AttnArgs a, const ScratchSource* scratch, hipStream_
 // Prefix partials live in their own workspace region: kCascadeEntries slots
 // (one per prefix part) x KV heads x kCascadeRows rows x kPartFloats floats.
 // Split-K decode: a context of `nchunks` 16-token chunks is cut into parts of
-// about kPartChunks chunks, at most P parts (P from max_seq_len, at most
-// kMaxParts), none empty.  Equal-sized parts keep the tail of the launch short
-// however uneven the context lengths are.  The plan and the decode kernels
-// call the same function, so their part ranges agree.
+// about part_chunks chunks (kPartChunks, or twice that for a planned list
+// that would otherwise need between one and two waves of the launch's wave
+// slots), at most P parts (P from max_seq_len, at most kMaxParts), none
+// empty.  Equal-sized parts keep the tail of the launch short however uneven
+// the context lengths are.  The plan, the decode kernels and the merge call
+// the same function with the same part_chunks, so their part ranges agree.
 constexpr int kPartChunks = 48;  // a context part is at most 48 chunks = 768 tokens
 constexpr int kMaxParts = 64;    // parts per sequence (longer parts past 48k tokens)
-__host__ __device__ __forceinline__ void plan_parts(int32_t nchunks, int32_t P, int32_t* nparts,
-                                                    int32_t* cpp) {
-  int32_t np = (nchunks + kPartChunks - 1) / kPartChunks;
+__host__ __device__ __forceinline__ void plan_parts(int32_t nchunks, int32_t P, int32_t* nparts, int32_t* cpp,
+                                                    int32_t part_chunks = kPartChunks) {
+  int32_t np = (nchunks + part_chunks - 1) / part_chunks;
   if (np > P) np = P;
   if (np < 1) np = 1;
   int32_t c = (nchunks + np - 1) / np;
@@ -140,8 +144,11 @@ PlanLayout plan_layout(int32_t S, int32_t T, int32_t G, int32_t P, bool prefill_
 // Shared-prefix (cascade) decode may run in this call: long enough contexts,
 // a batch small enough for the detection.
 bool cascade_possible(int32_t S, int32_t max_seqlen);
+// dec_slots: list entries (each one wave per KV head) that one wave of the
+// one-tile and of the two-tile decode launch holds, against which the plan
+// sizes each list's parts.
 hipError_t launch_attn_plan(const AttnArgs& a, int32_t rows_cap, int32_t P, bool prefill_on, bool cascade_on,
-                            int32_t* plan, hipStream_t stream);
+                            const int32_t dec_slots[2], int32_t* plan, hipStream_t stream);
 // Prefill query tiles and cascade prefix parts (their partials go to ws_pre).
 // lds_pad: extra dynamic LDS per workgroup (unused by the kernel; it caps
 // the workgroups per CU).

@@ -14,7 +14,7 @@ import torch
 
 import oracle
 import ragged_paged_attention_amd as rpa
-from tests.gpu_path import GpuRun, max_abs_err, tol_for
+from tests.gpu_path import GpuRun, capture_stderr, max_abs_err, tol_for
 from workloads import verify_batch
 from workloads.generators import build_workload
 
@@ -75,14 +75,21 @@ def test_row_classes_mixed_in_one_call(Hq, Hkv, ql):
 def test_verify_full_size_sampled_rows():
     """The verify workload at full size (64 sequences, query_len 2..8,
     contexts 2k..16k): every row of the 8 longest sequences and of 8 random
-    others, against the oracle."""
+    others, against the oracle.  Its two-tile list would fill between one
+    and two waves of that launch at the default part length, so the plan
+    gives it parts twice as long (the trace says so)."""
     w = verify_batch()
     offs = w.new_row_offsets()
     rng = np.random.default_rng(0)
     pick = set(np.argsort(-w.step.seq_lens)[:8].tolist()) | set(rng.choice(w.num_seqs, 8, replace=False).tolist())
     rows = sorted(r for s in pick for r in range(int(offs[s]), int(offs[s + 1])))
     print(f"[verify] full {w.summary()} rows={len(rows)}", flush=True)
-    g = GpuRun(w).run()
+    prev = rpa.pa_set_trace(1)
+    try:
+        g, text = capture_stderr(lambda: GpuRun(w).run())
+    finally:
+        rpa.pa_set_trace(prev)
+    assert "(parts of at most 768, 1536 tokens)" in text
     _, _, _, ref = oracle.run_step(w, rows=rows)
     assert g.err() == 0
     err = max_abs_err(g.out[torch.tensor(rows, device="cuda")], ref)
