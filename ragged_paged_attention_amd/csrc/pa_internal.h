@@ -115,7 +115,7 @@ pa_status_t attention_entry(AttnArgs a, const ScratchSource* scratch, hipStream_
 // empty.  Equal-sized parts keep the tail of the launch short however uneven
 // the context lengths are.  The plan, the decode kernels and the merge call
 // the same function with the same part_chunks, so their part ranges agree.
-constexpr int kPartChunks = 48;  // a context part is at most 48 chunks = 768 tokens
+constexpr int kPartChunks = 48;  // default part: at most 48 chunks = 768 tokens
 constexpr int kMaxParts = 64;    // parts per sequence (longer parts past 48k tokens)
 __host__ __device__ __forceinline__ void plan_parts(int32_t nchunks, int32_t P, int32_t* nparts, int32_t* cpp,
                                                     int32_t part_chunks = kPartChunks) {
