@@ -41,7 +41,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 # name fragment that identifies each kernel in rocprofv3 output (bf16 instances)
 KERNEL_MATCH = {
     "decode_kernel": "decode_kernel<pa::BF16, 1, 128, true",  # also the instance run beside the prefill kernel
-    "decode_kernel_2t": "decode_kernel<pa::BF16, 2, 128, true>",
+    "decode_kernel_2t": "decode_kernel<pa::BF16, 2, 128, true",
     "merge_kernel": "merge_kernel<pa::BF16, 128>",
     "prefill_kernel": "prefill_kernel<pa::BF16, true, 128>",
     "write_kv_kernel": "write_kv_kernel",

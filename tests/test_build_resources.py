@@ -58,3 +58,20 @@ def test_decode_beside_prefill_register_split():
         assert _regs(b) > 256                    # two of its waves never share a SIMD
         for p in prefill:
             assert _regs(b) + _regs(p) <= 512    # one of each does
+
+
+def test_bench_kernel_name_fragments_match_built_kernels():
+    """bench.py picks each kernel out of rocprofv3 output by a fragment of its
+    name; every fragment must match a kernel the sources build (a template
+    argument added to a kernel once left a counter summary empty)."""
+    filt = shutil.which("c++filt")
+    if filt is None:
+        pytest.skip("needs c++filt")
+    import bench
+    names = []
+    for src in ("attn_fast.hip", "attn_prefill.hip", "write_kv.hip", "copy_blocks.hip"):
+        mangled = list(_resources(src))
+        out = subprocess.run([filt], input="\n".join(mangled), capture_output=True, text=True, timeout=60).stdout
+        names += [n.replace("(anonymous namespace)::", "") for n in out.splitlines()]
+    for kernel, frag in bench.KERNEL_MATCH.items():
+        assert any(frag in n for n in names), (kernel, frag)
