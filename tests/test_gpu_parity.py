@@ -12,7 +12,7 @@ import torch
 
 import oracle
 import ragged_paged_attention_amd as rpa
-from workloads import config, random_batch, relabel_blocks, unshare
+from workloads import config, decode_variant, random_batch, relabel_blocks, unshare
 from workloads.device import to_numpy_bits
 
 from tests.gpu_path import GpuRun, capture_stderr, max_abs_err, one_stream_output, tol_for
@@ -352,3 +352,25 @@ def test_duplicate_slots_flagged_with_validation():
         assert int(d_err.item()) == 0
     finally:
         rpa.pa_set_validation(prev)
+
+
+def test_plan_doubles_the_parts_of_a_list_between_one_and_two_waves():
+    """40 decode sequences of 2101 tokens at 32 KV heads: with a plan (the
+    contexts are long enough for shared-prefix detection) the one-tile list
+    would hold 120 entries of 768-token parts against 96 that one wave of
+    the launch holds (3 waves per SIMD x 1024 SIMDs / 32 heads), so the plan
+    cuts 1536-token parts instead (80 entries, the trace says so); every row
+    matches the oracle."""
+    w = decode_variant(128, 16, S=40, hist_len=2100)
+    print(f"[case] doubled parts {w.summary()}", flush=True)
+    prev = rpa.pa_set_trace(1)
+    try:
+        g, text = capture_stderr(lambda: GpuRun(w).run())
+    finally:
+        rpa.pa_set_trace(prev)
+    assert "decode items 80 one-tile, 0 two-tile (parts of at most 1536, 768 tokens)" in text
+    assert g.err() == 0
+    _, _, _, ref = oracle.run_step(w)
+    err = max_abs_err(g.out, ref)
+    print(f"[doubled parts] max_abs_err={err:.3e}", flush=True)
+    assert err <= tol_for(w.dtype)
