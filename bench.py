@@ -444,7 +444,7 @@ def main():
 
     import ragged_paged_attention_amd as rpa
     from ragged_paged_attention_amd.step import forward_step
-    from workloads import accounting, config, decode_variant, prefill_variant, verify_batch
+    from workloads import accounting, config, decode_variant, permute_sequences, prefill_variant, verify_batch
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     timer = Timer(torch)
@@ -524,10 +524,36 @@ def main():
                 if r.get("mfma_busy"):
                     # counter collection runs dispatches one at a time
                     r["mfma_busy"]["measured_alone"] = True
-        if not args.no_cpu_baseline:
-            result["cpu_baseline"] = cpu_baseline(config(4, poison=False), args.cpu_sample_rows)
         del g, ws, out
         torch.cuda.empty_cache()
+        # The prefill sub-batch alone (the chunks without the decode
+        # sequences): the prefill kernel at two workgroups per CU, as in a
+        # batch with few decodes, so its own roofline on this shape stands
+        # next to the shared-phase figure above.
+        chunks = [s for s in range(w.num_seqs) if int(ql[s]) > 1]
+        if chunks:
+            wc = permute_sequences(w, chunks)
+            gc = setup(wc, torch)
+            outc = torch.empty_like(gc.db.q)
+            wsc = workspace_for(wc, rpa, torch)
+            dbc = gc.db
+
+            def step_chunks():
+                forward_step(dbc.q, dbc.k, dbc.v, gc.k_cache, gc.v_cache, dbc.query_lens, dbc.seq_lens,
+                             dbc.block_tables, wc.scale, wc.max_query_len, wc.max_seq_len, out=outc, workspace=wsc)
+
+            msc = timer.time(step_chunks, args.steps, args.warmup)
+            kc = timer.kernels(rpa, step_chunks, args.steps)
+            pk_ms = kc["prefill_kernel"][1]
+            a_tf = split["prefill_kernel"] / (pk_ms / 1e3) / 1e12
+            result["prefill_sub_batch_alone"] = {
+                "workload": f"the step's {len(chunks)} prefill chunks alone", "ms_per_call": msc,
+                "prefill_kernel_ms": pk_ms, "TFLOPs": a_tf, "frac_bf16_peak": a_tf / BF16_PEAK_TFLOPS,
+                "kernels_ms": {k: round(n * avg / args.steps, 5) for k, (n, avg) in kc.items()}}
+            del gc, wsc, outc
+            torch.cuda.empty_cache()
+        if not args.no_cpu_baseline:
+            result["cpu_baseline"] = cpu_baseline(config(4, poison=False), args.cpu_sample_rows)
 
     # ---------------- decode-only batch: KV-read bandwidth ----------------
     if args.only in (None, "decode"):
