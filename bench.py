@@ -78,7 +78,14 @@ def parse():
     ap.add_argument("--summarize-mfma", nargs=3, metavar=("PMC_DIR", "KERNEL", "WORKLOAD"),
                     help="write profiles/KERNEL.WORKLOAD.mfma.pmc.md from one rocprofv3 --pmc --kernel-trace run "
                          "with the MFMA counters; no GPU needed")
-    ap.add_argument("--command", default="", help="the command that produced the rocprofv3 output (recorded)")
+    ap.add_argument("--summarize-mempath", nargs=1, metavar="PMC_DIR",
+                    help="write profiles/prefill_kernel.chunked_mixed.memory_path.pmc.md from one rocprofv3 --pmc run "
+                         "of the step leg with the TA / TD / TCP / TCC counters; no GPU needed")
+    ap.add_argument("--summarize-waves", nargs=2, metavar=("STEP_PMC_DIR", "PREFILL_PMC_DIR"),
+                    help="write profiles/prefill_kernel.wave_states.pmc.md from rocprofv3 --pmc runs of the step and "
+                         "prefill legs with the SQ wave-state counters; no GPU needed")
+    ap.add_argument("--command", default="", help="the command that produced the rocprofv3 output (recorded; "
+                                                  "for --summarize-waves, STEP_OR_PREFILL stands for the leg)")
     ap.add_argument("--note", default="", help="a paragraph added to a counter summary (how to read it)")
     return ap.parse_args()
 
@@ -409,6 +416,81 @@ def summarize_mfma(pmc_dir, kernel, workload, command, note=""):
     print(f"wrote {out_md}")
 
 
+def _per_dispatch_avg(rows, kernel_substr):
+    """{counter: value per dispatch, averaged} over the dispatches of one kernel."""
+    per = {}
+    for r in rows:
+        if kernel_substr not in r["Kernel_Name"]:
+            continue
+        d = per.setdefault(r["Dispatch_Id"], {})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    if not per:
+        return {}, 0
+    names = set().union(*per.values())
+    return {c: sum(d.get(c, 0.0) for d in per.values()) / len(per) for c in names}, len(per)
+
+
+SPLIT_NOTE = ("Counter collection runs the dispatches one at a time: on the mixed batch the prefill launch holds one "
+              "workgroup per CU (the decode launch runs beside it in the timed step), so here it runs alone at half "
+              "occupancy.")
+
+
+def summarize_mempath(pmc_dir, command):
+    """TA / TD busy per CU, the TCP data stall and L1-to-L2 reads, and the L2
+    hit rate of the mixed step's prefill kernel, per dispatch."""
+    avg, n = _per_dispatch_avg(_csv_rows(_find(pmc_dir, "counter_collection.csv")), KERNEL_MATCH["prefill_kernel"])
+    act = avg["GRBM_GUI_ACTIVE"] / 8
+    h, m = avg["TCC_HIT_sum"], avg["TCC_MISS_sum"]
+    text = f"""# Memory-path counters: prefill_kernel on the chunked_mixed workload
+
+Command (run from the repository root on one MI355X):
+- `{command}`
+
+Per dispatch, averaged over {n} dispatches.  `_sum` counters add up all instances (one TA,
+TD and TCP per CU, 256 CUs); GRBM_GUI_ACTIVE adds up the 8 XCDs.  Busy fractions are per CU
+against GRBM_GUI_ACTIVE / 8.  {SPLIT_NOTE}
+
+| quantity | value |
+|---|---|
+| GRBM_GUI_ACTIVE | {avg['GRBM_GUI_ACTIVE']:.3e} |
+| TA_TA_BUSY_sum | {avg['TA_TA_BUSY_sum']:.3e} ({avg['TA_TA_BUSY_sum'] / 256 / act:.0%} of the active cycles per CU) |
+| TD_TD_BUSY_sum | {avg['TD_TD_BUSY_sum']:.3e} ({avg['TD_TD_BUSY_sum'] / 256 / act:.0%} per CU) |
+| TCP_TCP_TA_DATA_STALL_CYCLES_sum | {avg['TCP_TCP_TA_DATA_STALL_CYCLES_sum']:.3e} |
+| TCP_TCC_READ_REQ_sum | {avg['TCP_TCC_READ_REQ_sum']:.3e} |
+| TCC_HIT_sum / TCC_MISS_sum | {h:.3e} / {m:.3e} (L2 hit rate {h / (h + m):.0%}) |
+
+source_sha256_16: {source_hash(KERNEL_SOURCES['prefill_kernel'])}
+"""
+    out_md = os.path.join(PROFILES, "prefill_kernel.chunked_mixed.memory_path.pmc.md")
+    with open(out_md, "w") as f:
+        f.write(text)
+    print(f"wrote {out_md}")
+
+
+def summarize_waves(step_dir, prefill_dir, command):
+    """Wave-state fractions of the prefill kernel's resident wave cycles on the
+    mixed step and the ragged prefill legs."""
+    cols = ["SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_WAIT_INST_LDS", "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VALU",
+            "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_VMEM"]
+    lines = ["# Wave-state counters: prefill_kernel (chunked_mixed and ragged_prefill workloads)", "",
+             "Commands (run from the repository root on one MI355X):",
+             f"- `{command.replace('STEP_OR_PREFILL', 'step')}`", f"- `{command.replace('STEP_OR_PREFILL', 'prefill')}`",
+             "", f"Per dispatch of `{KERNEL_MATCH['prefill_kernel']}`, averaged; fractions are of SQ_WAVE_CYCLES",
+             "(every wave's resident cycles).  SQ_WAIT_ANY: waiting on a counter, a barrier or a dependency;",
+             "SQ_WAIT_INST_ANY: an instruction ready but not issued; SQ_ACTIVE_INST_*: issuing.", SPLIT_NOTE, "",
+             "| workload | dispatches | SQ_WAVE_CYCLES | wait_any | wait_inst_any | wait_inst_lds | active_any | "
+             "active_valu | active_lds | active_vmem |", "|---|---|---|---|---|---|---|---|---|---|"]
+    for d, wl in ((step_dir, "chunked_mixed"), (prefill_dir, "ragged_prefill")):
+        avg, n = _per_dispatch_avg(_csv_rows(_find(d, "counter_collection.csv")), KERNEL_MATCH["prefill_kernel"])
+        wc = avg["SQ_WAVE_CYCLES"]
+        lines.append(f"| {wl} | {n} | {wc:.3e} | " + " | ".join(f"{avg[c] / wc:.2f}" for c in cols) + " |")
+    lines += ["", f"source_sha256_16: {source_hash(KERNEL_SOURCES['prefill_kernel'])}", ""]
+    out_md = os.path.join(PROFILES, "prefill_kernel.wave_states.pmc.md")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines))
+    print(f"wrote {out_md}")
+
+
 def mfma_from_profiles(kernel: str, workload: str):
     """MFMA busy fraction and shader clock from the committed counter summary,
     or None if there is none or the kernel's source changed since."""
@@ -435,6 +517,12 @@ def main():
         return
     if args.summarize_mfma:
         summarize_mfma(*args.summarize_mfma, args.command, args.note)
+        return
+    if args.summarize_mempath:
+        summarize_mempath(args.summarize_mempath[0], args.command)
+        return
+    if args.summarize_waves:
+        summarize_waves(*args.summarize_waves, args.command)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (--gpus {args.gpus} was asked for): the library has no multi-GPU "
