@@ -21,16 +21,16 @@
  *     `stream` (a hipStream_t; NULL = default stream) and is complete when
  *     that stream is.  The caller owns the KV cache (the engine allocates
  *     one pool and hands out per-layer views, [VP] §3.6).
- *   - One exception, in pa_attention only: on a large mixed batch (prefill
- *     rows, head_dim 128, a block size that is a multiple of 16, at least 64
- *     sequences and at most 64 new tokens per sequence on average) the
- *     decode launches run on a side stream beside the prefill kernel, which
- *     stays on `stream`.  That stream (non-blocking, default priority) and
- *     its two events are created by the library on the first such call on a
- *     device and kept until the process ends; the fork from and join back
- *     into `stream` are event records and waits made under a process-wide
- *     lock, so the call still completes with `stream`.
- *     pa_attention_noalloc never uses it.
+ *   - One exception, in pa_attention and pa_write_kv_attention only: on a
+ *     large mixed batch (prefill rows, head_dim 128, a block size that is a
+ *     multiple of 16, at least 64 sequences and at most 64 new tokens per
+ *     sequence on average) the decode launches run on a side stream beside
+ *     the prefill kernel, which stays on `stream`.  That stream
+ *     (non-blocking, default priority) and its two events are created by
+ *     the library on the first such call on a device and kept until the
+ *     process ends; the fork from and join back into `stream` are event
+ *     records and waits made under a process-wide lock, so the call still
+ *     completes with `stream`.  pa_attention_noalloc never uses it.
  *   - Host-checkable problems (null pointers, bad sizes, unsupported shapes,
  *     a too-small workspace, a failed launch) are returned synchronously as
  *     pa_status_t and nothing is enqueued.
@@ -277,6 +277,40 @@ pa_status_t pa_attention(const void* q, const void* k_cache, const void* v_cache
                          int32_t max_query_len, int32_t max_seq_len, float scale, pa_dtype_t dtype,
                          void* out, void* workspace, size_t workspace_bytes, int32_t* d_err,
                          void* stream);
+
+/*
+ * pa_write_kv_attention — pa_write_kv followed by pa_attention, in one call.
+ *
+ * [VP] §3.7: the attention layer's forward stores the step's new K/V into
+ * the cache and then attends, as one operation; [FS] §2.3 第一步/第二步: the
+ * write goes first.  This call does exactly that: its results (the caches
+ * and out) are those of pa_write_kv(k, v, slot_mapping, num_tokens,
+ * num_kv_heads, head_dim, k_cache, v_cache, num_blocks, block_size, dtype,
+ * d_err, stream) followed by pa_attention(...) with the same arguments, bit
+ * for bit.  The difference is only in scheduling: the attention call's
+ * planning launch reads lengths and block tables, not the cache, so when the
+ * call has one (prefill rows, or contexts long enough for shared prefixes)
+ * the write runs in that launch as workgroups of its own, beside the
+ * planning workgroup, and every kernel that reads the cache follows it on
+ * `stream`.  Otherwise (no planning launch; k, v, the caches or the row size
+ * not 16-byte aligned; validation on) the write is a launch of its own
+ * before everything else on `stream`.
+ *   k, v  [num_tokens, num_kv_heads, head_dim], `dtype`: the new rows
+ *   slot_mapping [num_tokens]: as for pa_write_kv (from pa_build_metadata)
+ *   every other argument: as for pa_attention (k_cache / v_cache are
+ *        written, so they are not const here)
+ * Errors: pa_write_kv's checks, then pa_attention's; nothing is enqueued
+ * unless both pass.  With pa_set_validation on, the duplicate-slot check of
+ * pa_write_kv runs too.
+ */
+pa_status_t pa_write_kv_attention(const void* k, const void* v, const int32_t* slot_mapping, const void* q,
+                                  void* k_cache, void* v_cache, const int32_t* block_tables,
+                                  const int32_t* query_start_loc, const int32_t* seq_lens, int32_t num_seqs,
+                                  int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                  int32_t max_blocks_per_seq, int32_t max_query_len, int32_t max_seq_len,
+                                  float scale, pa_dtype_t dtype, void* out, void* workspace,
+                                  size_t workspace_bytes, int32_t* d_err, void* stream);
 
 /*
  * pa_attention_noalloc — pa_attention for callers that cannot allocate

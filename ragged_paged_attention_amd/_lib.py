@@ -87,6 +87,8 @@ _lib.pa_bench_timing_end.restype = _i32
 _lib.pa_bench_timing_end.argtypes = [ctypes.POINTER(KernelTime), _i32, ctypes.POINTER(_i32)]
 _lib.pa_attention.restype = _i32
 _lib.pa_attention.argtypes = [_p, _p, _p, _p, _p, _p] + [_i32] * 10 + [_f32, _i32, _p, _p, _size, _p, _p]
+_lib.pa_write_kv_attention.restype = _i32
+_lib.pa_write_kv_attention.argtypes = [_p] * 9 + [_i32] * 10 + [_f32, _i32, _p, _p, _size, _p, _p]
 _lib.pa_attention_noalloc.restype = _i32
 _lib.pa_attention_noalloc.argtypes = [_p, _p, _p, _p, _p, _p] + [_i32] * 10 + [_f32, _i32, _p, _p, _p]
 
@@ -269,6 +271,39 @@ def pa_attention(q, k_cache, v_cache, block_tables, query_start_loc, seq_lens, m
                            int(max_query_len), int(max_seq_len), float(scale), _dtype_code(q.dtype),
                            _ptr(out), _ptr(workspace), wbytes, _ptr(d_err), _stream(q.device))
     _check(st, "pa_attention")
+    return out
+
+
+def pa_write_kv_attention(k, v, slot_mapping, q, k_cache, v_cache, block_tables, query_start_loc, seq_lens,
+                          max_query_len: int, max_seq_len: int, scale: float, out=None, workspace=None,
+                          d_err=None):
+    """Calls pa_write_kv_attention: pa_write_kv(k, v, slot_mapping, ...) then
+    pa_attention(q, ...), in one call.  k, v [T, Hkv, D]; q [T, Hq, D];
+    caches [NB, BS, Hkv, D] (written); returns out."""
+    torch = _torch()
+    for t, n in ((k, "k"), (v, "v"), (q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (out, "out")):
+        _need(t, n, q.dtype)
+    for t, n in ((slot_mapping, "slot_mapping"), (block_tables, "block_tables"),
+                 (query_start_loc, "query_start_loc"), (seq_lens, "seq_lens")):
+        _need(t, n, torch.int32)
+    T, Hq, D = (int(x) for x in q.shape)
+    NB, BS, Hkv = int(k_cache.shape[0]), int(k_cache.shape[1]), int(k_cache.shape[2])
+    if int(k_cache.shape[3]) != D or v_cache.shape != k_cache.shape or tuple(k.shape) != (T, Hkv, D) or \
+            v.shape != k.shape:
+        raise ValueError("shape mismatch between new rows, queries and caches")
+    S = int(seq_lens.shape[0])
+    if out is None:
+        out = torch.empty_like(q)
+    need = pa_attention_workspace_size(S, T, Hq, Hkv, D, max_query_len, max_seq_len)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = _lib.pa_write_kv_attention(_ptr(k), _ptr(v), _ptr(slot_mapping), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                    _ptr(block_tables), _ptr(query_start_loc), _ptr(seq_lens), S, T, Hq, Hkv, D,
+                                    BS, NB, int(block_tables.shape[1]), int(max_query_len), int(max_seq_len),
+                                    float(scale), _dtype_code(q.dtype), _ptr(out), _ptr(workspace), wbytes,
+                                    _ptr(d_err), _stream(q.device))
+    _check(st, "pa_write_kv_attention")
     return out
 
 

@@ -709,7 +709,7 @@ bool decode_beside_prefill(const AttnArgs& a) {
          static_cast<int64_t>(a.T) <= static_cast<int64_t>(kBesideMaxMeanQuery) * a.S;
 }
 
-hipError_t launch_attn_fast(const AttnArgs& a, hipStream_t stream, bool side_stream_ok) {
+hipError_t launch_attn_fast(const AttnArgs& a, hipStream_t stream, bool side_stream_ok, const WriteJob* w) {
   const FastPlan f = fast_plan(a.S, a.T, a.Hq, a.Hkv, a.D, a.max_qlen, a.max_seqlen);
   DecodeArgs d;
   d.q = static_cast<const uint16_t*>(a.q);
@@ -757,24 +757,39 @@ hipError_t launch_attn_fast(const AttnArgs& a, hipStream_t stream, bool side_str
   // taking every slot a prefill workgroup frees).  Other calls run their
   // launches one after the other on `stream`.
   const bool beside = side_stream_ok && decode_beside_prefill(a);
+  // A KV write that comes with the call (pa_write_kv_attention) goes into the
+  // planning launch as workgroups of its own: planning reads only lengths and
+  // block tables, and everything that reads the cache follows that launch.
+  // (On the side stream beside the planning launches instead, the two event
+  // waits it needs cost as much as the overlap gained: mixed batch 0.677 ms
+  // per step either way.)  Without a plan it goes first on `stream`.
+  const bool write_in_plan = w && f.mfma_prefill && write_in_plan_ok(*w);
+  if (w && !write_in_plan) {
+    const hipError_t e = launch_write_kv(w->k, w->v, w->slot_mapping, w->T, w->row_bytes, w->k_cache, w->v_cache,
+                                         w->num_slots, w->d_err, w->validate, stream);
+    if (e != hipSuccess) return e;
+  }
   std::unique_lock<std::mutex> side_lock(g_side_mu, std::defer_lock);
-  SideStream* side = nullptr;
-  hipStream_t ds = stream;  // the decode launches' stream
+  SideStream* ss = nullptr;
+  if (beside) {
+    side_lock.lock();
+    ss = side_stream_locked();
+  }
+  SideStream* side = nullptr;  // the side stream when the decode launches run on it
+  hipStream_t ds = stream;     // the decode launches' stream
   if (f.mfma_prefill) {
     int32_t* plan = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(a.workspace) + f.plan_off);
     // list entries one wave of each decode launch holds: waves per SIMD x
     // 1024 SIMDs, one wave per KV head of an entry
     const int32_t dec_slots[2] = {kSimds * (beside || a.D == 256 ? 1 : 3) / a.Hkv, kSimds * 2 / a.Hkv};
-    hipError_t e = launch_attn_plan(a, f.rows_cap, f.P, f.prefill_on, f.cascade_on, dec_slots, plan, stream);
+    hipError_t e = launch_attn_plan(a, f.rows_cap, f.P, f.prefill_on, f.cascade_on, dec_slots, plan,
+                                    write_in_plan ? w : nullptr, stream);
     if (e != hipSuccess) return e;
-    if (beside) {  // the decode launches wait for the plan only
-      side_lock.lock();
-      side = side_stream_locked();
-      if (side && hipEventRecord(side->fork, stream) == hipSuccess &&
-          hipStreamWaitEvent(side->s, side->fork, 0) == hipSuccess)
-        ds = side->s;
-      else
-        side = nullptr;
+    if (beside && ss) {  // the decode launches wait for the planning launch (and the write in it)
+      if (hipEventRecord(ss->fork, stream) == hipSuccess && hipStreamWaitEvent(ss->s, ss->fork, 0) == hipSuccess) {
+        side = ss;
+        ds = ss->s;
+      }
     }
     e = launch_attn_prefill(a, f.rows_cap, f.P, f.prefill_on, f.cascade_on, plan,
                             reinterpret_cast<float*>(static_cast<uint8_t*>(a.workspace) + f.pre_off),
@@ -843,15 +858,16 @@ static hipError_t trace_d_err(const AttnArgs& a, hipStream_t stream) {
   return r;
 }
 
-// Waits for the call, copies its plan to the host and prints it.
-hipError_t trace_attn_fast(const AttnArgs& a, hipStream_t stream) {
+// Waits for the call, copies its plan to the host and prints it.  w: the KV
+// write the call also did (in the planning launch, or first), or null.
+hipError_t trace_attn_fast(const AttnArgs& a, hipStream_t stream, const WriteJob* w) {
   const FastPlan f = fast_plan(a.S, a.T, a.Hq, a.Hkv, a.D, a.max_qlen, a.max_seqlen);
   trace_header(a, "fast");
   std::fprintf(stderr,
                "[pa_trace]   split: G=%d decode_parts<=%d rows_per_decode_item<=%d "
-               "prefill_rows=%d shared_prefix=%d decode_beside_prefill=%d workspace_bytes=%zu\n",
+               "prefill_rows=%d shared_prefix=%d decode_beside_prefill=%d kv_write=%s workspace_bytes=%zu\n",
                f.G, f.P, f.rows_cap, f.prefill_on ? 1 : 0, f.cascade_on ? 1 : 0, decode_beside_prefill(a) ? 1 : 0,
-               f.bytes);
+               !w ? "none" : f.mfma_prefill && write_in_plan_ok(*w) ? "in_plan" : "first", f.bytes);
   hipError_t e = hipStreamSynchronize(stream);
   if (e != hipSuccess) return e;
   if (!f.mfma_prefill) {

@@ -88,6 +88,16 @@ struct PlanArgs {
   const int2* match; // per sequence: (leader, blocks shared with it), from cascade_match_kernel
   int2* dec;         // decode lists: one-tile at dec, two-tile at dec + cap_dec
   int32_t* d_err;
+  // a KV write done by workgroups 1.. of the launch, 16 token rows each
+  // (write_kv_row; 16-byte rows and pointers); wT = 0: none
+  const char* wk;
+  const char* wv;
+  const int32_t* wslot;
+  char* wk_cache;
+  char* wv_cache;
+  int64_t w_row_bytes, w_num_slots;
+  int32_t* w_err;
+  int32_t wT;
 };
 
 struct MatchArgs {
@@ -261,6 +271,14 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(PlanArgs a) {
   __shared__ int32_t dhist[2][2][kDecBuckets];  // [default, doubled part length][list][weight]
   __shared__ int32_t dcur[2][kDecBuckets];
   __shared__ int32_t dcount[2];  // decode list entries at the default part length
+  if (blockIdx.x > 0) {  // the KV write's workgroups: one wave per token row
+    const int64_t t = static_cast<int64_t>(blockIdx.x - 1) * (kPlanThreads / 64) +
+                      __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (t < a.wT)
+      write_kv_row<16>(a.wk, a.wv, a.wslot, t, a.w_row_bytes, a.wk_cache, a.wv_cache, a.w_num_slots, a.w_err,
+                       threadIdx.x & 63);
+    return;
+  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int i = tid; i < kPlanBuckets; i += kPlanThreads) hist[i] = 0;
   for (int i = tid; i < kDecBuckets; i += kPlanThreads) {
@@ -969,7 +987,7 @@ bool cascade_possible(int32_t S, int32_t max_seqlen) {
 }
 
 hipError_t launch_attn_plan(const AttnArgs& a, int32_t rows_cap, int32_t P, bool prefill_on, bool cascade_on,
-                            const int32_t dec_slots[2], int32_t* plan, hipStream_t stream) {
+                            const int32_t dec_slots[2], int32_t* plan, const WriteJob* w, hipStream_t stream) {
   const int32_t G = a.Hq / a.Hkv;
   const PlanLayout l = plan_layout(a.S, a.T, G, P, prefill_on, cascade_on);
   PlanArgs p;
@@ -999,6 +1017,15 @@ hipError_t launch_attn_plan(const AttnArgs& a, int32_t rows_cap, int32_t P, bool
   p.cap_dec = l.cap_dec;
   p.dec = reinterpret_cast<int2*>(reinterpret_cast<uint8_t*>(plan) + l.dec_off);
   p.d_err = a.d_err;
+  p.wk = w ? static_cast<const char*>(w->k) : nullptr;
+  p.wv = w ? static_cast<const char*>(w->v) : nullptr;
+  p.wslot = w ? w->slot_mapping : nullptr;
+  p.wk_cache = w ? static_cast<char*>(w->k_cache) : nullptr;
+  p.wv_cache = w ? static_cast<char*>(w->v_cache) : nullptr;
+  p.w_row_bytes = w ? w->row_bytes : 0;
+  p.w_num_slots = w ? w->num_slots : 0;
+  p.w_err = w ? w->d_err : nullptr;
+  p.wT = w && w->row_bytes > 0 ? w->T : 0;
   if (cascade_on) {
     MatchArgs m;
     m.qsl = a.qsl;
@@ -1013,8 +1040,9 @@ hipError_t launch_attn_plan(const AttnArgs& a, int32_t rows_cap, int32_t P, bool
     cascade_match_kernel<<<static_cast<uint32_t>(a.S), kMatchThreads, 0, stream>>>(m);
     launch_done(stream);
   }
+  const int64_t wgs = 1 + (static_cast<int64_t>(p.wT) + kPlanThreads / 64 - 1) / (kPlanThreads / 64);
   launch_mark("attn_plan_kernel", stream);
-  attn_plan_kernel<<<1, kPlanThreads, 0, stream>>>(p);
+  attn_plan_kernel<<<static_cast<uint32_t>(wgs), kPlanThreads, 0, stream>>>(p);
   launch_done(stream);
   return hipGetLastError();
 }

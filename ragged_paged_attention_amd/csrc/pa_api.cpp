@@ -44,12 +44,13 @@ int64_t elem_bytes(pa_dtype_t d) { return d == PA_F32 ? 4 : 2; }
 
 namespace pa {
 
-// Argument checks and path selection shared by pa_attention and
-// pa_attention_noalloc.  scratch: a workspace the library owns (its size is
-// a.workspace_bytes); the caller's workspace arguments are then not used, and
-// a call that would need more is refused with PA_ERR_WORKSPACE before any
-// other HIP call is made.
-pa_status_t attention_entry(AttnArgs a, const ScratchSource* scratch, hipStream_t stream) {
+// Argument checks and path selection shared by pa_attention,
+// pa_attention_noalloc and pa_write_kv_attention.  scratch: a workspace the
+// library owns (its size is a.workspace_bytes); the caller's workspace
+// arguments are then not used, and a call that would need more is refused
+// with PA_ERR_WORKSPACE before any other HIP call is made.  w: a KV write
+// (already checked) that must land before the attention reads the cache.
+pa_status_t attention_entry(AttnArgs a, const ScratchSource* scratch, hipStream_t stream, const WriteJob* w) {
   if (bad_dtype(a.dtype)) return PA_ERR_DTYPE;
   if (a.S < 0 || a.T < 0 || a.Hq < 1 || a.Hkv < 1 || a.D < 1 || a.bs < 1 || a.NB < 1 || a.MB < 0)
     return PA_ERR_SHAPE;
@@ -80,12 +81,15 @@ pa_status_t attention_entry(AttnArgs a, const ScratchSource* scratch, hipStream_
   hipError_t e;
   clear_stale_error();
   if (policy == PA_POLICY_GENERIC || (policy == PA_POLICY_AUTO && !fast_ok)) {
-    e = launch_attn_generic(a, stream);
+    e = w ? launch_write_kv(w->k, w->v, w->slot_mapping, w->T, w->row_bytes, w->k_cache, w->v_cache, w->num_slots,
+                            w->d_err, w->validate, stream)
+          : hipSuccess;
+    if (e == hipSuccess) e = launch_attn_generic(a, stream);
   } else {
     if (!fast_ok) return PA_ERR_UNSUPPORTED;
     if (need > 0 && (!a.workspace || a.workspace_bytes < need)) return PA_ERR_WORKSPACE;
-    e = launch_attn_fast(a, stream, /*side_stream_ok=*/scratch == nullptr);
-    if (e == hipSuccess && !scratch && g_trace.load()) e = trace_attn_fast(a, stream);
+    e = launch_attn_fast(a, stream, /*side_stream_ok=*/scratch == nullptr, w);
+    if (e == hipSuccess && !scratch && g_trace.load()) e = trace_attn_fast(a, stream, w);
     return hip_status(e, "pa_attention");
   }
   if (e == hipSuccess && !scratch && g_trace.load()) trace_attn_generic(a);
@@ -211,6 +215,31 @@ pa_status_t pa_attention(const void* q, const void* k_cache, const void* v_cache
                  num_blocks, max_blocks_per_seq, max_query_len, max_seq_len, scale, dtype,
                  out, workspace, workspace_bytes, d_err};
   return pa::attention_entry(a, nullptr, static_cast<hipStream_t>(stream));
+}
+
+pa_status_t pa_write_kv_attention(const void* k, const void* v, const int32_t* slot_mapping, const void* q,
+                                  void* k_cache, void* v_cache, const int32_t* block_tables,
+                                  const int32_t* query_start_loc, const int32_t* seq_lens, int32_t num_seqs,
+                                  int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                  int32_t max_blocks_per_seq, int32_t max_query_len, int32_t max_seq_len,
+                                  float scale, pa_dtype_t dtype, void* out, void* workspace,
+                                  size_t workspace_bytes, int32_t* d_err, void* stream) {
+  // pa_write_kv's checks first (the attention's follow in attention_entry);
+  // nothing is enqueued unless both pass
+  if (bad_dtype(dtype)) return PA_ERR_DTYPE;
+  if (num_tokens < 0 || num_kv_heads < 1 || head_dim < 1 || num_blocks < 1 || block_size < 1)
+    return PA_ERR_SHAPE;
+  if (static_cast<int64_t>(num_blocks) * block_size > INT32_MAX) return PA_ERR_SHAPE;
+  if (num_tokens > 0 && (!k || !v || !slot_mapping)) return PA_ERR_NULL;
+  const pa::WriteJob w{k, v, slot_mapping, num_tokens,
+                       static_cast<int64_t>(num_kv_heads) * head_dim * elem_bytes(dtype), k_cache, v_cache,
+                       static_cast<int64_t>(num_blocks) * block_size, d_err, g_validate.load() != 0};
+  pa::AttnArgs a{q, k_cache, v_cache, block_tables, query_start_loc, seq_lens,
+                 num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim, block_size,
+                 num_blocks, max_blocks_per_seq, max_query_len, max_seq_len, scale, dtype,
+                 out, workspace, workspace_bytes, d_err};
+  return pa::attention_entry(a, nullptr, static_cast<hipStream_t>(stream), &w);
 }
 
 }  // extern "C"

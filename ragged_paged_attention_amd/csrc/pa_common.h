@@ -60,6 +60,58 @@ __device__ __forceinline__ void flag(int32_t* d_err, int32_t bits) {
 __host__ __device__ __forceinline__ int32_t ceil_div(int32_t a, int32_t b) { return (a + b - 1) / b; }
 
 // ---------------------------------------------------------------------------
+// KV write: one token row into its cache slot
+// ---------------------------------------------------------------------------
+// With the cache laid out [num_blocks, block_size, Hkv, D], the K (or V) of
+// all heads of one slot is one contiguous row of Hkv*D elements, like a row of
+// the new k/v [T, Hkv, D] ("vLLM Continuous Batching：从 Forward Shape 理解两个
+// 核心参数" §2.3 第一步: slot_mapping names each token's physical slot).  One
+// wave copies row t: the slot is one load, then each lane copies VEC-byte
+// chunks, two K and two V loads in flight per pass, every access coalesced.
+// A negative slot is skipped (a padding token); a slot past the pool flags
+// PA_DERR_SLOT_OOB and writes nothing.
+template <int VEC>
+struct KvVec;
+template <> struct KvVec<16> { using T = uint4; };
+template <> struct KvVec<8> { using T = uint2; };
+template <> struct KvVec<4> { using T = uint32_t; };
+template <> struct KvVec<2> { using T = uint16_t; };
+
+template <int VEC>
+__device__ __forceinline__ void write_kv_row(const char* __restrict__ k, const char* __restrict__ v,
+                                             const int32_t* __restrict__ slot_mapping, int64_t t, int64_t row_bytes,
+                                             char* __restrict__ k_cache, char* __restrict__ v_cache,
+                                             int64_t num_slots, int32_t* d_err, int lane) {
+  using V = typename KvVec<VEC>::T;
+  const int32_t slot = slot_mapping[t];
+  if (slot < 0) return;
+  if (slot >= num_slots) {
+    if (lane == 0) flag(d_err, PA_DERR_SLOT_OOB);
+    return;
+  }
+  const int64_t per_row = row_bytes / VEC;
+  const V* ks = reinterpret_cast<const V*>(k + t * row_bytes);
+  const V* vs = reinterpret_cast<const V*>(v + t * row_bytes);
+  V* kd = reinterpret_cast<V*>(k_cache + static_cast<int64_t>(slot) * row_bytes);
+  V* vd = reinterpret_cast<V*>(v_cache + static_cast<int64_t>(slot) * row_bytes);
+  for (int64_t c = lane; c < per_row; c += 128) {
+    const bool two = c + 64 < per_row;
+    const V k0 = ks[c], v0 = vs[c];
+    V k1 = k0, v1 = v0;
+    if (two) {
+      k1 = ks[c + 64];
+      v1 = vs[c + 64];
+    }
+    kd[c] = k0;
+    vd[c] = v0;
+    if (two) {
+      kd[c + 64] = k1;
+      vd[c + 64] = v1;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // wave64 reductions: butterfly over lane distances 32..1 with __shfl_xor
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float wave_max(float v) {

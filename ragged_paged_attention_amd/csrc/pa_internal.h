@@ -58,10 +58,33 @@ hipError_t launch_attn_generic_rows(const AttnArgs& a, int32_t skip_rows_le, hip
 bool fast_path_supported(const AttnArgs& a);
 size_t fast_workspace_bytes(int32_t S, int32_t T, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_q,
                             int32_t max_seqlen);
+// The KV write of pa_write_kv_attention: what launch_write_kv takes.
+struct WriteJob {
+  const void* k;
+  const void* v;
+  const int32_t* slot_mapping;
+  int32_t T;
+  int64_t row_bytes;
+  void* k_cache;
+  void* v_cache;
+  int64_t num_slots;
+  int32_t* d_err;
+  bool validate;
+};
+// The planning launch can take the write as extra workgroups (16-byte rows
+// and pointers; without validation, whose check is a launch of its own).
+inline bool write_in_plan_ok(const WriteJob& w) {
+  const uintptr_t align = reinterpret_cast<uintptr_t>(w.k) | reinterpret_cast<uintptr_t>(w.v) |
+                          reinterpret_cast<uintptr_t>(w.k_cache) | reinterpret_cast<uintptr_t>(w.v_cache) |
+                          static_cast<uintptr_t>(w.row_bytes);
+  return !w.validate && align % 16 == 0;
+}
 // side_stream_ok: a large mixed batch may run its decode launches on the
 // library's side stream beside the prefill kernel (decode_beside_prefill);
-// false keeps every launch on `stream`.
-hipError_t launch_attn_fast(const AttnArgs& a, hipStream_t stream, bool side_stream_ok);
+// false keeps every launch on `stream`.  A KV write w goes into the planning
+// launch when the call has one (write_in_plan_ok), else first on `stream`.
+hipError_t launch_attn_fast(const AttnArgs& a, hipStream_t stream, bool side_stream_ok,
+                            const WriteJob* w = nullptr);
 // A call whose decode launches run beside the prefill kernel (given a side
 // stream): prefill rows, head_dim 128, a block size that is a multiple of 16,
 // at least kBesideMinSeqs sequences and at most kBesideMaxMeanQuery new
@@ -72,7 +95,7 @@ constexpr int kBesideMaxMeanQuery = 64;
 constexpr size_t kBesideLdsPad = 20 << 10;  // prefill launch's extra LDS: 84 KB per workgroup, one per CU
 // Plan trace (pa_set_trace): waits for `stream`, then prints the call's work
 // split and plan to stderr; the generic path prints its header line only.
-hipError_t trace_attn_fast(const AttnArgs& a, hipStream_t stream);
+hipError_t trace_attn_fast(const AttnArgs& a, hipStream_t stream, const WriteJob* w = nullptr);
 void trace_attn_generic(const AttnArgs& a);
 
 // A workspace owned by the library (pa_attention_noalloc): its size, and how
@@ -81,8 +104,10 @@ struct ScratchSource {
   size_t bytes;
   pa_status_t (*lookup)(void** ptr);
 };
-// pa_api.cpp: checks, path selection and launches of one attention call.
-pa_status_t attention_entry(AttnArgs a, const ScratchSource* scratch, hipStream_t stream);
+// pa_api.cpp: checks, path selection and launches of one attention call;
+// w: the KV write to run first (pa_write_kv_attention), or null.
+pa_status_t attention_entry(AttnArgs a, const ScratchSource* scratch, hipStream_t stream,
+                            const WriteJob* w = nullptr);
 
 // attn_prefill.hip: rows of sequences with query_len * (Hq/Hkv) > min_rows.
 // Work plan of one call on the MFMA paths, written to the workspace by the
@@ -146,9 +171,11 @@ PlanLayout plan_layout(int32_t S, int32_t T, int32_t G, int32_t P, bool prefill_
 bool cascade_possible(int32_t S, int32_t max_seqlen);
 // dec_slots: list entries (each one wave per KV head) that one wave of the
 // one-tile and of the two-tile decode launch holds, against which the plan
-// sizes each list's parts.
+// sizes each list's parts.  w (may be null; write_in_plan_ok): a KV write
+// that the planning launch also does, in workgroups of its own beside the
+// planning one.
 hipError_t launch_attn_plan(const AttnArgs& a, int32_t rows_cap, int32_t P, bool prefill_on, bool cascade_on,
-                            const int32_t dec_slots[2], int32_t* plan, hipStream_t stream);
+                            const int32_t dec_slots[2], int32_t* plan, const WriteJob* w, hipStream_t stream);
 // Prefill query tiles and cascade prefix parts (their partials go to ws_pre).
 // lds_pad: extra dynamic LDS per workgroup (unused by the kernel; it caps
 // the workgroups per CU).

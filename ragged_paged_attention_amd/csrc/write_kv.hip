@@ -16,51 +16,15 @@
 namespace pa {
 namespace {
 
-template <int VEC>
-struct Vec;
-template <> struct Vec<16> { using T = uint4; };
-template <> struct Vec<8> { using T = uint2; };
-template <> struct Vec<4> { using T = uint32_t; };
-template <> struct Vec<2> { using T = uint16_t; };
-
-// One wave per token row: the row's slot is one scalar load, then each lane
-// copies VEC-byte chunks of the row, two K and two V loads in flight per pass.
+// One wave per token row (write_kv_row), four rows per workgroup.
 template <int VEC>
 __global__ __launch_bounds__(256) void write_kv_kernel(
     const char* __restrict__ k, const char* __restrict__ v, const int32_t* __restrict__ slot_mapping,
     int32_t T, int64_t row_bytes, char* __restrict__ k_cache, char* __restrict__ v_cache,
     int64_t num_slots, int32_t* __restrict__ d_err) {
-  using V = typename Vec<VEC>::T;
-  const int lane = threadIdx.x & 63;
   const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (t >= T) return;
-  const int32_t slot = slot_mapping[t];
-  if (slot < 0) return;
-  if (slot >= num_slots) {
-    if (lane == 0) flag(d_err, PA_DERR_SLOT_OOB);
-    return;
-  }
-  const int64_t per_row = row_bytes / VEC;
-  const V* ks = reinterpret_cast<const V*>(k + t * row_bytes);
-  const V* vs = reinterpret_cast<const V*>(v + t * row_bytes);
-  V* kd = reinterpret_cast<V*>(k_cache + static_cast<int64_t>(slot) * row_bytes);
-  V* vd = reinterpret_cast<V*>(v_cache + static_cast<int64_t>(slot) * row_bytes);
-  // two chunks per lane per pass, both loads of a pass issued before its stores
-  for (int64_t c = lane; c < per_row; c += 128) {
-    const bool two = c + 64 < per_row;
-    const V k0 = ks[c], v0 = vs[c];
-    V k1 = k0, v1 = v0;
-    if (two) {
-      k1 = ks[c + 64];
-      v1 = vs[c + 64];
-    }
-    kd[c] = k0;
-    vd[c] = v0;
-    if (two) {
-      kd[c + 64] = k1;
-      vd[c + 64] = v1;
-    }
-  }
+  write_kv_row<VEC>(k, v, slot_mapping, t, row_bytes, k_cache, v_cache, num_slots, d_err, threadIdx.x & 63);
 }
 
 // Validation (pa_set_validation): flags PA_DERR_DUP_SLOT when two rows of

@@ -84,6 +84,14 @@ def test_host_side_rejections_need_no_gpu():
     assert att(scale=float("nan")) == 7   # non-finite softmax scale
     assert att(scale=float("inf")) == 7
     assert lib.pa_attention_workspace_size(4, 100, 32, 32, 128, 1, 2001) >= 0
+    # the fused write + attention: pa_write_kv's checks, then pa_attention's
+    wa = lambda **kw: lib.pa_write_kv_attention(*_write_attn_args(**kw))
+    assert wa(dtype=9) == 3               # bad dtype
+    assert wa(NB=1 << 20, bs=1 << 12) == 2  # slots overflowing int32
+    assert wa(T=0) == 0                   # empty batch: nothing to do
+    assert wa() == 1                      # null new rows
+    assert wa(fake_rows=True, Hq=6, Hkv=4) == 2   # then the attention's own checks
+    assert wa(fake_rows=True, scale=float("nan")) == 7
     cp = lambda nsrc=4, ndst=4, n=1, bb=8192, ptr=16: lib.pa_copy_blocks(ptr, ptr, ptr, ptr, nsrc, ndst, ptr, n, bb,
                                                                           NULL, NULL)
     assert cp(bb=8200) == 2               # block bytes not a multiple of 16
@@ -111,3 +119,9 @@ def test_noalloc_refuses_calls_beyond_its_scratch_without_a_gpu():
 
 def _attn_args(T=3, Hq=4, Hkv=2, D=16, max_q=2, S=2, scale=0.25):
     return [None] * 6 + [S, T, Hq, Hkv, D, 16, 8, 4, max_q, 8, ctypes.c_float(scale), 1, None, None, 0, None, None]
+
+
+def _write_attn_args(T=3, Hq=4, Hkv=2, D=16, max_q=2, S=2, scale=0.25, dtype=1, NB=8, bs=16, fake_rows=False):
+    rows = [ctypes.c_void_p(1 << 20)] * 3 if fake_rows else [None] * 3   # never dereferenced: checks come first
+    return rows + [None] * 6 + [S, T, Hq, Hkv, D, bs, NB, 4, max_q, 8, ctypes.c_float(scale), dtype, None, None, 0,
+                                None, None]
