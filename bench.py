@@ -67,6 +67,9 @@ def parse():
                     default=None,
                     help="run one leg only (for profiling)")
     ap.add_argument("--cpu-sample-rows", type=int, default=2048)
+    ap.add_argument("--no-sub-batch", action="store_true",
+                    help="in the step leg, skip the prefill chunks' run on their own (profiles of the mixed step "
+                         "then hold only its dispatches)")
     ap.add_argument("--cold-launches", type=int, default=50,
                     help="single launches timed after a cache flush each (median reported)")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("ROCPROF_DIR", "OUT_MD"),
@@ -619,7 +622,7 @@ def main():
         # batch with few decodes, so its own roofline on this shape stands
         # next to the shared-phase figure above.
         chunks = [s for s in range(w.num_seqs) if int(ql[s]) > 1]
-        if chunks:
+        if chunks and not args.no_sub_batch:
             wc = permute_sequences(w, chunks)
             gc = setup(wc, torch)
             outc = torch.empty_like(gc.db.q)
