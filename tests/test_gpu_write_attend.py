@@ -24,6 +24,11 @@ CASES = {
     "verify": lambda: verify_batch(scale_down=4),           # a plan (contexts long enough for shared prefixes)
     "decode_no_plan": lambda: config(3, scale_down=8),      # no plan: the write goes first
     "tiny_generic": lambda: config(1),                      # fp32: the generic kernel
+    # the same mixed batch in fp16, and with blocks of 32 and of 8 tokens
+    # (the instances for block sizes that divide 16)
+    "mixed_split_f16": lambda: config(4, scale_down=4, dtype="f16"),
+    "mixed_bs32": lambda: config(4, scale_down=4, block_size=32),
+    "mixed_bs8": lambda: config(4, scale_down=4, block_size=8),
     # three shared-prefix groups next to prefill chunks: cascade matching
     # reads block tables while the write fills the groups' new rows
     "groups_split": lambda: grouped_batch(31, [("group", 22, 2048, 1, 200), ("single", 96, 1500),
@@ -35,7 +40,8 @@ CASES = {
 # launch; "first": its own launch before everything else on the caller's
 # stream); the generic kernel prints no split line
 WRITE_AT = {"mixed_split": "in_plan", "ragged_prefill": "in_plan", "verify": "in_plan",
-            "decode_no_plan": "first", "tiny_generic": None, "groups_split": "in_plan"}
+            "decode_no_plan": "first", "tiny_generic": None, "groups_split": "in_plan",
+            "mixed_split_f16": "in_plan", "mixed_bs32": "in_plan", "mixed_bs8": "in_plan"}
 
 
 def _separate(w, g):
@@ -59,7 +65,7 @@ def test_fused_write_and_attention_equal_the_two_calls(name):
         g, text = capture_stderr(lambda: GpuRun(w).run())   # forward_step: metadata, then the fused call
     finally:
         rpa.pa_set_trace(prev)
-    if name in ("mixed_split", "groups_split"):
+    if name in ("mixed_split", "groups_split", "mixed_split_f16", "mixed_bs32"):
         assert "decode_beside_prefill=1" in text
     if WRITE_AT[name]:
         assert f"kv_write={WRITE_AT[name]}" in text
