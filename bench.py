@@ -163,6 +163,31 @@ def setup(w, torch):
     return g
 
 
+def metadata_and_write(w, g, rpa, timer, args):
+    """pa_build_metadata and pa_write_kv of a leg's step, each on its own (the
+    step itself runs the write inside pa_write_kv_attention's planning
+    launch): back to back and cold-cache times.  The write's algorithmic bytes
+    are 2 (K, V) x 2 (read, write) x T x Hkv x D x element size; rewriting the
+    same rows leaves the cache as it was."""
+    db = g.db
+    md = rpa.pa_build_metadata(db.query_lens, db.seq_lens, w.num_tokens, db.block_tables, w.block_size,
+                               w.num_blocks)
+    meta = lambda: rpa.pa_build_metadata(db.query_lens, db.seq_lens, w.num_tokens, db.block_tables, w.block_size,
+                                         w.num_blocks, out=md)
+    write = lambda: rpa.pa_write_kv(db.k, db.v, md["slot_mapping"], g.k_cache, g.v_cache)
+    n = max(args.steps, 20)
+    ms_m, cold_m = timer.time(meta, n, args.warmup), timer.time_cold(meta, args.cold_launches)
+    ms_w, cold_w = timer.time(write, n, args.warmup), timer.time_cold(write, args.cold_launches)
+    wb = 4 * w.num_tokens * w.num_kv_heads * w.head_dim * (4 if w.dtype == "f32" else 2)
+    gbs = wb / (ms_w / 1e3) / 1e9
+    return {
+        "pa_build_metadata": {"seqs": w.num_seqs, "tokens": w.num_tokens, "ms_per_call": ms_m,
+                              "cold_median_ms": cold_m["median_ms"]},
+        "pa_write_kv": {"rows": w.num_tokens, "bytes": wb, "ms_per_call": ms_w, "GBps": gbs,
+                        "frac_hbm_peak": gbs / HBM_PEAK_GBS, "cold_median_ms": cold_w["median_ms"],
+                        "cold_GBps": wb / (cold_w["median_ms"] / 1e3) / 1e9}}
+
+
 def workspace_for(w, rpa, torch):
     need = rpa.pa_attention_workspace_size(w.num_seqs, w.num_tokens, w.num_q_heads, w.num_kv_heads, w.head_dim,
                                            w.max_query_len, w.max_seq_len)
@@ -615,6 +640,7 @@ def main():
                 if r.get("mfma_busy"):
                     # counter collection runs dispatches one at a time
                     r["mfma_busy"]["measured_alone"] = True
+        result["step_metadata_and_write"] = metadata_and_write(w, g, rpa, timer, args)
         del g, ws, out
         torch.cuda.empty_cache()
         # The prefill sub-batch alone (the chunks without the decode
@@ -675,6 +701,7 @@ def main():
             "decode_kernel_GBps": kv3 / (kern3["decode_kernel"][1] / 1e3) / 1e9,
             "ceiling_stream_read_GBps": stream_gbs,
             "ceiling_paged_read_no_math_GBps": rounded / (ms_paged / 1e3) / 1e9}
+        result["decode_kv_read"]["metadata_and_write"] = metadata_and_write(w3, g3, rpa, timer, args)
         if args.only == "decode":
             result["roofline"] = roofline_for("decode_kernel", kern3["decode_kernel"][1], w3, w3.name)
         del g3, ws3, out3
@@ -750,7 +777,8 @@ def main():
             "logical_bytes": kv5, "unique_bytes": uq5,
             "kernels_ms": {k: round(avg, 5) for k, (n, avg) in kern5.items()},
             "cold_cache": {**cold5, "logical_GBps": kv5 / (cold5["median_ms"] / 1e3) / 1e9,
-                           "unique_GBps": uq5 / (cold5["median_ms"] / 1e3) / 1e9}}
+                           "unique_GBps": uq5 / (cold5["median_ms"] / 1e3) / 1e9},
+            "metadata_and_write": metadata_and_write(w5, g5, rpa, timer, args)}
         del g5, ws5, out5
         torch.cuda.empty_cache()
 
@@ -787,6 +815,7 @@ def main():
         if args.only == "verify":
             k6 = "decode_kernel" if one6 else "decode_kernel_2t"
             result["roofline"] = roofline_for(k6, kern6[k6][1], w6, w6.name, one6)
+        result["verify_kv_read"]["metadata_and_write"] = metadata_and_write(w6, g6, rpa, timer, args)
         del g6, ws6, out6
         torch.cuda.empty_cache()
 
@@ -811,7 +840,8 @@ def main():
             "cold_cache": {**cold2, "TFLOPs": fl2 / (cold2["median_ms"] / 1e3) / 1e12},
             "kernels_ms": {k: round(avg, 5) for k, (n, avg) in kern2.items()},
             "prefill_kernel_TFLOPs": fl2 / (kern2["prefill_kernel"][1] / 1e3) / 1e12,
-            "mfma_busy": mfma_from_profiles("prefill_kernel", w2.name)}
+            "mfma_busy": mfma_from_profiles("prefill_kernel", w2.name),
+            "metadata_and_write": metadata_and_write(w2, g2, rpa, timer, args)}
         if args.only == "prefill":
             result["roofline"] = roofline_for("prefill_kernel", kern2["prefill_kernel"][1], w2, w2.name)
 
