@@ -117,11 +117,13 @@ int32_t pa_set_validation(int32_t on);
  * Plan trace, process-wide (same thread-safety as the kernel policy): 1 = on,
  * 0 = off (the default, or on when the environment variable PA_TRACE is set
  * to anything but "" or "0" when the library is loaded).  With it on, every
- * pa_attention call that launched its kernels then waits for its stream,
- * copies its work plan from the workspace to the host and prints it to
- * stderr, each line starting with "[pa_trace]": the path taken, the work
- * split (query heads per KV head, decode parts, rows per decode item,
- * whether prefill rows and shared prefixes are planned, workspace bytes),
+ * pa_attention or pa_write_kv_attention call that launched its kernels then
+ * waits for its stream, copies its work plan from the workspace to the host
+ * and prints it to stderr, each line starting with "[pa_trace]": the path
+ * taken, the work split (query heads per KV head, decode parts, rows per
+ * decode item, whether prefill rows and shared prefixes are planned, whether
+ * the decode launches ran beside the prefill kernel, where the KV write of
+ * pa_write_kv_attention ran, workspace bytes),
  * the prefill list (prefill query tiles and shared-prefix parts), every
  * shared-prefix group (its members, prefix tokens and parts), the first
  * entries of each decode list, and d_err.  The wait makes it a debugging aid:
