@@ -66,6 +66,7 @@ struct PrefillArgs {
   const int4* groups;   // cascade groups
   const int32_t* members;  // cascade members (a group's x is its first position)
   float* ws_pre;        // cascade prefix partials: (slot, KV head, group row)
+  int32_t prio;         // 1: raise the waves' issue priority (launched beside the decode kernel)
 };
 
 constexpr int kPlanThreads = 1024;
@@ -596,6 +597,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(prefil
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, h = lane >> 5;  // the lane's row of the wave, and its half
+  // Beside the decode kernel's waves (one of each per SIMD) the prefill waves
+  // issue first: mixed step's prefill launch 578 -> 540-549 us, its decode
+  // launch 542 -> 558-564 us, so the two chains end closer together (the
+  // two-tile decode launch then follows the prefill kernel; launch_attn_fast)
+  if (a.prio) __builtin_amdgcn_s_setprio(1);
 
   // Items.  Workgroup b runs on XCD b % 8, and an XCD hands its workgroups
   // in order, round-robin, to its 4 shader engines, each waiting for a free
@@ -1072,6 +1078,7 @@ hipError_t launch_attn_prefill(const AttnArgs& a, int32_t rows_cap, int32_t P, b
   p.groups = reinterpret_cast<const int4*>(reinterpret_cast<const uint8_t*>(plan) + l.groups_off);
   p.members = reinterpret_cast<const int32_t*>(reinterpret_cast<const uint8_t*>(plan) + l.members_off);
   p.ws_pre = ws_pre;
+  p.prio = lds_pad > 0 ? 1 : 0;
   const int64_t n_eb = (static_cast<int64_t>(l.cap_entries) + kQtRun - 1) / kQtRun;
   const int64_t items_raw = n_eb * kQtRun * a.Hkv;
   const int64_t run_len = static_cast<int64_t>(kQtRun) * prefill_head_group(a.Hkv);
