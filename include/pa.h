@@ -24,8 +24,9 @@
  *   - One exception, in pa_attention and pa_write_kv_attention only: on a
  *     large mixed batch (prefill rows, head_dim 128, a block size that is a
  *     multiple of 16, at least 64 sequences and at most 64 new tokens per
- *     sequence on average) the decode launches run on a side stream beside
- *     the prefill kernel, which stays on `stream`.  That stream
+ *     sequence on average) the prefill kernel (and the two-tile decode
+ *     launch after it) runs on a side stream beside the one-tile decode
+ *     launch, which stays on `stream`.  That stream
  *     (non-blocking, default priority) and its two events are created by
  *     the library on the first such call on a device and kept until the
  *     process ends; the fork from and join back into `stream` are event
@@ -331,7 +332,7 @@ pa_status_t pa_write_kv_attention(const void* k, const void* v, const int32_t* s
  *     different streams, or from several threads, without ordering between
  *     them) race on it: the caller must order them.
  *   - Every launch stays on `stream` (pa_attention may put a large mixed
- *     batch's decode launches on the library's side stream).
+ *     batch's prefill kernel on the library's side stream).
  */
 #define PA_NOALLOC_SCRATCH_BYTES (64u << 20)
 pa_status_t pa_attention_noalloc(const void* q, const void* k_cache, const void* v_cache,

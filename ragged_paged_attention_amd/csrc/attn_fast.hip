@@ -674,8 +674,8 @@ static void launch_merge(const DecodeArgs& d, int32_t D, dim3 grid, hipStream_t 
   else merge_kernel<F, 128><<<grid, 256, 0, stream>>>(d);
 }
 
-// A side stream per device for the decode launches of a large mixed batch,
-// which run beside the prefill kernel (launch_attn_fast).  Created on first
+// A side stream per device for the prefill kernel of a large mixed batch,
+// which runs beside the decode launches (launch_attn_fast).  Created on first
 // use, default priority, never destroyed; the fork and join events are
 // recorded and waited on under one lock, so concurrent calls cannot
 // interleave them.
@@ -748,8 +748,9 @@ hipError_t launch_attn_fast(const AttnArgs& a, hipStream_t stream, bool side_str
   d.n_items = static_cast<int32_t>(items);
 
   // A large mixed batch (many decode sequences next to a few prefill
-  // chunks) runs its decode launches on a side stream beside the prefill
-  // kernel: the prefill kernel takes one workgroup per CU (its launch asks
+  // chunks) runs its decode launches and its prefill kernel side by side,
+  // the prefill kernel on a side stream: the prefill kernel takes one
+  // workgroup per CU (its launch asks
   // for kBesideLdsPad more bytes of LDS) and the decode kernel one wave per
   // SIMD (its kBeside instance), so the HBM-bound decode and the MFMA-bound
   // prefill share every CU (mixed batch: 0.715 -> 0.68 ms per step; the same
@@ -775,8 +776,8 @@ hipError_t launch_attn_fast(const AttnArgs& a, hipStream_t stream, bool side_str
     side_lock.lock();
     ss = side_stream_locked();
   }
-  SideStream* side = nullptr;  // the side stream when the decode launches run on it
-  hipStream_t ds = stream;     // the decode launches' stream
+  SideStream* side = nullptr;  // the side stream when the prefill kernel runs on it
+  const hipStream_t ds = stream;  // the one-tile decode launch's stream
   if (f.mfma_prefill) {
     int32_t* plan = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(a.workspace) + f.plan_off);
     // list entries one wave of each decode launch holds: waves per SIMD x
@@ -785,15 +786,20 @@ hipError_t launch_attn_fast(const AttnArgs& a, hipStream_t stream, bool side_str
     hipError_t e = launch_attn_plan(a, f.rows_cap, f.P, f.prefill_on, f.cascade_on, dec_slots, plan,
                                     write_in_plan ? w : nullptr, stream);
     if (e != hipSuccess) return e;
-    if (beside && ss) {  // the decode launches wait for the planning launch (and the write in it)
+    // Beside the decode launches the prefill kernel runs on the side stream,
+    // behind the planning launch (and the write in it); the one-tile decode
+    // launch, the longer of the two chains, starts on `stream` without the
+    // wait for the fork.
+    hipStream_t ps = stream;  // the prefill kernel's stream
+    if (beside && ss) {
       if (hipEventRecord(ss->fork, stream) == hipSuccess && hipStreamWaitEvent(ss->s, ss->fork, 0) == hipSuccess) {
         side = ss;
-        ds = ss->s;
+        ps = ss->s;
       }
     }
     e = launch_attn_prefill(a, f.rows_cap, f.P, f.prefill_on, f.cascade_on, plan,
                             reinterpret_cast<float*>(static_cast<uint8_t*>(a.workspace) + f.pre_off),
-                            side ? kBesideLdsPad : 0, stream);
+                            side ? kBesideLdsPad : 0, ps);
     if (e != hipSuccess) {
       if (side) {  // rejoin, so `stream` still orders after the side stream
         (void)hipEventRecord(side->join, side->s);
@@ -819,18 +825,20 @@ hipError_t launch_attn_fast(const AttnArgs& a, hipStream_t stream, bool side_str
   else launch_decode<F16, 1>(d, a.D, blk16, static_cast<uint32_t>(grid), ds, side != nullptr);
   launch_done(ds);
   if (d.rows_cap > kTileRows) {
-    // Beside the prefill kernel the two-tile launch follows it on `stream`,
-    // so the side stream holds only the one-tile launch.  With the prefill
-    // waves at a higher issue priority the prefill chain is the shorter one,
-    // and it takes the (often empty) two-tile launch: mixed step 0.662 ->
-    // 0.654 ms (the move alone, at equal priorities: 0.668 ms).
-    const hipStream_t ds2 = side ? stream : ds;
+    // Beside the prefill kernel the two-tile launch follows it on the side
+    // stream.  With the prefill waves at a higher issue priority the prefill
+    // chain is the shorter one, and it takes the (often empty) two-tile
+    // launch: mixed step 0.662 -> 0.654 ms (the move alone, at equal
+    // priorities: 0.668 ms).  The one-tile launch, now the longer chain,
+    // stays on `stream` and starts without the wait for the fork (cold
+    // median 0.626-0.629 -> 0.620-0.625 ms).
+    const hipStream_t ds2 = side ? side->s : ds;
     launch_mark("decode_kernel_2t", ds2);
     if (a.dtype == PA_BF16) launch_decode<BF16, 2>(d, a.D, blk16, static_cast<uint32_t>(grid), ds2);
     else launch_decode<F16, 2>(d, a.D, blk16, static_cast<uint32_t>(grid), ds2);
     launch_done(ds2);
   }
-  if (side) {  // join: the merge and everything after it wait for the decode launches
+  if (side) {  // join: the merge and everything after it wait for the side stream's launches
     hipError_t e = hipEventRecord(side->join, side->s);
     if (e == hipSuccess) e = hipStreamWaitEvent(stream, side->join, 0);
     side_lock.unlock();

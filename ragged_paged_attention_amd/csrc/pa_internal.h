@@ -79,8 +79,8 @@ inline bool write_in_plan_ok(const WriteJob& w) {
                           static_cast<uintptr_t>(w.row_bytes);
   return !w.validate && align % 16 == 0;
 }
-// side_stream_ok: a large mixed batch may run its decode launches on the
-// library's side stream beside the prefill kernel (decode_beside_prefill);
+// side_stream_ok: a large mixed batch may run its prefill kernel on the
+// library's side stream beside the decode launches (decode_beside_prefill);
 // false keeps every launch on `stream`.  A KV write w goes into the planning
 // launch when the call has one (write_in_plan_ok), else first on `stream`.
 hipError_t launch_attn_fast(const AttnArgs& a, hipStream_t stream, bool side_stream_ok,
