@@ -157,8 +157,8 @@ class Timer:
 
 
 def setup(w, torch):
-    from tests.gpu_path import GpuRun
-    g = GpuRun(w).fill_history()
+    from tests.gpu_path import DeviceRun
+    g = DeviceRun(w).fill_history()
     torch.cuda.synchronize()
     return g
 

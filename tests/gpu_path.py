@@ -19,7 +19,7 @@ from workloads.device import DeviceBatch
 DEVICE = "cuda"
 
 
-class GpuRun:
+class DeviceRun:
     def __init__(self, w, device=DEVICE):
         self.w = w
         self.db = DeviceBatch(w, device)

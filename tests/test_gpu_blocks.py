@@ -14,7 +14,7 @@ import torch
 import oracle
 import ragged_paged_attention_amd as rpa
 from ragged_paged_attention_amd.step import forward_step
-from tests.gpu_path import GpuRun, max_abs_err, tol_for
+from tests.gpu_path import DeviceRun, max_abs_err, tol_for
 from workloads import random_batch
 from workloads.device import tensor, to_numpy_bits, torch_dtype
 from workloads.generators import _pad_tables, f32_to_bf16_bits
@@ -161,7 +161,7 @@ def test_swap_out_and_in_through_pinned_host_memory():
     device blocks, swap them back in at other ids and repoint the tables:
     attention is bit-identical to the run before the swap."""
     w = random_batch(404, S=6, Hq=8, Hkv=2, D=128, bs=16, dtype="bf16", max_ctx=300, max_q=40, extra_blocks=60)
-    g = GpuRun(w).run()
+    g = DeviceRun(w).run()
     out0 = g.out.clone()
     bt = w.step.block_tables.copy()
     used = set(int(x) for x in bt[bt >= 0])

@@ -17,7 +17,7 @@ import torch
 
 import oracle
 import ragged_paged_attention_amd as rpa
-from tests.gpu_path import GpuRun, capture_stderr, max_abs_err, one_stream_output, tol_for
+from tests.gpu_path import DeviceRun, capture_stderr, max_abs_err, one_stream_output, tol_for
 from workloads import config, permute_sequences, unshare, verify_batch
 from workloads.generators import build_workload
 
@@ -95,7 +95,7 @@ def test_cascade_matches_oracle(name):
     c = CASES[name]
     w = grouped_batch(len(name), c["segs"], c["Hq"], c["Hkv"])
     print(f"[cascade] {name} {w.summary()}", flush=True)
-    g = GpuRun(w).run()
+    g = DeviceRun(w).run()
     _, _, _, ref = oracle.run_step(w)
     assert g.err() == 0
     err = max_abs_err(g.out, ref)
@@ -105,12 +105,12 @@ def test_cascade_matches_oracle(name):
 
 def test_cascade_fp16_and_generic_agree():
     w = grouped_batch(11, [("group", 6, 2048, 1, 100), ("single", 1, 3000)], 32, 4, dtype="f16")
-    g = GpuRun(w).run()
+    g = DeviceRun(w).run()
     _, _, _, ref = oracle.run_step(w)
     assert max_abs_err(g.out, ref) <= tol_for("f16")
     prev = rpa.pa_set_kernel_policy(rpa.PA_POLICY_GENERIC)
     try:
-        g2 = GpuRun(w).run()
+        g2 = DeviceRun(w).run()
     finally:
         rpa.pa_set_kernel_policy(prev)
     assert max_abs_err(g.out, g2.out.to(torch.float64).cpu().numpy()) <= tol_for("f16")
@@ -125,7 +125,7 @@ def test_workspace_writes_stay_inside_reported_size(make):
     pa_attention_workspace_size(): a guard region right after it keeps its
     pattern."""
     w = make()
-    g = GpuRun(w).fill_history().write_step_rows()
+    g = DeviceRun(w).fill_history().write_step_rows()
     need = rpa.pa_attention_workspace_size(w.num_seqs, w.num_tokens, w.num_q_heads, w.num_kv_heads, w.head_dim,
                                            max(1, w.max_query_len), max(1, w.max_seq_len))
     guard = 1 << 16
@@ -151,15 +151,15 @@ def test_grouping_does_not_depend_on_batch_order(scale_down):
     perm = np.random.default_rng(17).permutation(w.num_seqs)
     wp = permute_sequences(w, perm)
     print(f"[cascade order] {w.summary()}", flush=True)
-    a = GpuRun(w).run().out
-    b = GpuRun(wp).run().out
+    a = DeviceRun(w).run().out
+    b = DeviceRun(wp).run().out
     inv = np.argsort(perm)          # sequences are single-token: row i is sequence i
     b_back = b[torch.from_numpy(inv).to("cuda")]
     assert torch.equal(a.view(torch.int16), b_back.view(torch.int16))
     w.num_blocks += int((w.step.block_tables >= 0).sum())
     used = set(int(x) for x in w.step.block_tables.ravel() if x >= 0)
     u = unshare(w, [x for x in range(w.num_blocks) if x not in used])
-    c = GpuRun(u).run().out
+    c = DeviceRun(u).run().out
     assert not torch.equal(a.view(torch.int16), c.view(torch.int16))
     rows = list(range(0, w.num_tokens, max(1, w.num_tokens // 16)))
     _, _, _, ref = oracle.run_step(wp, rows=rows)
@@ -175,7 +175,7 @@ def test_trace_lists_the_groups():
     w = grouped_batch(len("three_groups"), c["segs"], c["Hq"], c["Hkv"])
     prev = rpa.pa_set_trace(1)
     try:
-        g, text = capture_stderr(lambda: GpuRun(w).run())
+        g, text = capture_stderr(lambda: DeviceRun(w).run())
     finally:
         rpa.pa_set_trace(prev)
     print(text, flush=True)
@@ -206,7 +206,7 @@ def test_groups_beside_prefill_chunks():
                                            w.max_query_len, w.max_seq_len)
     prev = rpa.pa_set_trace(1)
     try:
-        g, text = capture_stderr(lambda: GpuRun(w).run())
+        g, text = capture_stderr(lambda: DeviceRun(w).run())
     finally:
         rpa.pa_set_trace(prev)
     assert "decode_beside_prefill=1" in text and "shared_prefix=1" in text

@@ -17,7 +17,7 @@ import torch
 
 import oracle
 import ragged_paged_attention_amd as rpa
-from tests.gpu_path import GpuRun, max_abs_err, tol_for
+from tests.gpu_path import DeviceRun, max_abs_err, tol_for
 from workloads.generators import build_workload
 
 pytestmark = pytest.mark.gpu
@@ -52,7 +52,7 @@ def test_decode_lists_match_oracle(S, Hq, Hkv):
     w = _mixed(S, Hq, Hkv, seed=S)
     print(f"[decode_list] {w.summary()}", flush=True)
     rpa.pa_bench_timing_begin()
-    g = GpuRun(w).run()
+    g = DeviceRun(w).run()
     t = rpa.pa_bench_timing_end()
     assert "attn_plan_kernel" in t       # the lists exist in this call
     _, _, _, ref = oracle.run_step(w)
@@ -72,7 +72,7 @@ def test_decode_lists_zero_fill_when_hint_is_violated():
     ql[4] = 9                             # 36 rows at G = 4: above the one-tile cap of the hint
     sl = [2100 + 37 * i for i in range(S)]
     w = _batch(32, 8, ql, sl, seed=9)
-    g = GpuRun(w).fill_history().write_step_rows()
+    g = DeviceRun(w).fill_history().write_step_rows()
     d_err = torch.zeros(1, dtype=torch.int32, device="cuda")
     out = torch.full_like(g.db.q, float("nan"))
     rpa.pa_bench_timing_begin()

@@ -16,7 +16,7 @@ import torch
 
 import oracle
 import ragged_paged_attention_amd as rpa
-from tests.gpu_path import GpuRun, max_abs_err, tol_for
+from tests.gpu_path import DeviceRun, max_abs_err, tol_for
 from workloads import Batch, Workload, config, plant_needles, random_batch
 from workloads.device import to_numpy_bits
 from workloads.generators import _pad_tables
@@ -69,7 +69,7 @@ def _run_fast(w):
     not support fails instead of falling back), timing which kernels ran."""
     prev = rpa.pa_set_kernel_policy(rpa.PA_POLICY_FAST)
     try:
-        g = GpuRun(w).fill_history()
+        g = DeviceRun(w).fill_history()
         torch.cuda.synchronize()
         rpa.pa_bench_timing_begin()
         g.step()
@@ -129,7 +129,7 @@ def test_full_size_needles(n):
 
 def test_empty_batch_is_a_no_op():
     w = config(1)
-    g = GpuRun(w).run()
+    g = DeviceRun(w).run()
     out = torch.full_like(g.db.q, 7.0)
     qsl = torch.zeros(1, dtype=torch.int32, device="cuda")
     sl = torch.zeros(0, dtype=torch.int32, device="cuda")
@@ -161,7 +161,7 @@ def test_zero_length_queries_mixed_in(dtype):
         tables.append([int(x) for x in ids[o:o + c]])
         o += c
     w = _explicit(dtype, 8, 2, 128, bs, 64, ql, sl, tables, 5)
-    g = GpuRun(w).run()
+    g = DeviceRun(w).run()
     _, _, _, ref = oracle.run_step(w)
     assert g.err() == 0
     assert max_abs_err(g.out, ref) <= tol_for(dtype)
@@ -173,7 +173,7 @@ def test_small_hints_flagged_and_still_correct_when_covered():
     two decode tiles), which covers any length, so the rows are right; a
     too-small max_seq_len only makes split parts longer."""
     w = config(2, scale_down=4)
-    g = GpuRun(w).fill_history().write_step_rows()
+    g = DeviceRun(w).fill_history().write_step_rows()
     d_err = torch.zeros(1, dtype=torch.int32, device="cuda")
     out = rpa.pa_attention(g.db.q, g.k_cache, g.v_cache, g.db.block_tables, g.meta["query_start_loc"],
                            g.db.seq_lens, 40, 3, w.scale, d_err=d_err)
@@ -197,7 +197,7 @@ def test_very_long_decode_context_beyond_part_cap(needles):
     w = _explicit("bf16", 4, 1, 128, bs, nb + 8, [1], [L], tables, 11)
     if needles:
         w = plant_needles(w, seed=12)
-    g = GpuRun(w).run()
+    g = DeviceRun(w).run()
     _, _, _, ref = oracle.run_step(w)
     assert g.err() == 0
     err = max_abs_err(g.out, ref)
@@ -212,7 +212,7 @@ def test_very_long_decode_context_beyond_part_cap(needles):
 def test_other_shapes(shape):
     w = random_batch(77, S=5, Hq=shape["Hq"], Hkv=shape["Hkv"], D=shape["D"], bs=shape["bs"], dtype="bf16",
                      max_ctx=300, max_q=70)
-    g = GpuRun(w).run()
+    g = DeviceRun(w).run()
     _, _, _, ref = oracle.run_step(w)
     assert g.err() == 0
     assert max_abs_err(g.out, ref) <= tol_for("bf16")
@@ -226,7 +226,7 @@ def test_invalid_block_ids_on_the_mfma_paths():
     match the oracle.  The rows of the two damaged sequences are
     unspecified and not compared."""
     w = config(4, scale_down=8)
-    g = GpuRun(w).fill_history().write_step_rows()
+    g = DeviceRun(w).fill_history().write_step_rows()
     ql, sl = w.step.query_lens, w.step.seq_lens
     G = w.num_q_heads // w.num_kv_heads
     dec = [s for s in range(w.num_seqs) if ql[s] == 1]

@@ -15,7 +15,7 @@ import pytest
 
 import oracle
 import ragged_paged_attention_amd as rpa
-from tests.gpu_path import GpuRun, max_abs_err, tol_for
+from tests.gpu_path import DeviceRun, max_abs_err, tol_for
 from workloads.generators import build_workload
 
 pytestmark = pytest.mark.gpu
@@ -49,7 +49,7 @@ def test_group_sizes_match_oracle(Hq, Hkv):
     w = _batch(Hq, Hkv, QL, SL, seed=Hq * 10 + Hkv)
     print(f"[groups] Hq={Hq} Hkv={Hkv}", flush=True)
     rpa.pa_bench_timing_begin()
-    g = GpuRun(w).run()
+    g = DeviceRun(w).run()
     t = rpa.pa_bench_timing_end()
     _, _, _, ref = oracle.run_step(w)
     assert g.err() == 0
@@ -61,7 +61,7 @@ def test_group_sizes_match_oracle(Hq, Hkv):
 
 def test_group_of_five_fp16():
     w = _batch(20, 4, [1, 6, 129, 1], [3000, 700, 129, 9], seed=5, dtype="f16")
-    g = GpuRun(w).run()
+    g = DeviceRun(w).run()
     _, _, _, ref = oracle.run_step(w)
     assert g.err() == 0
     assert max_abs_err(g.out, ref) <= tol_for("f16")
@@ -82,7 +82,7 @@ def test_shared_prefix_group_of_three():
     tables = [pre + [next(ids) for _ in range(-(-L // bs) - prefix // bs)] for L in sl]
     w = _batch(24, 8, ql, sl, seed=11, tables=tables, shared=[(list(range(n)), prefix)])
     rpa.pa_bench_timing_begin()
-    g = GpuRun(w).run()
+    g = DeviceRun(w).run()
     t = rpa.pa_bench_timing_end()
     _, _, _, ref = oracle.run_step(w)
     assert g.err() == 0

@@ -15,7 +15,7 @@ import ragged_paged_attention_amd as rpa
 from workloads import config, decode_variant, random_batch, relabel_blocks, unshare
 from workloads.device import to_numpy_bits
 
-from tests.gpu_path import GpuRun, capture_stderr, max_abs_err, one_stream_output, tol_for
+from tests.gpu_path import DeviceRun, capture_stderr, max_abs_err, one_stream_output, tol_for
 
 pytestmark = pytest.mark.gpu
 
@@ -51,7 +51,7 @@ SMALL = [("tiny_mixed", lambda: config(1))] + \
 def test_metadata_and_scatter_bitexact(name, make):
     w = make()
     print(f"[case] {name} {w.summary()}", flush=True)
-    g = GpuRun(w).run()
+    g = DeviceRun(w).run()
     md, kc, vc, _ = oracle.run_step(w, rows=[0])
     _meta_equal(g.meta, md, w.num_tokens)
     assert np.array_equal(_bits(to_numpy_bits(g.k_cache)), _bits(kc)), "k_cache differs"
@@ -62,7 +62,7 @@ def test_metadata_and_scatter_bitexact(name, make):
 def test_tiny_mixed_fp32_attention():
     """The forward-shape walkthrough batch (B, C decode; A prefills 5)."""
     w = config(1)
-    g = GpuRun(w).run()
+    g = DeviceRun(w).run()
     _, _, _, ref = oracle.run_step(w)
     err = max_abs_err(g.out, ref)
     print(f"[tiny_mixed] max_abs_err={err:.3e}", flush=True)
@@ -89,7 +89,7 @@ def test_random_sweep(case, policy):
     rpa.pa_set_kernel_policy(rpa.PA_POLICY_GENERIC if policy == "generic" else rpa.PA_POLICY_AUTO)
     w = random_batch(case["seed"], S=6, Hq=case["Hq"], Hkv=case["Hkv"], D=case["D"], bs=case["bs"],
                      dtype=case["dtype"], max_ctx=70, max_q=40, decode_frac=0.5)
-    g = GpuRun(w).run()
+    g = DeviceRun(w).run()
     _, _, _, ref = oracle.run_step(w)
     err = max_abs_err(g.out, ref)
     assert err <= tol_for(w.dtype), f"max_abs_err {err}"
@@ -104,7 +104,7 @@ def test_scaled_configs(n, policy):
     rpa.pa_set_kernel_policy(rpa.PA_POLICY_GENERIC if policy == "generic" else rpa.PA_POLICY_AUTO)
     w = config(n, scale_down=16)
     print(f"[case] scaled config {n} {w.summary()}", flush=True)
-    g = GpuRun(w).run()
+    g = DeviceRun(w).run()
     _, _, _, ref = oracle.run_step(w)
     err = max_abs_err(g.out, ref)
     print(f"[scaled cfg{n} {policy}] max_abs_err={err:.3e}", flush=True)
@@ -116,8 +116,8 @@ def test_placement_invariance_bitexact():
     """Relabelled physical blocks give bit-identical outputs."""
     w = config(4, scale_down=16)
     perm = np.random.default_rng(5).permutation(w.num_blocks)
-    a = GpuRun(w).run().out
-    b = GpuRun(relabel_blocks(w, perm)).run().out
+    a = DeviceRun(w).run().out
+    b = DeviceRun(relabel_blocks(w, perm)).run().out
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
@@ -127,8 +127,8 @@ def test_sharing_invariance_bitexact():
     w.num_blocks += int((w.step.block_tables >= 0).sum())
     used = set(int(b) for b in w.step.block_tables.ravel() if b >= 0)
     u = unshare(w, [b for b in range(w.num_blocks) if b not in used])
-    a = GpuRun(w).run().out
-    b = GpuRun(u).run().out
+    a = DeviceRun(w).run().out
+    b = DeviceRun(u).run().out
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
@@ -141,7 +141,7 @@ def test_isolation_from_other_sequences_blocks_bitexact(n):
     own block table), while the odd sequences' outputs change."""
     w = config(n, scale_down=8)
     print(f"[case] isolation cfg{n} {w.summary()}", flush=True)
-    g = GpuRun(w).run()
+    g = DeviceRun(w).run()
     before = g.out.clone()
     bt = w.step.block_tables
     keep = sorted(set(int(b) for s in range(0, w.num_seqs, 2) for b in bt[s] if b >= 0))
@@ -171,7 +171,7 @@ def test_mixed_batch_decode_beside_prefill():
     print(f"[case] beside {w.summary()}", flush=True)
     prev = rpa.pa_set_trace(1)
     try:
-        g, text = capture_stderr(lambda: GpuRun(w).run())
+        g, text = capture_stderr(lambda: DeviceRun(w).run())
     finally:
         rpa.pa_set_trace(prev)
     assert "decode_beside_prefill=1" in text
@@ -204,7 +204,7 @@ def test_mixed_batch_beside_equals_one_stream(dtype, bs):
                                            w.max_query_len, w.max_seq_len)
     prev = rpa.pa_set_trace(1)
     try:
-        g, text = capture_stderr(lambda: GpuRun(w).run())
+        g, text = capture_stderr(lambda: DeviceRun(w).run())
     finally:
         rpa.pa_set_trace(prev)
     assert "decode_beside_prefill=1" in text
@@ -219,7 +219,7 @@ def test_mixed_batch_beside_equals_one_stream(dtype, bs):
 
 def test_deterministic():
     w = config(4, scale_down=8)
-    g = GpuRun(w).run()
+    g = DeviceRun(w).run()
     first = g.out.clone()
     g.step()
     torch.cuda.synchronize()
@@ -230,7 +230,7 @@ def test_error_flags_from_host_forced_data():
     """Invalid metadata is flagged on the device and no access leaves the
     buffers (the pool is NaN-poisoned; outputs of flagged rows are zero)."""
     w = config(1)
-    g = GpuRun(w).run()          # history and this step's rows are in the pool
+    g = DeviceRun(w).run()          # history and this step's rows are in the pool
     dev = g.db
     # query_len > seq_len for sequence 0
     bad_sl = dev.seq_lens.clone()
@@ -272,7 +272,7 @@ def test_workspace_too_small_is_rejected():
     """A mixed batch needs workspace (the work plan and split-K partials); one
     byte less is refused with PA_ERR_WORKSPACE and nothing runs."""
     w = config(4, scale_down=8)
-    g = GpuRun(w).fill_history()
+    g = DeviceRun(w).fill_history()
     need = rpa.pa_attention_workspace_size(w.num_seqs, w.num_tokens, w.num_q_heads, w.num_kv_heads,
                                            w.head_dim, w.max_query_len, w.max_seq_len)
     assert need > 0
@@ -306,7 +306,7 @@ def test_any_finite_scale(n, scale):
     oracle at scale 0 (every visible key weighs the same), a negative scale
     and a large positive one; scale <= 0 runs on the generic kernel."""
     w = _Scaled(config(n, scale_down=16), scale)
-    g = GpuRun(w).run()
+    g = DeviceRun(w).run()
     _, _, _, ref = oracle.run_step(w)
     err = max_abs_err(g.out, ref)
     print(f"[scale {scale}] config {n} max_abs_err={err:.3e}", flush=True)
@@ -321,7 +321,7 @@ def test_duplicate_slots_flagged_with_validation():
     slots (a whole mixed step) is not flagged; with validation off nothing is
     checked."""
     w = config(4, scale_down=8)
-    g = GpuRun(w)
+    g = DeviceRun(w)
     prev = rpa.pa_set_validation(1)
     try:
         g.fill_history()
@@ -365,7 +365,7 @@ def test_plan_doubles_the_parts_of_a_list_between_one_and_two_waves():
     print(f"[case] doubled parts {w.summary()}", flush=True)
     prev = rpa.pa_set_trace(1)
     try:
-        g, text = capture_stderr(lambda: GpuRun(w).run())
+        g, text = capture_stderr(lambda: DeviceRun(w).run())
     finally:
         rpa.pa_set_trace(prev)
     assert "decode items 80 one-tile, 0 two-tile (parts of at most 1536, 768 tokens)" in text

@@ -14,7 +14,7 @@ import torch
 
 import oracle
 import ragged_paged_attention_amd as rpa
-from tests.gpu_path import GpuRun, max_abs_err, tol_for
+from tests.gpu_path import DeviceRun, max_abs_err, tol_for
 from workloads import plant_needles
 from workloads.generators import build_workload
 
@@ -50,7 +50,7 @@ def test_variant_matches_oracle(shape, D, bs, Hq, Hkv):
     w = _batch(Hq, Hkv, D, bs, c["ql"], c["sl"], seed=D + bs + Hq)
     print(f"[variant] {shape} D={D} bs={bs} Hq={Hq} Hkv={Hkv}", flush=True)
     rpa.pa_bench_timing_begin()
-    g = GpuRun(w).run()
+    g = DeviceRun(w).run()
     t = rpa.pa_bench_timing_end()
     _, _, _, ref = oracle.run_step(w)
     assert g.err() == 0
@@ -65,7 +65,7 @@ def test_variant_matches_oracle(shape, D, bs, Hq, Hkv):
 @pytest.mark.parametrize("D,bs", [(64, 8), (256, 16)])
 def test_variant_fp16(D, bs):
     w = _batch(32, 8, D, bs, [1, 1, 2, 1], [1500, 3100, 600, 33], seed=D, dtype="f16")
-    g = GpuRun(w).run()
+    g = DeviceRun(w).run()
     _, _, _, ref = oracle.run_step(w)
     assert g.err() == 0
     assert max_abs_err(g.out, ref) <= tol_for("f16")
@@ -88,7 +88,7 @@ def test_variant_shared_prefix_bs8():
     tables.append([next(ids) for _ in range(-(-sl[n] // bs))])
     w = build_workload("shared_bs8", "bf16", 32, 4, 128, bs, NB, ql, sl, tables, 3, rng,
                        shared=[(list(range(n)), prefix)])
-    g = GpuRun(w).run()
+    g = DeviceRun(w).run()
     _, _, _, ref = oracle.run_step(w)
     assert g.err() == 0
     assert max_abs_err(g.out, ref) <= tol_for("bf16")
@@ -102,7 +102,7 @@ def test_variant_needles(D, bs):
     error."""
     c = SHAPES["mixed"]
     w = plant_needles(_batch(16, 4, D, bs, c["ql"], c["sl"], seed=D + bs), seed=bs)
-    g = GpuRun(w).run()
+    g = DeviceRun(w).run()
     _, _, _, ref = oracle.run_step(w)
     assert g.err() == 0
     err = max_abs_err(g.out, ref)

@@ -14,7 +14,7 @@ import torch
 
 import oracle
 import ragged_paged_attention_amd as rpa
-from tests.gpu_path import GpuRun, capture_stderr, max_abs_err, tol_for
+from tests.gpu_path import DeviceRun, capture_stderr, max_abs_err, tol_for
 from workloads import verify_batch
 from workloads.generators import build_workload
 
@@ -33,7 +33,7 @@ def policy(request):
 def test_verify_batch_scaled(seed, dtype, policy):
     w = verify_batch(seed=seed, dtype=dtype, scale_down=8)
     print(f"[verify] seed={seed} {dtype} {policy} {w.summary()}", flush=True)
-    g = GpuRun(w).run()
+    g = DeviceRun(w).run()
     _, _, _, ref = oracle.run_step(w)
     assert g.err() == 0
     assert max_abs_err(g.out, ref) <= tol_for(dtype)
@@ -66,7 +66,7 @@ def test_row_classes_mixed_in_one_call(Hq, Hkv, ql):
     ctx[0] = 40
     w = _explicit(Hq, Hkv, ql, ctx, seed=Hq + Hkv)
     print(f"[verify] classes Hq={Hq} Hkv={Hkv} ql={ql}", flush=True)
-    g = GpuRun(w).run()
+    g = DeviceRun(w).run()
     _, _, _, ref = oracle.run_step(w)
     assert g.err() == 0
     assert max_abs_err(g.out, ref) <= tol_for("bf16")
@@ -86,7 +86,7 @@ def test_verify_full_size_sampled_rows():
     print(f"[verify] full {w.summary()} rows={len(rows)}", flush=True)
     prev = rpa.pa_set_trace(1)
     try:
-        g, text = capture_stderr(lambda: GpuRun(w).run())
+        g, text = capture_stderr(lambda: DeviceRun(w).run())
     finally:
         rpa.pa_set_trace(prev)
     assert "(parts of at most 768, 1536 tokens)" in text
@@ -103,7 +103,7 @@ def test_too_small_query_len_hint_is_flagged():
     raised; sequences whose rows still fit one decode tile are computed,
     the others come back as zeros (never garbage)."""
     w = verify_batch(seed=3, scale_down=8)
-    g = GpuRun(w).fill_history().write_step_rows()
+    g = DeviceRun(w).fill_history().write_step_rows()
     d_err = torch.zeros(1, dtype=torch.int32, device="cuda")
     out = torch.full_like(g.db.q, float("nan"))
     rpa.pa_attention(g.db.q, g.k_cache, g.v_cache, g.db.block_tables, g.meta["query_start_loc"], g.db.seq_lens,

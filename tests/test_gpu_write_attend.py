@@ -12,7 +12,7 @@ import torch
 
 import oracle
 import ragged_paged_attention_amd as rpa
-from tests.gpu_path import GpuRun, capture_stderr, max_abs_err, tol_for
+from tests.gpu_path import DeviceRun, capture_stderr, max_abs_err, tol_for
 from tests.test_gpu_cascade import grouped_batch
 from workloads import config, verify_batch
 
@@ -46,7 +46,7 @@ WRITE_AT = {"mixed_split": "in_plan", "ragged_prefill": "in_plan", "verify": "in
 
 def _separate(w, g):
     """pa_write_kv then pa_attention into fresh caches holding the same history."""
-    h = GpuRun(w).fill_history()
+    h = DeviceRun(w).fill_history()
     md = rpa.pa_build_metadata(h.db.query_lens, h.db.seq_lens, w.num_tokens, h.db.block_tables, w.block_size,
                                w.num_blocks, d_err=h.d_err)
     rpa.pa_write_kv(h.db.k, h.db.v, md["slot_mapping"], h.k_cache, h.v_cache, d_err=h.d_err)
@@ -62,7 +62,7 @@ def test_fused_write_and_attention_equal_the_two_calls(name):
     print(f"[case] {name} {w.summary()}", flush=True)
     prev = rpa.pa_set_trace(1)
     try:
-        g, text = capture_stderr(lambda: GpuRun(w).run())   # forward_step: metadata, then the fused call
+        g, text = capture_stderr(lambda: DeviceRun(w).run())   # forward_step: metadata, then the fused call
     finally:
         rpa.pa_set_trace(prev)
     if name in ("mixed_split", "groups_split", "mixed_split_f16", "mixed_bs32"):
@@ -93,7 +93,7 @@ def test_fused_write_of_unaligned_rows_goes_first():
     launch's workgroups copy 16-byte chunks only, so the write runs as its own
     launch first; the caches and output still equal the two separate calls."""
     w = config(2, scale_down=4)
-    g = GpuRun(w).fill_history()
+    g = DeviceRun(w).fill_history()
     md = rpa.pa_build_metadata(g.db.query_lens, g.db.seq_lens, w.num_tokens, g.db.block_tables, w.block_size,
                                w.num_blocks, d_err=g.d_err)
     kbuf = torch.empty(g.db.k.numel() + 1, dtype=g.db.k.dtype, device=g.db.k.device)
@@ -121,7 +121,7 @@ def test_fused_call_flags_duplicate_slots_with_validation():
     """With validation on, the write inside the fused call checks for
     repeated slots like pa_write_kv does."""
     w = config(4, scale_down=4)
-    g = GpuRun(w).fill_history()
+    g = DeviceRun(w).fill_history()
     md = rpa.pa_build_metadata(g.db.query_lens, g.db.seq_lens, w.num_tokens, g.db.block_tables, w.block_size,
                                w.num_blocks, d_err=g.d_err)
     slots = md["slot_mapping"].clone()
@@ -143,7 +143,7 @@ def test_fused_write_flags_slots_past_the_pool():
     PA_DERR_SLOT_OOB, and no cache row changes but the ones the other
     tokens name."""
     w = config(2, scale_down=4)
-    g = GpuRun(w).fill_history()
+    g = DeviceRun(w).fill_history()
     md = rpa.pa_build_metadata(g.db.query_lens, g.db.seq_lens, w.num_tokens, g.db.block_tables, w.block_size,
                                w.num_blocks, d_err=g.d_err)
     torch.cuda.synchronize()
@@ -151,7 +151,7 @@ def test_fused_write_flags_slots_past_the_pool():
     slots = md["slot_mapping"].clone()
     bad = w.num_tokens // 2
     slots[bad] = w.num_blocks * w.block_size
-    h = GpuRun(w).fill_history()
+    h = DeviceRun(w).fill_history()
     slots_h = slots.clone()
     slots_h[bad] = -1  # the same write with that row skipped
     rpa.pa_write_kv(h.db.k, h.db.v, slots_h, h.k_cache, h.v_cache, d_err=h.d_err)

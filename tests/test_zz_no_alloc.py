@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import ragged_paged_attention_amd as rpa
-from tests.gpu_path import GpuRun, max_abs_err, tol_for
+from tests.gpu_path import DeviceRun, max_abs_err, tol_for
 from workloads import config, verify_batch
 
 pytestmark = pytest.mark.gpu
@@ -30,7 +30,7 @@ def test_noalloc_matches_pa_attention_on_consecutive_calls():
         assert 0 < need <= rpa.PA_NOALLOC_SCRATCH_BYTES
         assert prev_need is None or need < prev_need
         prev_need = need
-        g = GpuRun(w).fill_history().write_step_rows()
+        g = DeviceRun(w).fill_history().write_step_rows()
         db, qsl = g.db, g.meta["query_start_loc"]
         args = (db.q, g.k_cache, g.v_cache, db.block_tables, qsl, db.seq_lens, w.max_query_len, w.max_seq_len,
                 w.scale)
